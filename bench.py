@@ -1,0 +1,196 @@
+"""Throughput of the DeepSeekMoE layer forward pass on one MI355X.
+
+One step = one full layer forward (router, dispatch, grouped expert GEMMs,
+combine) over the 16B-shaped workload: T=16384 tokens, d=2048, 64 routed
+experts (inner 1408, top-6, softmax gate) + 2 shared experts, bf16 with an
+fp32 router, seeded synthetic inputs resident in HBM before timing starts.
+
+Prints one JSON line with tokens/s, activated TFLOP/s and the fraction of
+the bf16 matrix peak, per-stage times from HIP events recorded on the
+layer's stream during the timed steps, a roofline entry for the dominant
+kernel, and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer fwd tokens/s + activated TFLOP/s (% bf16 MFMA peak), "
+          "16B-shape, 1 GPU")
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (TFLOP/s)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (GB/s)
+DOMINANT = "gemm_gateup_routed"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_routed.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_mk_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, host, n_tokens):
+    """Time the fp64 CPU oracle on the first n_tokens tokens."""
+    import numpy as np
+    import threadpoolctl
+    import oracle
+    w = [t.float().numpy() for t in host["routed"]]
+    ws = [t.float().numpy() for t in host["shared"]] if host["shared"] is not None else None
+    x = host["x"][:n_tokens].float().numpy()
+    wg = host["w_gate"].numpy()
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, wg, tuple(w), tuple(ws) if ws else None, cfg.top_k,
+                       n_shared=cfg.n_shared, score=cfg.score)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"first {n_tokens} of {cfg.T} tokens of the same workload "
+                      f"(numpy fp64 oracle, BLAS threads={cores})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="deepseekmoe-16b")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for "
+                         "scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    import workloads
+    import mixture_experts_layer_mk_amd as moe
+
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name}")
+    inp = workloads.make_inputs(cfg)
+    host = inp.torch_tensors("cpu")
+    d = {k: (tuple(t.to(dev) for t in v) if isinstance(v, tuple)
+             else (v.to(dev) if v is not None else None)) for k, v in host.items()}
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner,
+                         cfg.n_shared, cfg.shared_inner, n_groups=cfg.n_groups,
+                         topk_groups=cfg.topk_groups, score=cfg.score,
+                         norm_topk=cfg.norm_topk, routed_scale=cfg.routed_scale,
+                         dtype=cfg.dtype)
+    ws = torch.empty(moe.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["x"])
+    names = moe.trace_stage_names()
+    nst = len(names)
+    events = [moe.HipEvents(nst + 1) for _ in range(args.steps)]
+
+    def step(ev=None):
+        moe.moe_layer_forward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k,
+                              score=cfg.score, norm_topk=cfg.norm_topk,
+                              n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                              select_bias=d["select_bias"], logit_bias=d["logit_bias"],
+                              routed_scale=cfg.routed_scale, out=out, workspace=ws,
+                              trace_events=None if ev is None else ev.handles)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {n: 0.0 for n in names}
+    total_ev = 0.0
+    for ev in events:
+        for i, n in enumerate(names):
+            stage_ms[n] += ev.elapsed_ms(i, i + 1) / args.steps
+        total_ev += ev.elapsed_ms(0, nst) / args.steps
+    for ev in events:
+        ev.close()
+    ms = wall * 1e3 / args.steps
+    tok_s = cfg.T / (ms / 1e3)
+    fpt = oracle.expert_flops_per_token(cfg.d, cfg.top_k, cfg.inner, cfg.n_shared,
+                                        cfg.shared_inner)
+    act_tflops = fpt * cfg.T / (ms / 1e3) / 1e12
+    router_gflop = 2 * cfg.T * cfg.d * cfg.n_routed / 1e9
+
+    # dominant kernel: routed gate/up GEMM, 2 * (T*K) * d * (2 * inner) flops
+    dom_flops = 2.0 * cfg.T * cfg.top_k * cfg.d * 2 * cfg.inner
+    dom_ms = stage_ms[DOMINANT]
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    roofline = {"kernel": "gemm_bf16_kernel<GATEUP> (routed launch)", "bound": "mfma",
+                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(),
+                "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)}
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline on {args.cpu_tokens} tokens")
+        cpu = cpu_baseline(cfg, host, min(args.cpu_tokens, cfg.T))
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": (f"{cfg.name} MoE layer: T={cfg.T}, d={cfg.d}, "
+                                f"{cfg.n_routed} routed (inner {cfg.inner}, top-{cfg.top_k}, "
+                                f"{cfg.score}) + {cfg.n_shared} shared (inner {cfg.shared_inner})"),
+                   "tokens": cfg.T, "parallelism": "single-gpu"},
+        "activated_tflops": round(act_tflops, 1),
+        "frac_bf16_peak": round(act_tflops / PEAK_BF16_TFLOPS, 4),
+        "router_gflop": round(router_gflop, 2),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "events_ms_per_step": round(total_ev, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * moe_layer.h -- C ABI of the MI355X (gfx950) DeepSeekMoE layer forward pass.
+ *
+ * The operation (DeepSeekMoE paper abstract; DeepSeekMoE blog post, sections
+ * "Fine-Grained Expert Segmentation (Section 3.1)", "Shared Expert Isolation
+ * (Section 3.2)" and "DeepSeekMoE 2B Model Example"; DeepSeek-V3 Technical
+ * Report summary, section "2. Architecture"):
+ *
+ *   for every token u_t (row t of x):
+ *     l_e   = u_t . Wg_e (+ logit_bias_e)                 fp32, e < n_routed
+ *     s_e   = softmax_e(l) | sigmoid(l_e)
+ *     key_e = s_e (+ select_bias_e)        bias used for choosing only
+ *     [group limit: experts split into n_groups contiguous groups; a group's
+ *      score is the sum of its two highest keys; only the topk_groups best
+ *      groups stay eligible]
+ *     sel   = the top_k largest keys (key descending, then index ascending)
+ *     g_k   = s_{sel_k} [/ sum_k s_{sel_k} if norm_topk] * routed_scale
+ *     out_t = u_t + sum_{s<n_shared} FFN^sh_s(u_t) + sum_k g_k FFN_{sel_k}(u_t)
+ *   with every expert a SwiGLU FFN:  FFN(u) = W2 (silu(W1 u) * (W3 u)).
+ *
+ * No token is dropped (no capacity limit).  Shared experts are always active
+ * with weight one.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP), row-major, densely packed,
+ *    unless stated otherwise.  The caller owns all memory; the library never
+ *    allocates or frees device memory and keeps no global state, so calls on
+ *    different streams may run concurrently (with distinct workspaces).
+ *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
+ *    (a hipStream_t, NULL = the null stream) and return without waiting.
+ *  - Validation errors are returned before anything is enqueued.  A failed
+ *    kernel launch returns MOE_ERR_HIP.
+ *  - Results are bitwise reproducible for identical inputs and shapes (no
+ *    floating-point atomics; the expert-contiguous order is stable).
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad descriptor field or NULL required pointer */
+  MOE_ERR_WORKSPACE = -2,   /* workspace NULL or smaller than required       */
+  MOE_ERR_UNSUPPORTED = -3, /* valid layer, but a shape this build rejects   */
+  MOE_ERR_ALIAS = -4,       /* out overlaps x                                 */
+  MOE_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed     */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_t;
+
+/* Shape and routing options of one MoE layer. */
+typedef struct {
+  int32_t T;            /* tokens (rows of x and out), >= 0                    */
+  int32_t d;            /* hidden size, >= 1                                    */
+  int32_t n_routed;     /* mN routed experts, 1..256                           */
+  int32_t top_k;        /* mK kept per token, 1..min(n_routed, 32)             */
+  int32_t inner;        /* routed expert SwiGLU inner size, >= 1               */
+  int32_t n_shared;     /* K_s always-active shared experts, >= 0              */
+  int32_t shared_inner; /* shared expert inner size (ignored if n_shared == 0) */
+  int32_t n_groups;     /* expert groups for group-limited routing (1 = off);
+                           must divide n_routed, <= 64                          */
+  int32_t topk_groups;  /* groups kept per token, 1..n_groups, and
+                           topk_groups * (n_routed / n_groups) >= top_k        */
+  int32_t score;        /* moe_score_t                                          */
+  int32_t norm_topk;    /* 1: kept gate weights renormalised to sum to 1       */
+  float routed_scale;   /* factor on the routed gate weights (1.0 = none)      */
+  int32_t dtype;        /* moe_dtype_t of x, out and all expert weights        */
+} moe_layer_desc_t;
+
+/* One set of expert weights, stacked over E experts (E = n_routed or
+ * n_shared), in the output-major layout of a linear layer's weight:
+ *   w1, w3 : [E][inner][d]   (gate and up projections, d -> inner)
+ *   w2     : [E][d][inner]   (down projection, inner -> d)
+ * dtype = desc->dtype. */
+typedef struct {
+  const void* w1;
+  const void* w3;
+  const void* w2;
+} moe_ffn_weights_t;
+
+/* Byte offsets of the intermediate buffers inside the workspace, for
+ * inspection after a forward call has completed (-1 = not materialised).
+ * Element types: *_i32 int32, *_f32 float, others desc->dtype.  Rows of
+ * xp / h_routed / y are in expert-contiguous order (expert ascending, token
+ * ascending); row r came from token row_src[r]. */
+typedef struct {
+  int64_t topk_idx_i32;     /* [T][top_k]                                     */
+  int64_t topk_w_f32;       /* [T][top_k]                                     */
+  int64_t counts_i32;       /* [n_routed] tokens per routed expert            */
+  int64_t offsets_i32;      /* [n_routed + 1] exclusive prefix sum of counts  */
+  int64_t slot_row_i32;     /* [T][top_k] row of token t's k-th expert        */
+  int64_t row_src_i32;      /* [T * top_k] source token of each row           */
+  int64_t xp;               /* [T * top_k][d] gathered token rows             */
+  int64_t h_routed;         /* [T * top_k][inner] silu(W1 u) * (W3 u)         */
+  int64_t h_shared;         /* [T][n_shared * shared_inner]                   */
+  int64_t y;                /* [T * top_k][d] routed expert outputs           */
+  int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32)        */
+  int64_t total_bytes;      /* = moe_layer_workspace_size                     */
+} moe_workspace_layout_t;
+
+/* Host-only check of a descriptor; no device call.  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG (including desc == NULL) or MOE_ERR_UNSUPPORTED
+ * (bf16 needs d, inner and shared_inner to be multiples of 64; fp32 needs
+ * multiples of 4; row counts times widths must stay below 2^31). */
+moe_status_t moe_layer_validate(const moe_layer_desc_t* desc);
+
+/* Workspace bytes moe_layer_forward needs for `desc` (host-only).  `bytes`
+ * must be non-NULL.  Validates desc first. */
+moe_status_t moe_layer_workspace_size(const moe_layer_desc_t* desc,
+                                      size_t* bytes);
+
+/* Offsets of the intermediates inside the workspace (host-only). */
+moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
+                                        moe_workspace_layout_t* layout);
+
+/* The layer forward pass.
+ *   x            [T][d] dtype                        (required if T > 0)
+ *   w_gate       [n_routed][d] float                 (required)
+ *   logit_bias   [n_routed] float or NULL: added to the gate logits, so it
+ *                changes both the choice and the weights
+ *   select_bias  [n_routed] float or NULL: added to the scores for choosing
+ *                experts only; weights use the unbiased scores
+ *   routed       weights of the n_routed routed experts    (required)
+ *   shared       weights of the n_shared shared experts (ignored if 0)
+ *   out          [T][d] dtype, written; must not overlap x (MOE_ERR_ALIAS)
+ *   topk_idx     [T][top_k] int32 or NULL: kept experts, key descending
+ *   topk_w       [T][top_k] float or NULL: their gate weights g
+ *   expert_counts [n_routed] int32 or NULL: tokens routed to each expert
+ *   workspace    device scratch of >= moe_layer_workspace_size bytes,
+ *                256-byte aligned; contents on entry are ignored
+ *   stream       hipStream_t (NULL = null stream)
+ * T == 0 is valid and enqueues nothing. */
+moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
+                               const float* w_gate, const float* logit_bias,
+                               const float* select_bias,
+                               moe_ffn_weights_t routed,
+                               moe_ffn_weights_t shared, void* out,
+                               int32_t* topk_idx, float* topk_w,
+                               int32_t* expert_counts, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Number of kernel stages moe_layer_forward_traced brackets with events,
+ * and the name of stage i (NULL if out of range). */
+int32_t moe_layer_trace_stage_count(void);
+const char* moe_layer_trace_stage_name(int32_t i);
+
+/* moe_layer_forward, with hipEvent_t events[i] recorded on `stream` before
+ * stage i and events[n] after the last stage (n = stage count), so the
+ * caller can time every stage.  `events` holds n + 1 created events
+ * (MOE_ERR_INVALID_ARG if n_events is smaller).  Otherwise identical. */
+moe_status_t moe_layer_forward_traced(
+    const moe_layer_desc_t* desc, const void* x, const float* w_gate,
+    const float* logit_bias, const float* select_bias,
+    moe_ffn_weights_t routed, moe_ffn_weights_t shared, void* out,
+    int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
+    size_t workspace_bytes, void* stream, void* const* events,
+    int32_t n_events);
+
+/* Static description of a status code. */
+const char* moe_strerror(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_H */

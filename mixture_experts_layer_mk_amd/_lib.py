@@ -1,0 +1,267 @@
+"""ctypes binding of ``libmoe_layer.so`` (C ABI in ``include/moe_layer.h``).
+
+Argument marshalling only: shapes are read off the torch tensors, device
+pointers and the current HIP stream are passed through, and every step of the
+layer runs in the library's HIP kernels.  If the library has not been built
+the binding raises instead of computing anything another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_layer.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe_layer.h")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_WORKSPACE = -2
+MOE_ERR_UNSUPPORTED = -3
+MOE_ERR_ALIAS = -4
+MOE_ERR_HIP = -5
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+
+
+class MoeLayerDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("n_routed", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inner", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("shared_inner", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("norm_topk", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class FfnWeights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "topk_idx_i32", "topk_w_f32", "counts_i32", "offsets_i32",
+        "slot_row_i32", "row_src_i32", "xp", "h_routed", "h_shared", "y",
+        "s_f32", "total_bytes")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library (raises RuntimeError if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_mk_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(MoeLayerDesc)
+    lib.moe_layer_validate.argtypes = [D]
+    lib.moe_layer_validate.restype = ctypes.c_int
+    lib.moe_layer_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_layer_workspace_size.restype = ctypes.c_int
+    lib.moe_layer_workspace_layout.argtypes = [D, ctypes.POINTER(WorkspaceLayout)]
+    lib.moe_layer_workspace_layout.restype = ctypes.c_int
+    fwd = [D, P, P, P, P, FfnWeights, FfnWeights, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.moe_layer_forward.argtypes = fwd
+    lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_forward_traced.argtypes = fwd + [ctypes.POINTER(P), ctypes.c_int32]
+    lib.moe_layer_forward_traced.restype = ctypes.c_int
+    lib.moe_layer_trace_stage_count.argtypes = []
+    lib.moe_layer_trace_stage_count.restype = ctypes.c_int32
+    lib.moe_layer_trace_stage_name.argtypes = [ctypes.c_int32]
+    lib.moe_layer_trace_stage_name.restype = ctypes.c_char_p
+    lib.moe_strerror.argtypes = [ctypes.c_int]
+    lib.moe_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions ``include/moe_layer.h`` declares."""
+    import re
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def strerror(status: int) -> str:
+    return load_library().moe_strerror(status).decode()
+
+
+def make_desc(T, d, n_routed, top_k, inner, n_shared=0, shared_inner=0, *,
+              n_groups=1, topk_groups=1, score="softmax", norm_topk=False,
+              routed_scale=1.0, dtype="bf16") -> MoeLayerDesc:
+    return MoeLayerDesc(
+        T=T, d=d, n_routed=n_routed, top_k=top_k, inner=inner,
+        n_shared=n_shared, shared_inner=shared_inner, n_groups=n_groups,
+        topk_groups=topk_groups,
+        score={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score]
+        if isinstance(score, str) else int(score),
+        norm_topk=int(bool(norm_topk)), routed_scale=float(routed_scale),
+        dtype={"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
+        if isinstance(dtype, str) else int(dtype))
+
+
+def validate(desc: Optional[MoeLayerDesc]) -> int:
+    lib = load_library()
+    return lib.moe_layer_validate(ctypes.byref(desc) if desc is not None else None)
+
+
+def workspace_size(desc: MoeLayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().moe_layer_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return n.value
+
+
+def workspace_layout(desc: MoeLayerDesc) -> dict:
+    lay = WorkspaceLayout()
+    st = load_library().moe_layer_workspace_layout(ctypes.byref(desc), ctypes.byref(lay))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return {n: getattr(lay, n) for n, _ in WorkspaceLayout._fields_}
+
+
+def trace_stage_names() -> list:
+    lib = load_library()
+    return [lib.moe_layer_trace_stage_name(i).decode()
+            for i in range(lib.moe_layer_trace_stage_count())]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, dtype, shape, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
+                      K: int, *, score: str = "softmax", norm_topk: bool = False,
+                      n_groups: int = 1, topk_groups: int = 1, select_bias=None,
+                      logit_bias=None, routed_scale: float = 1.0,
+                      return_routing: bool = False, out=None, workspace=None,
+                      stream=None, trace_events=None):
+    """DeepSeekMoE layer forward on the GPU.
+
+    x [T, d] (bf16 or fp32), W_gate [E, d] fp32, experts = (w1 [E, I, d],
+    w3 [E, I, d], w2 [E, d, I]), shared = same with K_s experts or None,
+    K routed experts kept per token.  Returns out [T, d] (and, with
+    ``return_routing``, a dict with topk_idx [T, K] int32, topk_w [T, K] fp32
+    and expert_counts [E] int32).  ``workspace`` (uint8, >= workspace_size)
+    may be passed to reuse one buffer; ``trace_events`` (a list of n + 1 raw
+    hipEvent_t handles) records every stage boundary."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    dt = x.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {dt}")
+    T, d = x.shape
+    w1, w3, w2 = experts
+    E, I = w1.shape[0], w1.shape[1]
+    Ks, Is = (shared[0].shape[0], shared[0].shape[1]) if shared is not None else (0, 0)
+    _check_tensor("x", x, dt, (T, d), dev)
+    _check_tensor("W_gate", W_gate, torch.float32, (E, d), dev)
+    _check_tensor("experts.w1", w1, dt, (E, I, d), dev)
+    _check_tensor("experts.w3", w3, dt, (E, I, d), dev)
+    _check_tensor("experts.w2", w2, dt, (E, d, I), dev)
+    if shared is not None:
+        _check_tensor("shared.w1", shared[0], dt, (Ks, Is, d), dev)
+        _check_tensor("shared.w3", shared[1], dt, (Ks, Is, d), dev)
+        _check_tensor("shared.w2", shared[2], dt, (Ks, d, Is), dev)
+    for name, b in (("select_bias", select_bias), ("logit_bias", logit_bias)):
+        if b is not None:
+            _check_tensor(name, b, torch.float32, (E,), dev)
+    desc = make_desc(T, d, E, K, I, Ks, Is, n_groups=n_groups,
+                     topk_groups=topk_groups, score=score, norm_topk=norm_topk,
+                     routed_scale=routed_scale,
+                     dtype="bf16" if dt == torch.bfloat16 else "f32")
+    st = lib.moe_layer_validate(ctypes.byref(desc))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_tensor("out", out, dt, (T, d), dev)
+    nbytes = workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    idx = wts = cnt = None
+    if return_routing:
+        idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+        cnt = torch.empty((E,), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ffn_r = FfnWeights(w1.data_ptr(), w3.data_ptr(), w2.data_ptr())
+    ffn_s = (FfnWeights(shared[0].data_ptr(), shared[1].data_ptr(), shared[2].data_ptr())
+             if shared is not None else FfnWeights(None, None, None))
+    args = [ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias),
+            _ptr(select_bias), ffn_r, ffn_s, _ptr(out), _ptr(idx), _ptr(wts),
+            _ptr(cnt), workspace.data_ptr(), workspace.numel(), stream]
+    if trace_events is None:
+        st = lib.moe_layer_forward(*args)
+    else:
+        arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
+        st = lib.moe_layer_forward_traced(*args, arr, len(trace_events))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    if return_routing:
+        return out, {"topk_idx": idx, "topk_w": wts, "expert_counts": cnt}
+    return out
+
+
+class HipEvents:
+    """A set of HIP events (hipEventCreate) for ``trace_events``, with
+    elapsed-time queries.  Thin ctypes wrapper of the HIP runtime."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self.hip.hipEventSynchronize(self.handles[j])
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i],
+                                        self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(h)
+        self.handles = []

@@ -1,0 +1,112 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Element helpers
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaN stays a quiet NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+    return static_cast<bf16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Load one element as fp32 / store fp32 as the element type.
+template <typename T> __device__ __forceinline__ float ld_f32(const T* p);
+template <> __device__ __forceinline__ float ld_f32<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld_f32<bf16_t>(const bf16_t* p) {
+  return bf16_to_f32(*p);
+}
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
+  return f32_to_bf16(v);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (byte offsets; -1 = absent)
+// ---------------------------------------------------------------------------
+struct Layout {
+  int64_t topk_idx, topk_w, rank, block_counts, block_base, counts, offsets,
+      tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, s, total;
+  int32_t nblk;       // router workgroups (histogram blocks)
+  int32_t bm;         // rows per GEMM M-tile
+  int32_t max_mtiles; // upper bound on routed M-tiles
+};
+
+// Tile of the routed grouped GEMMs: rows [row0, row0 + rows) of expert e.
+struct MTile {
+  int32_t expert, row0, rows, pad;
+};
+
+constexpr int MAX_EXPERTS = 256;
+constexpr int MAX_TOPK = 32;
+constexpr int MAX_GROUPS = 64;
+
+// ---------------------------------------------------------------------------
+// Launchers (each in the .hip file that holds its kernel)
+// ---------------------------------------------------------------------------
+struct RouterArgs {
+  const void* x; int dtype;   // 0 = f32, 1 = bf16
+  const float* w_gate; const float* logit_bias; const float* select_bias;
+  int T, d, E, K, score, n_groups, topk_groups, norm_topk;
+  float routed_scale;
+  int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+int router_tokens_per_block(int T);   // tokens per router workgroup
+
+struct ScanArgs {
+  const int32_t* block_counts; int32_t* block_base; int32_t* counts;
+  int32_t* user_counts; int32_t* offsets; MTile* tiles; int32_t* n_tiles;
+  int nblk, E, bm;
+};
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+struct PermuteArgs {
+  const void* x; int dtype; int T, d, K, E, rt;   // rt: router tokens/block
+  const int32_t* topk_idx; const int32_t* rank; const int32_t* block_base;
+  const int32_t* offsets; int32_t* slot_row; int32_t* row_src; void* xp;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// Grouped GEMM stages.
+//  GATEUP : H[r][c] = silu(A W1^T) * (A W3^T)   A = xp rows (routed) or x (shared)
+//  DOWN   : Y[r][n] = H W2^T                     routed rows
+//  DOWN_SHARED : S[t][n] = x[t][n] + sum_s H_s W2_s^T   (fp32)
+struct GemmArgs {
+  int mode;           // 0 GATEUP, 1 DOWN, 2 DOWN_SHARED
+  bool shared;        // GATEUP: the shared-expert group (rows = tokens)
+  const void* a; int lda;        // activation rows
+  const void* w1; const void* w3; const void* w2;
+  int d, inner, n_experts;       // inner of the group; n_experts in group
+  void* out; int ldo;            // H (dtype) / Y (dtype) / S (f32)
+  const void* x;                 // DOWN_SHARED residual
+  const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
+  int T;                          // rows for shared group
+  int bm;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const void* base; bool base_f32;   // S (f32) or x (dtype) when no shared
+  const void* y; const float* topk_w; const int32_t* slot_row;
+  void* out; int dtype; int T, d, K;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,321 @@
+// Host side of the C ABI (include/moe_layer.h): validation, workspace
+// layout, and the kernel sequence of one layer forward pass, enqueued on the
+// caller's stream with no host synchronisation and no device allocation.
+#include "moe_layer.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kStages = 8;
+const char* const kStageNames[kStages] = {
+    "router",            "scan",             "permute",
+    "gemm_gateup_routed", "gemm_gateup_shared", "gemm_down_routed",
+    "gemm_down_shared",  "combine"};
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+int elem_size(const moe_layer_desc_t& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+
+// Rows per routed M-tile: large tiles when experts receive many rows, smaller
+// ones when the average expert group is short (weight-streaming regime).
+int choose_bm(const moe_layer_desc_t& d) {
+  if (d.dtype != MOE_BF16) return 64;
+  const int64_t avg = (int64_t)d.T * d.top_k / d.n_routed;
+  if (avg >= 192) return 256;
+  if (avg >= 96) return 128;
+  return 64;
+}
+
+moe_status_t validate(const moe_layer_desc_t* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->d < 1 || d->n_routed < 1 || d->inner < 1) return MOE_ERR_INVALID_ARG;
+  if (d->top_k < 1 || d->top_k > d->n_routed) return MOE_ERR_INVALID_ARG;
+  if (d->n_shared < 0 || (d->n_shared > 0 && d->shared_inner < 1)) return MOE_ERR_INVALID_ARG;
+  if (d->n_groups < 1 || d->n_routed % d->n_groups != 0) return MOE_ERR_INVALID_ARG;
+  if (d->topk_groups < 1 || d->topk_groups > d->n_groups) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)d->topk_groups * (d->n_routed / d->n_groups) < d->top_k)
+    return MOE_ERR_INVALID_ARG;
+  if (d->score != MOE_SCORE_SOFTMAX && d->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(d->routed_scale)) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->n_routed > MAX_EXPERTS || d->top_k > MAX_TOPK || d->n_groups > MAX_GROUPS)
+    return MOE_ERR_UNSUPPORTED;
+  const int q = d->dtype == MOE_BF16 ? 64 : 4;
+  if (d->d % q || d->inner % q || (d->n_shared > 0 && d->shared_inner % q))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)d->T * d->top_k;
+  const int64_t lim = int64_t(1) << 31;
+  if (rows * d->d >= lim || rows * d->inner >= lim ||
+      (int64_t)d->T * d->n_shared * d->shared_inner >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Layout layout_of(const moe_layer_desc_t& d) {
+  Layout L;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t esz = elem_size(d);
+  const int64_t TK = (int64_t)d.T * d.top_k;
+  const int rt = router_tokens_per_block(d.T);
+  L.nblk = (d.T + rt - 1) / rt;
+  L.bm = choose_bm(d);
+  L.max_mtiles = (int32_t)((TK + (int64_t)d.n_routed * (L.bm - 1)) / L.bm);
+  L.topk_idx = take(TK * 4);
+  L.topk_w = take(TK * 4);
+  L.rank = take(TK * 4);
+  L.block_counts = take((int64_t)L.nblk * d.n_routed * 4);
+  L.block_base = take((int64_t)L.nblk * d.n_routed * 4);
+  L.counts = take((int64_t)d.n_routed * 4);
+  L.offsets = take((int64_t)(d.n_routed + 1) * 4);
+  L.tiles = take((int64_t)L.max_mtiles * (int64_t)sizeof(MTile));
+  L.n_tiles = take(4);
+  L.slot_row = take(TK * 4);
+  L.row_src = take(TK * 4);
+  L.xp = take(TK * d.d * esz);
+  L.h_routed = take(TK * d.inner * esz);
+  L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
+  L.y = take(TK * d.d * esz);
+  L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
+  L.total = off;
+  return L;
+}
+
+bool overlaps(const void* a, const void* b, size_t n) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + n && pb < pa + n;
+}
+
+moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
+                          const float* w_gate, const float* logit_bias,
+                          const float* select_bias, moe_ffn_weights_t routed,
+                          moe_ffn_weights_t shared, void* out,
+                          int32_t* topk_idx, float* topk_w,
+                          int32_t* expert_counts, void* workspace,
+                          size_t workspace_bytes, void* stream_ptr,
+                          void* const* events) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_layer_desc_t& d = *desc;
+  if (!w_gate || !routed.w1 || !routed.w3 || !routed.w2) return MOE_ERR_INVALID_ARG;
+  if (d.n_shared > 0 && (!shared.w1 || !shared.w3 || !shared.w2)) return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+  if (d.T == 0) {   // nothing to compute
+    for (int i = 0; i <= kStages; ++i)
+      if (!mark(i)) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
+  const Layout L = layout_of(d);
+  if (!workspace || workspace_bytes < (size_t)L.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return MOE_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)d.T * d.d * elem_size(d);
+  if (overlaps(x, out, xbytes)) return MOE_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
+  int32_t* idx = topk_idx ? topk_idx : static_cast<int32_t*>(at(L.topk_idx));
+  float* gw = topk_w ? topk_w : static_cast<float*>(at(L.topk_w));
+  const bool bf16 = d.dtype == MOE_BF16;
+  hipError_t err;
+#define MOE_CHECK(call)                      \
+  do {                                       \
+    err = (call);                            \
+    if (err != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+  // 1. router
+  if (!mark(0)) return MOE_ERR_HIP;
+  {
+    RouterArgs r{};
+    r.x = x; r.dtype = bf16 ? 1 : 0;
+    r.w_gate = w_gate; r.logit_bias = logit_bias; r.select_bias = select_bias;
+    r.T = d.T; r.d = d.d; r.E = d.n_routed; r.K = d.top_k; r.score = d.score;
+    r.n_groups = d.n_groups; r.topk_groups = d.topk_groups; r.norm_topk = d.norm_topk;
+    r.routed_scale = d.routed_scale;
+    r.topk_idx = idx; r.topk_w = gw;
+    r.rank = static_cast<int32_t*>(at(L.rank));
+    r.block_counts = static_cast<int32_t*>(at(L.block_counts));
+    MOE_CHECK(launch_router(r, s));
+  }
+  // 2. scan + tile schedule
+  if (!mark(1)) return MOE_ERR_HIP;
+  MTile* tiles = static_cast<MTile*>(at(L.tiles));
+  int32_t* n_tiles = static_cast<int32_t*>(at(L.n_tiles));
+  {
+    ScanArgs c{};
+    c.block_counts = static_cast<const int32_t*>(at(L.block_counts));
+    c.block_base = static_cast<int32_t*>(at(L.block_base));
+    c.counts = static_cast<int32_t*>(at(L.counts));
+    c.user_counts = expert_counts;
+    c.offsets = static_cast<int32_t*>(at(L.offsets));
+    c.tiles = tiles; c.n_tiles = n_tiles;
+    c.nblk = L.nblk; c.E = d.n_routed; c.bm = L.bm;
+    MOE_CHECK(launch_scan(c, s));
+  }
+  // 3. permute
+  if (!mark(2)) return MOE_ERR_HIP;
+  {
+    PermuteArgs p{};
+    p.x = x; p.dtype = bf16 ? 1 : 0; p.T = d.T; p.d = d.d; p.K = d.top_k;
+    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T);
+    p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
+    p.block_base = static_cast<const int32_t*>(at(L.block_base));
+    p.offsets = static_cast<const int32_t*>(at(L.offsets));
+    p.slot_row = static_cast<int32_t*>(at(L.slot_row));
+    p.row_src = static_cast<int32_t*>(at(L.row_src));
+    p.xp = at(L.xp);
+    MOE_CHECK(launch_permute(p, s));
+  }
+  auto gemm = [&](const GemmArgs& g) {
+    return bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+  };
+  GemmArgs base{};
+  base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
+  base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
+  // 4. routed gate/up
+  if (!mark(3)) return MOE_ERR_HIP;
+  {
+    GemmArgs g = base;
+    g.mode = 0; g.shared = false; g.a = at(L.xp); g.lda = d.d;
+    g.w1 = routed.w1; g.w3 = routed.w3; g.inner = d.inner; g.n_experts = d.n_routed;
+    g.out = at(L.h_routed); g.ldo = d.inner;
+    MOE_CHECK(gemm(g));
+  }
+  // 5. shared gate/up
+  if (!mark(4)) return MOE_ERR_HIP;
+  if (d.n_shared > 0) {
+    GemmArgs g = base;
+    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
+    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.h_shared); g.ldo = d.n_shared * d.shared_inner;
+    MOE_CHECK(gemm(g));
+  }
+  // 6. routed down
+  if (!mark(5)) return MOE_ERR_HIP;
+  {
+    GemmArgs g = base;
+    g.mode = 1; g.a = at(L.h_routed); g.lda = d.inner;
+    g.w2 = routed.w2; g.inner = d.inner; g.n_experts = d.n_routed;
+    g.out = at(L.y); g.ldo = d.d;
+    MOE_CHECK(gemm(g));
+  }
+  // 7. shared down (+ residual, fp32)
+  if (!mark(6)) return MOE_ERR_HIP;
+  if (d.n_shared > 0) {
+    GemmArgs g = base;
+    g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;
+    g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.s); g.ldo = d.d;
+    MOE_CHECK(gemm(g));
+  }
+  // 8. combine
+  if (!mark(7)) return MOE_ERR_HIP;
+  {
+    CombineArgs c{};
+    c.base = d.n_shared > 0 ? at(L.s) : x;
+    c.base_f32 = d.n_shared > 0;
+    c.y = at(L.y); c.topk_w = gw; c.slot_row = static_cast<const int32_t*>(at(L.slot_row));
+    c.out = out; c.dtype = bf16 ? 1 : 0; c.T = d.T; c.d = d.d; c.K = d.top_k;
+    MOE_CHECK(launch_combine(c, s));
+  }
+  if (!mark(8)) return MOE_ERR_HIP;
+#undef MOE_CHECK
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_layer_validate(const moe_layer_desc_t* desc) { return validate(desc); }
+
+moe_status_t moe_layer_workspace_size(const moe_layer_desc_t* desc, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  *bytes = (size_t)layout_of(*desc).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
+                                        moe_workspace_layout_t* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const Layout L = layout_of(*desc);
+  out->topk_idx_i32 = L.topk_idx;
+  out->topk_w_f32 = L.topk_w;
+  out->counts_i32 = L.counts;
+  out->offsets_i32 = L.offsets;
+  out->slot_row_i32 = L.slot_row;
+  out->row_src_i32 = L.row_src;
+  out->xp = L.xp;
+  out->h_routed = L.h_routed;
+  out->h_shared = L.h_shared;
+  out->y = L.y;
+  out->s_f32 = L.s;
+  out->total_bytes = L.total;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
+                               const float* w_gate, const float* logit_bias,
+                               const float* select_bias, moe_ffn_weights_t routed,
+                               moe_ffn_weights_t shared, void* out, int32_t* topk_idx,
+                               float* topk_w, int32_t* expert_counts, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
+                      topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+int32_t moe_layer_trace_stage_count(void) { return kStages; }
+
+const char* moe_layer_trace_stage_name(int32_t i) {
+  return (i >= 0 && i < kStages) ? kStageNames[i] : nullptr;
+}
+
+moe_status_t moe_layer_forward_traced(
+    const moe_layer_desc_t* desc, const void* x, const float* w_gate,
+    const float* logit_bias, const float* select_bias, moe_ffn_weights_t routed,
+    moe_ffn_weights_t shared, void* out, int32_t* topk_idx, float* topk_w,
+    int32_t* expert_counts, void* workspace, size_t workspace_bytes, void* stream,
+    void* const* events, int32_t n_events) {
+  if (!events || n_events < kStages + 1) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i <= kStages; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
+                      topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
+                      stream, events);
+}
+
+const char* moe_strerror(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "success";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_UNSUPPORTED: return "layer shape not supported by this build";
+    case MOE_ERR_ALIAS: return "out overlaps x";
+    case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

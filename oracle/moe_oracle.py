@@ -219,14 +219,17 @@ def moe_forward(x, w_gate, routed, shared, top_k: int, *, n_shared: int = 0,
         w1, w3, w2 = shared_fn(s_i)
         y += swiglu_ffn(x64, w1, w3, w2)
         macs += T * 3 * d * np.asarray(w1).shape[0]
+    # Each kept expert's FFN output for each (token, slot); every expert's
+    # weights are fetched once, for all rows that chose it.
     routed_fn = _as_expert_fn(routed)
+    contrib = np.zeros((T, top_k, d))
+    for e in np.unique(r.idx):
+        tt, kk = np.nonzero(r.idx == e)
+        w1, w3, w2 = routed_fn(int(e))
+        contrib[tt, kk] = swiglu_ffn(x64[tt], w1, w3, w2)
+        macs += tt.size * 3 * d * np.asarray(w1).shape[0]
     for k in range(top_k):
-        col = r.idx[:, k]
-        for e in np.unique(col):
-            rows = np.nonzero(col == e)[0]
-            w1, w3, w2 = routed_fn(int(e))
-            y[rows] += r.g[rows, k, None] * swiglu_ffn(x64[rows], w1, w3, w2)
-            macs += rows.size * 3 * d * np.asarray(w1).shape[0]
+        y += r.g[:, k, None] * contrib[:, k]
     if stats is not None:
         stats["macs"] = int(macs)
     return y, r

@@ -1,0 +1,157 @@
+"""Shared logic of the GPU parity tests: run the HIP layer and the CPU oracle
+on the same seeded inputs and compare them under the stated rules.
+
+Rules (the layer's acceptance criteria):
+* routing: for every token whose K-th and (K+1)-th selection keys (and, with
+  group-limited routing, whose kept and first dropped group scores) differ by
+  more than 1e-5, the kept experts must be exactly the oracle's.  Tokens
+  inside that margin may take any choice that is optimal within 1e-5; the
+  GPU's choice is checked for that and the output is compared with the oracle
+  run on the GPU's choice.
+* per-expert counts equal the histogram of the GPU's choices (exactly), and
+  equal the oracle's when no token is ambiguous.
+* outputs: max |err| <= 2e-2 * rms(out) for bf16 layers, <= 1e-4 * rms(out)
+  for fp32 layers, against the fp64 oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+from mixture_experts_layer_mk_amd import moe_layer_forward
+
+MARGIN = 1e-5
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+class Case:
+    """One workload: host tensors (generator output), device copies, and the
+    oracle's view of the same values."""
+
+    def __init__(self, cfg: workloads.LayerConfig, seed: int = 0, device="cuda"):
+        self.cfg = cfg
+        self.inp = workloads.make_inputs(cfg, seed)
+        self.host = self.inp.torch_tensors(
+            "cpu", progress=lambda m: print(f"[{cfg.name}] {m}", flush=True))
+        self.dev = {k: (tuple(t.to(device) for t in v) if isinstance(v, tuple)
+                        else (v.to(device) if v is not None else None))
+                    for k, v in self.host.items()}
+        h = self.host
+        self.x = h["x"].float().numpy()
+        self.w_gate = h["w_gate"].numpy()
+        self.logit_bias = None if h["logit_bias"] is None else h["logit_bias"].numpy()
+        self.select_bias = None if h["select_bias"] is None else h["select_bias"].numpy()
+
+    def routed(self, e):
+        w1, w3, w2 = self.host["routed"]
+        return (w1[e].float().numpy(), w3[e].float().numpy(), w2[e].float().numpy())
+
+    def shared(self, s):
+        w1, w3, w2 = self.host["shared"]
+        return (w1[s].float().numpy(), w3[s].float().numpy(), w2[s].float().numpy())
+
+    def run_gpu(self, **kw):
+        c, d = self.cfg, self.dev
+        return moe_layer_forward(
+            d["x"], d["w_gate"], d["routed"], d["shared"], c.top_k,
+            score=c.score, norm_topk=c.norm_topk, n_groups=c.n_groups,
+            topk_groups=c.topk_groups, select_bias=d["select_bias"],
+            logit_bias=d["logit_bias"], routed_scale=c.routed_scale,
+            return_routing=True, **kw)
+
+    def oracle_kw(self):
+        c = self.cfg
+        return dict(n_shared=c.n_shared, score=c.score, logit_bias=self.logit_bias,
+                    select_bias=self.select_bias, n_groups=c.n_groups,
+                    topk_groups=c.topk_groups, norm_topk=c.norm_topk,
+                    routed_scale=c.routed_scale)
+
+    def oracle(self, rows, forced_idx=None):
+        return oracle.moe_forward(self.x[rows], self.w_gate, self.routed,
+                                  self.shared if self.cfg.n_shared else None,
+                                  self.cfg.top_k, forced_idx=forced_idx,
+                                  **self.oracle_kw())
+
+
+def choice_is_near_optimal(keys_unmasked, choice, cfg, tol=MARGIN) -> bool:
+    """Is `choice` a top-K that is optimal up to `tol` (group limit included)?"""
+    E, K = keys_unmasked.size, cfg.top_k
+    key = keys_unmasked.astype(np.float64)
+    if len(set(choice)) != K:
+        return False
+    if cfg.n_groups > 1:
+        gs = E // cfg.n_groups
+        G = np.array([np.sort(key[g * gs:(g + 1) * gs])[-2:].sum()
+                      for g in range(cfg.n_groups)])
+        chosen_groups = sorted({int(e) // gs for e in choice})
+        if len(chosen_groups) > cfg.topk_groups:
+            return False
+        g_cut = np.sort(G)[::-1][cfg.topk_groups - 1]
+        if any(G[g] < g_cut - tol for g in chosen_groups):
+            return False
+        # kept groups: the chosen ones plus the best of the rest
+        rest = [g for g in np.argsort(-G, kind="stable") if g not in chosen_groups]
+        kept = chosen_groups + rest[:cfg.topk_groups - len(chosen_groups)]
+        eligible = [e for e in range(E) if e // gs in kept]
+    else:
+        eligible = list(range(E))
+    unchosen = [e for e in eligible if e not in set(choice)]
+    if not unchosen:
+        return True
+    return min(key[list(choice)]) >= max(key[unchosen]) - tol
+
+
+def check_case(case: Case, rows=None, out=None, routing=None):
+    """Run (unless given) the GPU layer, compare rows `rows` (default all)
+    with the oracle; return a dict of diagnostics."""
+    cfg = case.cfg
+    if out is None:
+        out, routing = case.run_gpu()
+    torch.cuda.synchronize()
+    T, K = cfg.T, cfg.top_k
+    g_idx = routing["topk_idx"].cpu().numpy()
+    g_w = routing["topk_w"].cpu().numpy()
+    g_cnt = routing["expert_counts"].cpu().numpy()
+    g_out = out.float().cpu().numpy()
+
+    # properties at any size
+    assert g_idx.min() >= 0 and g_idx.max() < cfg.n_routed
+    assert (np.sort(g_idx, 1)[:, 1:] != np.sort(g_idx, 1)[:, :-1]).all(), "repeated expert"
+    assert np.array_equal(g_cnt, np.bincount(g_idx.ravel(), minlength=cfg.n_routed))
+    assert g_cnt.sum() == T * K
+    assert np.isfinite(g_out).all()
+
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    r = oracle.route(case.x[rows], case.w_gate, K, score=cfg.score,
+                     logit_bias=case.logit_bias, select_bias=case.select_bias,
+                     n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                     norm_topk=cfg.norm_topk, routed_scale=cfg.routed_scale)
+    amb = (r.margin <= MARGIN) | (r.group_margin <= MARGIN)
+    gi = g_idx[rows]
+    same = (np.sort(gi, 1) == np.sort(r.idx, 1)).all(1)
+    bad = np.nonzero(~same & ~amb)[0]
+    assert bad.size == 0, (f"routing differs on {bad.size} unambiguous tokens, "
+                           f"e.g. row {rows[bad[0]]}: gpu {gi[bad[0]]} oracle {r.idx[bad[0]]}")
+    unmasked = r.scores.astype(np.float32)
+    if case.select_bias is not None:
+        unmasked = unmasked + case.select_bias[None, :]
+    for i in np.nonzero(amb & ~same)[0]:
+        assert choice_is_near_optimal(unmasked[i], gi[i], cfg), f"row {rows[i]}"
+    # order: keys non-increasing along k (within the tie tolerance)
+    kk = np.take_along_axis(unmasked, gi.astype(np.int64), 1).astype(np.float64)
+    assert (np.diff(kk, axis=1) <= MARGIN).all(), "kept experts not in key order"
+    if amb.sum() == 0 and rows.size == T:
+        ref_cnt = np.bincount(r.idx.ravel(), minlength=cfg.n_routed)
+        assert np.array_equal(g_cnt, ref_cnt)
+
+    # gate weights and outputs against the oracle run on the GPU's choice
+    y_ref, r_f = case.oracle(rows, forced_idx=gi)
+    np.testing.assert_allclose(g_w[rows], r_f.g, rtol=1e-5, atol=1e-7)
+    err = np.abs(g_out[rows] - y_ref).max()
+    rms = np.sqrt(np.mean(y_ref ** 2))
+    tol = TOL[cfg.dtype]
+    assert err <= tol * rms, f"max|err| {err:.3e} > {tol} * rms {rms:.3e}"
+    return {"err_over_rms": err / rms, "ambiguous": int(amb.sum()),
+            "rows": int(rows.size)}

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP layer (through the C ABI) against the CPU oracle.
+
+Sizes: every workload at reduced T (full hidden/inner/expert shapes where the
+oracle stays within seconds) compared on every token, spanning several GEMM
+tiles with ragged tails; the full-size workloads compared on sampled tokens
+plus properties that hold at any size; and the edge cases of the method.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import Case, check_case
+
+pytestmark = pytest.mark.gpu
+
+C = workloads.CONFIGS
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+REDUCED = {
+    "tiny-fp32": C["tiny-fp32"],
+    "tiny-fp32-ragged": C["tiny-fp32"].replace(T=203, seed=3),
+    "2b-T2000": C["deepseekmoe-2b"].replace(T=2000),
+    "16b-T2600": C["deepseekmoe-16b"].replace(T=2600),
+    "16b-T1000": C["deepseekmoe-16b"].replace(T=1000, seed=1),
+    "v3-d512-T4096": C["deepseek-v3"].replace(d=512, inner=256, shared_inner=256),
+    "v3-d512-T700": C["deepseek-v3"].replace(T=700, d=512, inner=256,
+                                             shared_inner=256, seed=2),
+    "skewed-16b-small": C["skewed-16b-small"],
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_all_tokens(name):
+    cfg = REDUCED[name]
+    say(f"[parity] {name}: {cfg}")
+    info = check_case(Case(cfg))
+    say(f"[parity] {name}: {info}")
+
+
+def test_tiny_fp32_routing_bit_exact():
+    """On the tiny workload no token is near a tie: indices and counts must be
+    exactly the oracle's."""
+    case = Case(C["tiny-fp32"])
+    info = check_case(case)
+    assert info["ambiguous"] == 0
+
+
+@pytest.mark.parametrize("name,n_rows", [("deepseekmoe-2b", 256),
+                                         ("deepseekmoe-16b", 256),
+                                         ("deepseek-v3", 24)])
+def test_full_size_sampled(name, n_rows):
+    cfg = C[name]
+    say(f"[parity-full] {name}: generating inputs")
+    case = Case(cfg)
+    say(f"[parity-full] {name}: running")
+    rows = np.sort(np.random.default_rng(7).choice(cfg.T, n_rows, replace=False))
+    rows[0], rows[-1] = 0, cfg.T - 1
+    info = check_case(case, rows=rows)
+    say(f"[parity-full] {name}: {info}")
+
+
+def test_deterministic_bitwise():
+    case = Case(C["deepseekmoe-16b"].replace(T=3000, seed=5))
+    o1, r1 = case.run_gpu()
+    o2, r2 = case.run_gpu()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for k in r1:
+        assert torch.equal(r1[k], r2[k])
+
+
+def test_intermediates_dispatch_exact():
+    """Counts, offsets and the expert-contiguous permutation are integers and
+    copies: exact against the oracle's dispatch of the GPU's own choices."""
+    import oracle
+    from mixture_experts_layer_mk_amd import make_desc, workspace_layout, workspace_size
+    cfg = C["deepseekmoe-16b"].replace(T=1500, seed=4)
+    case = Case(cfg)
+    desc = make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner, cfg.n_shared,
+                     cfg.shared_inner)
+    lay = workspace_layout(desc)
+    ws = torch.empty(workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out, routing = case.run_gpu(workspace=ws)
+    torch.cuda.synchronize()
+    T, K, d, E = cfg.T, cfg.top_k, cfg.d, cfg.n_routed
+
+    def view(off, n, dt):
+        nbytes = n * torch.empty((), dtype=dt).element_size()
+        return ws[off:off + nbytes].view(dt).cpu()
+    idx = routing["topk_idx"].cpu().numpy()
+    dsp = oracle.dispatch(idx, E)
+    assert np.array_equal(view(lay["counts_i32"], E, torch.int32).numpy(), dsp.counts)
+    assert np.array_equal(view(lay["offsets_i32"], E + 1, torch.int32).numpy(), dsp.offsets)
+    assert np.array_equal(view(lay["row_src_i32"], T * K, torch.int32).numpy(), dsp.row_src)
+    assert np.array_equal(view(lay["slot_row_i32"], T * K, torch.int32).numpy().reshape(T, K),
+                          dsp.slot_row)
+    xp = view(lay["xp"], T * K * d, torch.bfloat16).view(T * K, d)
+    assert torch.equal(xp, case.host["x"][torch.from_numpy(dsp.row_src)])
+
+
+def test_T_zero_and_one():
+    case = Case(C["deepseekmoe-16b"].replace(T=1))
+    check_case(case)
+    d = case.dev
+    x0 = d["x"][:0]
+    from mixture_experts_layer_mk_amd import moe_layer_forward
+    out = moe_layer_forward(x0, d["w_gate"], d["routed"], d["shared"], 6)
+    assert out.shape == (0, 2048)
+
+
+def test_all_experts_kept_and_no_shared():
+    cfg = C["deepseekmoe-16b"].replace(T=333, n_routed=8, top_k=8, n_shared=0,
+                                       d=256, inner=128)
+    check_case(Case(cfg))
+
+
+def test_dense_reduction_bf16():
+    """mN = mK = 1, K_s = 0: every token goes to the one expert with weight 1."""
+    cfg = C["deepseekmoe-16b"].replace(T=777, n_routed=1, top_k=1, n_shared=0,
+                                       d=512, inner=384)
+    case = Case(cfg)
+    info = check_case(case)
+    out, routing = case.run_gpu()
+    assert (routing["topk_w"] == 1.0).all() and (routing["topk_idx"] == 0).all()
+    assert info["ambiguous"] == 0
+
+
+def test_zero_gate_ties_take_lowest_index():
+    """A zero gate makes every score equal: both sides keep experts 0..K-1."""
+    cfg = C["deepseekmoe-16b"].replace(T=300, d=256, inner=128, shared_inner=128)
+    case = Case(cfg)
+    case.dev["w_gate"].zero_()
+    out, routing = case.run_gpu()
+    idx = routing["topk_idx"].cpu().numpy()
+    assert (idx == np.arange(6)[None, :]).all()
+    assert np.allclose(routing["topk_w"].cpu().numpy(), 1 / 64)
+
+
+def test_disabled_experts_never_chosen():
+    """A logit bias of -inf switches experts off (the top-expert ablation is
+    expressed this way): they get no tokens, the rest of the layer is exact."""
+    cfg = C["deepseekmoe-16b"].replace(T=500, d=256, inner=128, shared_inner=128)
+    case = Case(cfg)
+    lb = torch.zeros(64, dtype=torch.float32)
+    lb[[0, 5, 17, 63]] = -float("inf")
+    case.dev["logit_bias"] = lb.cuda()
+    case.logit_bias = lb.numpy()
+    info = check_case(case)
+    out, routing = case.run_gpu()
+    cnt = routing["expert_counts"].cpu().numpy()
+    assert (cnt[[0, 5, 17, 63]] == 0).all()
+
+
+def test_routed_scale():
+    cfg = C["deepseekmoe-16b"].replace(T=400, d=256, inner=128, shared_inner=128,
+                                       routed_scale=2.5)
+    check_case(Case(cfg))

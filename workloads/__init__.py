@@ -206,7 +206,7 @@ class Inputs:
         return self._expert(TAG_SHARED, s, self.cfg.shared_inner)
 
     # -- device tensors -----------------------------------------------------
-    def torch_tensors(self, device="cpu"):
+    def torch_tensors(self, device="cpu", progress=None):
         """All tensors as torch tensors on ``device`` (dtype bf16 or fp32).
 
         Returns a dict: x [T,d], w_gate [E,d] fp32, logit_bias / select_bias
@@ -227,6 +227,8 @@ class Inputs:
                 w1[i] = torch.from_numpy(a).to(tdt)
                 w3[i] = torch.from_numpy(b).to(tdt)
                 w2[i] = torch.from_numpy(c).to(tdt)
+                if progress is not None and (i + 1) % 32 == 0:
+                    progress(f"generated {i + 1}/{n} experts")
             with ThreadPoolExecutor(_threads()) as ex:
                 list(ex.map(fill, range(n)))
             return tuple(t.to(device) for t in (w1, w3, w2))
