@@ -88,19 +88,20 @@ typedef struct {
 /* Byte offsets of the intermediate buffers inside the workspace, for
  * inspection after a forward call has completed (-1 = not materialised).
  * Element types: *_i32 int32, *_f32 float, others desc->dtype.  Rows of
- * xp / h_routed / y are in expert-contiguous order (expert ascending, token
+ * xp / h_routed / y_f32 are in expert-contiguous order (expert ascending, token
  * ascending); row r came from token row_src[r]. */
 typedef struct {
-  int64_t topk_idx_i32;     /* [T][top_k]                                     */
-  int64_t topk_w_f32;       /* [T][top_k]                                     */
+  int64_t topk_idx_i32;     /* [T][top_k]; written only when topk_idx == NULL */
+  int64_t topk_w_f32;       /* [T][top_k]; written only when topk_w == NULL   */
   int64_t counts_i32;       /* [n_routed] tokens per routed expert            */
   int64_t offsets_i32;      /* [n_routed + 1] exclusive prefix sum of counts  */
   int64_t slot_row_i32;     /* [T][top_k] row of token t's k-th expert        */
   int64_t row_src_i32;      /* [T * top_k] source token of each row           */
-  int64_t xp;               /* [T * top_k][d] gathered token rows             */
+  int64_t xp;               /* [T * top_k][d] gathered token rows (-1: the
+                               expert GEMM gathers rows of x directly)        */
   int64_t h_routed;         /* [T * top_k][inner] silu(W1 u) * (W3 u)         */
   int64_t h_shared;         /* [T][n_shared * shared_inner]                   */
-  int64_t y;                /* [T * top_k][d] routed expert outputs           */
+  int64_t y_f32;            /* [T * top_k][d] routed expert outputs (fp32)    */
   int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32)        */
   int64_t total_bytes;      /* = moe_layer_workspace_size                     */
 } moe_workspace_layout_t;

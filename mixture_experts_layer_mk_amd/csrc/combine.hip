@@ -1,4 +1,4 @@
-// Combine: out[t] = base[t] + sum_k g[t,k] * Y[slot_row[t,k]], summed in slot
+// Combine: out[t] = base[t] + sum_k g[t,k] * Y[slot_row[t,k]] (Y fp32), summed in slot
 // order k = 0..K-1 in fp32 and rounded once to the output type.  base is
 // x + (shared experts) in fp32, or x itself when there are no shared experts.
 // Every output element has one owner thread: no atomics, deterministic.
@@ -28,15 +28,19 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = ld_f32<T>(b + v);
   }
-  const T* y = static_cast<const T*>(a.y);
+  const float* y = a.y;
   for (int k = 0; k < a.K; ++k) {
     const int q = t * a.K + k;
     const float g = a.topk_w[q];
-    const T* yr = y + (size_t)a.slot_row[q] * a.d + n0;
-    T yv[VEC];
-    *reinterpret_cast<uint4*>(yv) = *reinterpret_cast<const uint4*>(yr);
+    const float4* yr = reinterpret_cast<const float4*>(y + (size_t)a.slot_row[q] * a.d + n0);
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = fmaf(g, ld_f32<T>(yv + v), acc[v]);
+    for (int v = 0; v < VEC / 4; ++v) {
+      const float4 yv = yr[v];
+      acc[4 * v + 0] = fmaf(g, yv.x, acc[4 * v + 0]);
+      acc[4 * v + 1] = fmaf(g, yv.y, acc[4 * v + 1]);
+      acc[4 * v + 2] = fmaf(g, yv.z, acc[4 * v + 2]);
+      acc[4 * v + 3] = fmaf(g, yv.w, acc[4 * v + 3]);
+    }
   }
   T o[VEC];
 #pragma unroll

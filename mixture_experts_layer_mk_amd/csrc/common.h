@@ -85,15 +85,17 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
 // Grouped GEMM stages.
 //  GATEUP : H[r][c] = silu(A W1^T) * (A W3^T)   A = xp rows (routed) or x (shared)
-//  DOWN   : Y[r][n] = H W2^T                     routed rows
+//  DOWN   : Y[r][n] = H W2^T                     routed rows (fp32 out)
 //  DOWN_SHARED : S[t][n] = x[t][n] + sum_s H_s W2_s^T   (fp32)
 struct GemmArgs {
   int mode;           // 0 GATEUP, 1 DOWN, 2 DOWN_SHARED
   bool shared;        // GATEUP: the shared-expert group (rows = tokens)
   const void* a; int lda;        // activation rows
+  const int32_t* a_rows;         // optional: source row of each tile row
+                                 // (gathers token rows of x; NULL = contiguous)
   const void* w1; const void* w3; const void* w2;
   int d, inner, n_experts;       // inner of the group; n_experts in group
-  void* out; int ldo;            // H (dtype) / Y (dtype) / S (f32)
+  void* out; int ldo;            // H (dtype) / Y (f32) / S (f32)
   const void* x;                 // DOWN_SHARED residual
   const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
   int T;                          // rows for shared group
@@ -104,7 +106,7 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const void* base; bool base_f32;   // S (f32) or x (dtype) when no shared
-  const void* y; const float* topk_w; const int32_t* slot_row;
+  const float* y; const float* topk_w; const int32_t* slot_row;
   void* out; int dtype; int T, d, K;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -4,19 +4,24 @@
 // Each expert is a SwiGLU FFN W2 (silu(W1 u) * (W3 u)) (expert form of the
 // DeepSeekMoE layer; blog post "Fine-Grained Expert Segmentation (Section
 // 3.1)").  Stages (same as the fp32 path):
-//   GATEUP      H = silu(A W1^T) * (A W3^T), gate and up fused in one tile
-//   DOWN        Y = H W2^T (routed rows, bf16 out)
+//   GATEUP      H = silu(A W1^T) * (A W3^T), gate and up fused in one tile;
+//               routed tiles gather their token rows straight from x
+//   DOWN        Y = H W2^T (routed rows, fp32 out)
 //   DOWN_SHARED S = x + sum_s H_s W2_s^T (all tokens, fp32 out)
 //
 // Tiling.  A workgroup (4 waves) owns BM token rows x 256 weight rows with a
 // 64-wide k step.  Both operands are k-contiguous in memory (token rows and
-// linear-layer weight rows), so every lane moves 16-byte chunks.  Tiles are
-// double-buffered in LDS (2 x (BM + 256) x 128 B), with the 16-byte chunks
-// of each 128-byte row XOR-swizzled so the matrix-core operand reads and the
-// tile writes are free of bank conflicts.  The matrix instruction takes the
-// weight fragment as its first operand, so each lane's accumulator holds 4
-// consecutive output columns of one token row (8- or 16-byte stores).
-// For GATEUP each wave's weight rows are 50% W1 and 50% W3 for the same
+// linear-layer weight rows), so tiles move as 16-byte chunks, global -> LDS
+// directly (global_load_lds_dwordx4: no staging registers, no LDS write
+// instructions), double-buffered (2 x (BM + 256) x 128 B of LDS).  The 16-byte
+// chunks of each 128-byte LDS row are XOR-swizzled so the matrix-operand
+// reads are free of bank conflicts; a direct load writes 1 KB of consecutive
+// LDS per wave, so each lane fetches the global chunk that the swizzle puts
+// in its slot.  Operand fragments are double-buffered in registers: the LDS
+// reads of k-step kk+1 are in flight while the 16 matrix ops of kk run.
+// The matrix instruction takes the weight fragment as its first operand, so
+// each lane's accumulator holds 4 consecutive output columns of one token
+// row.  For GATEUP each wave's weight rows are half W1, half W3 for the same
 // inner columns, so silu(gate) * up is formed in registers.
 // Blocks are remapped so that each XCD (blocks are dealt round-robin over the
 // 8 XCDs) runs a contiguous range of tiles, with the M-tiles of one weight
@@ -30,15 +35,15 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int BN = 256;   // weight rows per workgroup
 constexpr int BK = 64;    // k per stage (8 chunks of 16 B)
 
-// Chunk position of 16-byte chunk c of LDS row `row` (8 chunks per row).
-// Consecutive 8 rows, and 16 rows split by bank half, hit distinct banks.
-__device__ __forceinline__ int swz(int row, int c) {
-  return c ^ (row & 7) ^ ((row >> 3) & 1);
-}
+// XOR applied to the chunk index of LDS row `row` (8 chunks per row):
+// 8 consecutive rows, and 16 rows split by bank half, hit distinct banks.
+__device__ __forceinline__ int swz_x(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int x = b & 7, j = b >> 3, q = n >> 3, r = n & 7;
@@ -51,18 +56,37 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Instruction-scheduling groups for one k-step: N_MMA matrix ops with the
+// N_DS LDS reads (of the next k-step) spread over the first half, so they
+// land well before use, and N_VM global->LDS loads spread over all of them.
+template <int N_MMA, int N_DS, int N_VM, int I = 0>
+__device__ __forceinline__ void sched_groups() {
+  if constexpr (I < N_MMA) {
+    constexpr int S = (N_MMA / 2 > 0) ? N_MMA / 2 : 1;
+    constexpr int ds = (I < S) ? (I + 1) * N_DS / S - I * N_DS / S : 0;
+    constexpr int vm = (I + 1) * N_VM / N_MMA - I * N_VM / N_MMA;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // matrix op
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // LDS read
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM
+    sched_groups<N_MMA, N_DS, N_VM, I + 1>();
+  }
+}
+
 // MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED.  WAVES_M x (4 / WAVES_M) waves.
 template <int MODE, int BM, int WAVES_M>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int A_CH = BM / 32;     // A chunks per thread per stage
-  constexpr int B_CH = BN / 32;     // B chunks per thread per stage
+  constexpr int A_LD = BM / 32;     // 1 KB direct loads per wave per stage (A)
+  constexpr int B_LD = BN / 32;     // (B)
   static_assert(MB >= 1 && NB >= 2 && (NB % 2) == 0, "tile shape");
 
-  __shared__ u32x4 As[2][BM * 8];
-  __shared__ u32x4 Bs[2][BN * 8];
+  // Two LDS buffers per operand as distinct objects: accesses name their
+  // buffer statically, so the compiler can tell the direct loads into one
+  // buffer from the operand reads of the other and need not wait between.
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
@@ -80,20 +104,27 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     row0 = mt * BM; rows = min(BM, a.T - row0); e = 0;
   }
 
-  const bf16_t* A = static_cast<const bf16_t*>(a.a);
-  const int c8 = (tid & 7) * 8;          // element offset of this thread's chunk
-  const int rbase = tid >> 3;            // first row this thread loads
+  // This lane's slot in a wave's 1 KB load block: LDS row lr (of 8) and the
+  // global chunk that belongs in slot (lane & 7) of that row.
+  const int lr = lane >> 3;
+  const int cg0 = (lane & 7) ^ lr;         // rows with (row >> 3) even
+  const int cg1 = cg0 ^ 1;                 // rows with (row >> 3) odd
 
-  // A source rows (clamped into the tile's valid rows).
-  const bf16_t* pa[A_CH];
+  // A: tile row r = (wave * A_LD + j) * 8 + lr, clamped into the valid rows.
+  const bf16_t* A = static_cast<const bf16_t*>(a.a);
+  uint32_t aoff[A_LD];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int r = min(i * 32 + rbase, rows - 1);
-    pa[i] = A + (size_t)(row0 + r) * a.lda + c8;
+  for (int j = 0; j < A_LD; ++j) {
+    const int blk = wave * A_LD + j;
+    const int r = min(blk * 8 + lr, rows - 1);
+    const int src = a.a_rows ? a.a_rows[row0 + r] : row0 + r;
+    aoff[j] = (uint32_t)src * a.lda + ((blk & 1) ? cg1 : cg0) * 8;
   }
 
-  // B source rows.
-  const bf16_t* pb[B_CH];
+  // B: tile row r = (wave * B_LD + j) * 8 + lr.
+  const bf16_t* B1;
+  const bf16_t* B3 = nullptr;
+  uint32_t boff[B_LD];
   int kdim, n0 = 0, grp = 0, inner0 = 0;
   if (MODE == 0) {
     const int half = WN / 2;                       // inner columns per wave
@@ -102,56 +133,51 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     grp = routed ? e : nt / tiles_per;
     inner0 = (routed ? nt : nt % tiles_per) * per_wg;
     const size_t wo = (size_t)grp * a.inner * a.d;
-    const bf16_t* w1 = static_cast<const bf16_t*>(a.w1) + wo;
-    const bf16_t* w3 = static_cast<const bf16_t*>(a.w3) + wo;
+    B1 = static_cast<const bf16_t*>(a.w1) + wo;
+    B3 = static_cast<const bf16_t*>(a.w3) + wo;
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int r = i * 32 + rbase;
+    for (int j = 0; j < B_LD; ++j) {
+      const int blk = wave * B_LD + j;
+      const int r = blk * 8 + lr;
       const int rw = r / WN, rr = r % WN;
       const int inner = min(inner0 + rw * half + (rr % half), a.inner - 1);
-      pb[i] = ((rr < half) ? w1 : w3) + (size_t)inner * a.d + c8;
+      boff[j] = (uint32_t)inner * a.d + ((blk & 1) ? cg1 : cg0) * 8;
     }
     kdim = a.d;
   } else {
     n0 = nt * BN;
-    const bf16_t* w2 = static_cast<const bf16_t*>(a.w2) +
-                       (MODE == 1 ? (size_t)e * a.d * a.inner : 0);
+    B1 = static_cast<const bf16_t*>(a.w2) + (MODE == 1 ? (size_t)e * a.d * a.inner : 0);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int n = min(n0 + i * 32 + rbase, a.d - 1);
-      pb[i] = w2 + (size_t)n * a.inner + c8;
+    for (int j = 0; j < B_LD; ++j) {
+      const int blk = wave * B_LD + j;
+      const int n = min(n0 + blk * 8 + lr, a.d - 1);
+      boff[j] = (uint32_t)n * a.inner + ((blk & 1) ? cg1 : cg0) * 8;
     }
     kdim = (MODE == 1) ? a.inner : a.inner * a.n_experts;
   }
   const int nk = kdim / BK;
 
-  // Element offset of k-block kb in the B rows (DOWN_SHARED walks the
-  // shared experts one after the other along k).
-  auto boff = [&](int kb) -> size_t {
-    if (MODE != 2) return (size_t)kb * BK;
-    const int k = kb * BK, s = k / a.inner;
-    return (size_t)s * a.d * a.inner + (k - s * a.inner);
-  };
-
-  u32x4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kb) {
-    const size_t ka = (size_t)kb * BK, kbo = boff(kb);
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(pa[i] + ka);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(pb[i] + kbo);
-  };
-  auto lstore = [&](int buf) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int r = i * 32 + rbase;
-      As[buf][r * 8 + swz(r, c)] = ra[i];
+  // Issue the direct loads of k-block kb into the LDS buffers (Ab, Bb).
+  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
+    const size_t ka = (size_t)kb * BK;
+    size_t kbo = ka;
+    if (MODE == 2) {   // shared experts follow one another along k
+      const int k = kb * BK, s = k / a.inner;
+      kbo = (size_t)s * a.d * a.inner + (k - s * a.inner);
     }
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int r = i * 32 + rbase;
-      Bs[buf][r * 8 + swz(r, c)] = rb[i];
+    for (int j = 0; j < A_LD; ++j)
+      __builtin_amdgcn_global_load_lds((const glb_void*)(A + aoff[j] + ka),
+                                       (lds_void*)&Ab[(wave * A_LD + j) * 64], 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < B_LD; ++j) {
+      const bf16_t* base = B1;
+      if (MODE == 0) {
+        const int r = (wave * B_LD + j) * 8;        // uniform: W1 or W3 half
+        if ((r % WN) >= WN / 2) base = B3;
+      }
+      __builtin_amdgcn_global_load_lds((const glb_void*)(base + boff[j] + kbo),
+                                       (lds_void*)&Bb[(wave * B_LD + j) * 64], 16, 0, 0);
     }
   };
 
@@ -163,37 +189,71 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int l32 = lane & 31, hi = lane >> 5;
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    if (kb + 1 < nk) gload(kb + 1);
+  // Fragment registers, two sets: one feeds the matrix ops while the other
+  // is being read from LDS.
+  bf16x8 fa0[MB], fb0[NB], fa1[MB], fb1[NB];
+  auto load_frags = [&](bf16x8* fa, bf16x8* fb, const u32x4* Ab, const u32x4* Bb,
+                        int kk) {
+    const int c = 2 * kk + hi;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = 2 * kk + hi;
-      bf16x8 af[MB], bfr[NB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = wm * WM + mb * 32 + l32;
-        af[mb] = __builtin_bit_cast(bf16x8, As[cur][r * 8 + swz(r, c)]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int r = wn * WN + nb * 32 + l32;
-        bfr[nb] = __builtin_bit_cast(bf16x8, Bs[cur][r * 8 + swz(r, c)]);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nb], af[mb],
-                                                               acc[nb][mb], 0, 0, 0);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * WM + mb * 32 + l32;
+      fa[mb] = __builtin_bit_cast(bf16x8, Ab[r * 8 + (c ^ swz_x(r))]);
     }
-    if (kb + 1 < nk) lstore(cur ^ 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = wn * WN + nb * 32 + l32;
+      fb[nb] = __builtin_bit_cast(bf16x8, Bb[r * 8 + (c ^ swz_x(r))]);
+    }
+  };
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb],
+                                                             acc[nb][mb], 0, 0, 0);
+  };
+  // Scheduling: spread the LDS reads (and the direct loads) of a k-step
+  // between its matrix ops so the matrix pipe never waits on LDS latency.
+  constexpr int N_MMA = NB * MB, N_DS = NB + MB, N_VM = A_LD + B_LD;
+  auto sched_ds = [&]() { sched_groups<N_MMA, N_DS, 0>(); };
+  auto sched_ds_vm = [&]() { sched_groups<N_MMA, N_DS, N_VM>(); };
+
+  // One k-block from buffers (Ac, Bc) while the next block streams into
+  // (An, Bn).  `next` is the block to prefetch (the last block re-loads
+  // itself into the idle buffers: no branch; nothing reads that copy).
+  auto block = [&](int next, const u32x4* Ac, const u32x4* Bc, u32x4* An, u32x4* Bn) {
+    issue(next, An, Bn);
+    load_frags(fa1, fb1, Ac, Bc, 1);
+    mma(fa0, fb0);
+    sched_ds_vm();
+    load_frags(fa0, fb0, Ac, Bc, 2);
+    mma(fa1, fb1);
+    sched_ds();
+    load_frags(fa1, fb1, Ac, Bc, 3);
+    mma(fa0, fb0);
+    sched_ds();
+    // Next block landed (own loads + barrier); every wave is done reading
+    // this block's buffers, so the following issue may overwrite them.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    load_frags(fa0, fb0, An, Bn, 0);
+    mma(fa1, fb1);
+    sched_ds();
+  };
+
+  issue(0, As0, Bs0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  load_frags(fa0, fb0, As0, Bs0, 0);
+  int kb = 0;
+  for (; kb + 2 <= nk; kb += 2) {
+    block(min(kb + 1, nk - 1), As0, Bs0, As1, Bs1);
+    block(min(kb + 2, nk - 1), As1, Bs1, As0, Bs0);
   }
+  if (kb < nk) block(kb, As0, Bs0, As1, Bs1);
 
   // ---- epilogue ----
   // acc[nb][mb][r] = D[n][m] with n = nb*32 + 8*(r/4) + 4*hi + (r%4) and
@@ -224,22 +284,24 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         }
     }
   } else if (MODE == 1) {
-    bf16_t* out = static_cast<bf16_t*>(a.out);
+    float* out = static_cast<float*>(a.out);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = wm * WM + mb * 32 + l32;
       if (m >= rows) continue;
-      bf16_t* orow = out + (size_t)(row0 + m) * a.ldo;
+      float* orow = out + (size_t)(row0 + m) * a.ldo;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
           if (n >= a.d) continue;
-          uint2 v;
-          v.x = pack2(acc[nb][mb][4 * g + 0], acc[nb][mb][4 * g + 1]);
-          v.y = pack2(acc[nb][mb][4 * g + 2], acc[nb][mb][4 * g + 3]);
-          *reinterpret_cast<uint2*>(orow + n) = v;
+          float4 v;
+          v.x = acc[nb][mb][4 * g + 0];
+          v.y = acc[nb][mb][4 * g + 1];
+          v.z = acc[nb][mb][4 * g + 2];
+          v.w = acc[nb][mb][4 * g + 3];
+          *reinterpret_cast<float4*>(orow + n) = v;
         }
     }
   } else {

@@ -4,8 +4,8 @@
 // DeepSeekMoE layer; blog post "Fine-Grained Expert Segmentation (Section
 // 3.1)").  Stages:
 //   GATEUP      H = silu(A W1^T) * (A W3^T) for every routed M-tile (A = the
-//               expert-contiguous token rows) or for all tokens through each
-//               shared expert (A = x)
+//               tile's token rows, gathered from x) or for all tokens through
+//               each shared expert (A = x)
 //   DOWN        Y = H W2^T for every routed M-tile
 //   DOWN_SHARED S = x + sum_s H_s W2_s^T over the shared experts, fp32
 #include "common.h"
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
         const int li = tid + 256 * q, r = li / FK, k = li % FK;
         const bool kin = k0 + k < Kd;
         const int rr = min(r, rows - 1);
-        As[k][r] = kin ? A[(size_t)(row0 + rr) * lda + k0 + k] : 0.f;
+        const int src = a.a_rows ? a.a_rows[row0 + rr] : row0 + rr;
+        As[k][r] = kin ? A[(size_t)src * lda + k0 + k] : 0.f;
         const int nn = n0 + r;
         const bool nin = kin && nn < nvalid;
         B1s[k][r] = nin ? B1[(size_t)nn * ldb + k0 + k] : 0.f;

@@ -83,10 +83,10 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.n_tiles = take(4);
   L.slot_row = take(TK * 4);
   L.row_src = take(TK * 4);
-  L.xp = take(TK * d.d * esz);
+  L.xp = -1;   // routed gate/up tiles gather token rows from x directly
   L.h_routed = take(TK * d.inner * esz);
   L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
-  L.y = take(TK * d.d * esz);
+  L.y = take(TK * d.d * 4);
   L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
   L.total = off;
   return L;
@@ -180,7 +180,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     p.offsets = static_cast<const int32_t*>(at(L.offsets));
     p.slot_row = static_cast<int32_t*>(at(L.slot_row));
     p.row_src = static_cast<int32_t*>(at(L.row_src));
-    p.xp = at(L.xp);
+    p.xp = nullptr;
     MOE_CHECK(launch_permute(p, s));
   }
   auto gemm = [&](const GemmArgs& g) {
@@ -193,7 +193,8 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   if (!mark(3)) return MOE_ERR_HIP;
   {
     GemmArgs g = base;
-    g.mode = 0; g.shared = false; g.a = at(L.xp); g.lda = d.d;
+    g.mode = 0; g.shared = false; g.a = x; g.lda = d.d;
+    g.a_rows = static_cast<const int32_t*>(at(L.row_src));
     g.w1 = routed.w1; g.w3 = routed.w3; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.h_routed); g.ldo = d.inner;
     MOE_CHECK(gemm(g));
@@ -231,7 +232,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     CombineArgs c{};
     c.base = d.n_shared > 0 ? at(L.s) : x;
     c.base_f32 = d.n_shared > 0;
-    c.y = at(L.y); c.topk_w = gw; c.slot_row = static_cast<const int32_t*>(at(L.slot_row));
+    c.y = static_cast<const float*>(at(L.y)); c.topk_w = gw; c.slot_row = static_cast<const int32_t*>(at(L.slot_row));
     c.out = out; c.dtype = bf16 ? 1 : 0; c.T = d.T; c.d = d.d; c.K = d.top_k;
     MOE_CHECK(launch_combine(c, s));
   }
@@ -269,7 +270,7 @@ moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
   out->xp = L.xp;
   out->h_routed = L.h_routed;
   out->h_shared = L.h_shared;
-  out->y = L.y;
+  out->y_f32 = L.y;
   out->s_f32 = L.s;
   out->total_bytes = L.total;
   return MOE_OK;
