@@ -41,7 +41,9 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t topk_idx, topk_w, rank, block_counts, block_base, counts, offsets,
-      tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, s, total;
+      tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, s, planes,
+      plog, total;
+  int32_t ds, ep;     // router: d-slices, logit row stride
   int32_t nblk;       // router workgroups (histogram blocks)
   int32_t bm;         // rows per GEMM M-tile
   int32_t max_mtiles; // upper bound on routed M-tiles
@@ -64,10 +66,26 @@ struct RouterArgs {
   const float* w_gate; const float* logit_bias; const float* select_bias;
   int T, d, E, K, score, n_groups, topk_groups, norm_topk;
   float routed_scale;
+  int ds, ep;                 // d-slices of the logits GEMM; logit row stride
+  bf16_t* planes;             // [3][E][d] gate split into bf16 parts (bf16 x)
+  float* plog;                // [ds][T][ep] partial logits
+  int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
+};
+struct LogitsArgs {
+  const bf16_t* x; const float* xf; const bf16_t* planes; const float* w_gate;
+  int T, d, E, ep, ds;
+  float* plog;
+};
+struct SelectArgs {
+  const float* plog; int ep, ds;
+  const float* logit_bias; const float* select_bias;
+  int T, E, K, score, n_groups, topk_groups, norm_topk;
+  float routed_scale;
   int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
-int router_tokens_per_block(int T);   // tokens per router workgroup
+int router_tokens_per_block(int T);   // tokens per histogram block
+int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 
 struct ScanArgs {
   const int32_t* block_counts; int32_t* block_base; int32_t* counts;
@@ -77,7 +95,7 @@ struct ScanArgs {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 
 struct PermuteArgs {
-  const void* x; int dtype; int T, d, K, E, rt;   // rt: router tokens/block
+  const void* x; int dtype; int T, d, K, E, rt, nblk;   // rt: tokens per block
   const int32_t* topk_idx; const int32_t* rank; const int32_t* block_base;
   const int32_t* offsets; int32_t* slot_row; int32_t* row_src; void* xp;
 };

@@ -10,23 +10,44 @@ namespace moe {
 
 namespace {
 
-// One workgroup; thread e owns expert e (E <= 256).
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+// Scan over router blocks, one workgroup per expert: the block's rows for
+// expert e start at block_base[e][b] (relative to the expert's first row);
+// the expert's total goes to counts[e].  block_counts / block_base are
+// [E][nblk] (each expert's blocks contiguous).
+__global__ __launch_bounds__(256) void scan_blocks_kernel(ScanArgs a) {
+  __shared__ int part[256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int per = (a.nblk + 255) / 256;
+  const int b0 = min(tid * per, a.nblk), b1 = min(b0 + per, a.nblk);
+  const int32_t* bc = a.block_counts + (size_t)e * a.nblk;
+  int32_t* bb = a.block_base + (size_t)e * a.nblk;
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += bc[b];
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive scan of the 256 partial sums (Hillis-Steele)
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;            // exclusive prefix of this thread's range
+  for (int b = b0; b < b1; ++b) {
+    bb[b] = run;
+    run += bc[b];
+  }
+  if (tid == 255) a.counts[e] = part[255];
+}
+
+// Exclusive scan over experts, user counts, and the GEMM M-tile schedule
+// (one workgroup; thread e owns expert e, E <= 256).
+__global__ __launch_bounds__(256) void scan_experts_kernel(ScanArgs a) {
   __shared__ int tot[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS + 1];
   __shared__ int tstart[MAX_EXPERTS + 1];
   const int e = threadIdx.x;
-  if (e < a.E) {
-    int run = 0;
-#pragma unroll 8
-    for (int b = 0; b < a.nblk; ++b) {
-      const size_t o = (size_t)b * a.E + e;
-      const int c = a.block_counts[o];
-      a.block_base[o] = run;      // rows of earlier blocks for this expert
-      run += c;
-    }
-    tot[e] = run;
-  }
+  if (e < a.E) tot[e] = a.counts[e];
   __syncthreads();
   if (threadIdx.x == 0) {
     int o = 0, ts = 0;
@@ -42,7 +63,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   __syncthreads();
   if (e < a.E) {
     const int c = tot[e];
-    a.counts[e] = c;
     if (a.user_counts) a.user_counts[e] = c;
     a.offsets[e] = off[e];
     const int nt = tstart[e + 1] - tstart[e];
@@ -75,7 +95,7 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   for (int k = 0; k < a.K; ++k) {
     const int q = t * a.K + k;
     const int e = a.topk_idx[q];
-    const int row = a.offsets[e] + a.block_base[(size_t)b * a.E + e] + a.rank[q];
+    const int row = a.offsets[e] + a.block_base[(size_t)e * a.nblk + b] + a.rank[q];
     if (lane == 0) {
       a.slot_row[q] = row;
       a.row_src[row] = t;
@@ -91,7 +111,8 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
 }  // namespace
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(scan_blocks_kernel, dim3(a.E), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(scan_experts_kernel, dim3(1), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -50,7 +50,14 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.f + expf(-v)); }
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v), evaluated as v * rcp(1 + 2^(-v log2 e))
+// with the hardware base-2 exponential and reciprocal (about 1 ulp each; the
+// result is rounded to bf16 right after).  Large |v| saturates correctly:
+// 2^+big = inf gives rcp = 0, 2^-big = 0 gives rcp(1) = 1.
+__device__ __forceinline__ float silu_f(float v) {
+  const float e = __builtin_amdgcn_exp2f(v * -1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
@@ -70,6 +77,26 @@ __device__ __forceinline__ void sched_groups() {
     if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM
     sched_groups<N_MMA, N_DS, N_VM, I + 1>();
   }
+}
+
+constexpr int NGRP = 4;   // N-tiles per tile-order group
+
+// s_waitcnt immediate that waits until at most N vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] in bits [15:14]; the other counters left at their maximum).
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+}
+
+// N-tiles of one GEMM stage (GATEUP: 128 inner columns per tile, for each
+// expert of the shared group; DOWN: 256 output columns per tile).
+template <int MODE, int BM>
+__host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
+  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
+  if (MODE == 0) return ((a.inner + BN / 2 - 1) / (BN / 2)) * (routed ? 1 : a.n_experts);
+  return (a.d + BN - 1) / BN;
 }
 
 // MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED.  WAVES_M x (4 / WAVES_M) waves.
@@ -93,7 +120,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = L % mdim, nt = L / mdim;
+  // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
+  // one M-tile are adjacent, then the next M-tile (same expert, same weight
+  // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
+  // both its token-row tiles and its weight tiles in L2.
+  const int ndim = n_tiles_of<MODE, BM>(a);
+  int mt, nt;
+  {
+    const int full = ndim / NGRP;
+    const int ntg = L / (mdim * NGRP);
+    const int g = (ntg < full) ? NGRP : ndim - full * NGRP;
+    const int rem = L - ntg * mdim * NGRP;
+    mt = rem / g;
+    nt = ntg * NGRP + rem % g;
+  }
 
   int row0, rows, e;
   if (routed) {
@@ -221,39 +261,40 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   auto sched_ds = [&]() { sched_groups<N_MMA, N_DS, 0>(); };
   auto sched_ds_vm = [&]() { sched_groups<N_MMA, N_DS, N_VM>(); };
 
-  // One k-block from buffers (Ac, Bc) while the next block streams into
-  // (An, Bn).  `next` is the block to prefetch (the last block re-loads
-  // itself into the idle buffers: no branch; nothing reads that copy).
-  auto block = [&](int next, const u32x4* Ac, const u32x4* Bc, u32x4* An, u32x4* Bn) {
-    issue(next, An, Bn);
+  // One k-block from buffers (Ac, Bc); block kb+1 is already streaming into
+  // (An, Bn).  Once every wave has its last fragments of this block in
+  // registers (barrier), (Ac, Bc) are free and block `next2` = kb+2 starts
+  // streaming into them -- two blocks of matrix work to cover the latency.
+  // Blocks past the end re-load the last block (no branch; never read).
+  auto block = [&](int next2, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
     load_frags(fa1, fb1, Ac, Bc, 1);
     mma(fa0, fb0);
-    sched_ds_vm();
+    sched_ds();
     load_frags(fa0, fb0, Ac, Bc, 2);
     mma(fa1, fb1);
     sched_ds();
     load_frags(fa1, fb1, Ac, Bc, 3);
     mma(fa0, fb0);
     sched_ds();
-    // Next block landed (own loads + barrier); every wave is done reading
-    // this block's buffers, so the following issue may overwrite them.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb+1 landed
     __syncthreads();
+    issue(next2, Ac, Bc);
     load_frags(fa0, fb0, An, Bn, 0);
     mma(fa1, fb1);
-    sched_ds();
+    sched_ds_vm();
   };
 
   issue(0, As0, Bs0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  issue(min(1, nk - 1), As1, Bs1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());       // block 0 landed
   __syncthreads();
   load_frags(fa0, fb0, As0, Bs0, 0);
   int kb = 0;
   for (; kb + 2 <= nk; kb += 2) {
-    block(min(kb + 1, nk - 1), As0, Bs0, As1, Bs1);
-    block(min(kb + 2, nk - 1), As1, Bs1, As0, Bs0);
+    block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
+    block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
   }
-  if (kb < nk) block(kb, As0, Bs0, As1, Bs1);
+  if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
 
   // ---- epilogue ----
   // acc[nb][mb][r] = D[n][m] with n = nb*32 + 8*(r/4) + 4*hi + (r%4) and
@@ -335,13 +376,7 @@ template <int MODE, int BM, int WAVES_M>
 void launch_mode(const GemmArgs& a, hipStream_t s) {
   const bool routed = !(a.mode == 2 || (a.mode == 0 && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  int ndim;
-  if (MODE == 0) {
-    const int per_wg = BN / 2;
-    ndim = ((a.inner + per_wg - 1) / per_wg) * (routed ? 1 : a.n_experts);
-  } else {
-    ndim = (a.d + BN - 1) / BN;
-  }
+  const int ndim = n_tiles_of<MODE, BM>(a);
   hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WAVES_M>), dim3(mdim * ndim),
                      dim3(256), 0, s, a);
 }

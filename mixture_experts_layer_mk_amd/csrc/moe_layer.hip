@@ -88,6 +88,10 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
   L.y = take(TK * d.d * 4);
   L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
+  L.ds = router_dsplit(d.T, d.n_routed, d.d, d.dtype == MOE_BF16 ? 1 : 0);
+  L.ep = (d.n_routed + 3) & ~3;
+  L.planes = d.dtype == MOE_BF16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
+  L.plog = take((int64_t)L.ds * d.T * L.ep * 4);
   L.total = off;
   return L;
 }
@@ -149,6 +153,9 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     r.T = d.T; r.d = d.d; r.E = d.n_routed; r.K = d.top_k; r.score = d.score;
     r.n_groups = d.n_groups; r.topk_groups = d.topk_groups; r.norm_topk = d.norm_topk;
     r.routed_scale = d.routed_scale;
+    r.ds = L.ds; r.ep = L.ep;
+    r.planes = static_cast<bf16_t*>(at(L.planes));
+    r.plog = static_cast<float*>(at(L.plog));
     r.topk_idx = idx; r.topk_w = gw;
     r.rank = static_cast<int32_t*>(at(L.rank));
     r.block_counts = static_cast<int32_t*>(at(L.block_counts));
@@ -174,7 +181,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   {
     PermuteArgs p{};
     p.x = x; p.dtype = bf16 ? 1 : 0; p.T = d.T; p.d = d.d; p.K = d.top_k;
-    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T);
+    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
     p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
     p.block_base = static_cast<const int32_t*>(at(L.block_base));
     p.offsets = static_cast<const int32_t*>(at(L.offsets));

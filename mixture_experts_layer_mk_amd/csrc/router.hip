@@ -1,256 +1,345 @@
-// Router: fp32 gate GEMM, score (softmax or sigmoid), optional group limit,
-// top-K in registers, gate weights, and the per-block expert histogram with
-// each kept slot's rank inside its block (the inputs of a stable dispatch).
+// Router: gate logits, scores (softmax or sigmoid), optional group limit,
+// top-K, gate weights, and per-block expert histograms with each kept slot's
+// rank inside its block (the inputs of a stable dispatch).
 //
 // Method: DeepSeekMoE paper abstract (mK of mN fine-grained experts kept per
 // token); DeepSeek-V3 Technical Report summary, "2. Architecture" (selection
-// bias, limit on the number of nodes -- here groups -- a token may use).
+// bias; limit on the nodes -- here expert groups -- a token may use).
+//
+// Three kernels:
+//  1. split_gate: every fp32 gate weight w is split exactly into three bf16
+//     parts, w = hi + mid + lo (each part holds the next 8 significant bits;
+//     the residuals are exact in fp32).
+//  2. logits (bf16 x): l = x.hi + x.mid + x.lo on the matrix cores, 32
+//     experts x 32 tokens per wave.  x is bf16, so every product is exact in
+//     fp32 and the fp32 accumulation makes l an fp32-accurate dot product.
+//     The hidden dimension may be split over DS waves (more waves in flight);
+//     the DS partial sums are added in a fixed order by the select kernel.
+//     (fp32 x: a plain fp32 FMA GEMM instead.)
+//  3. select: one lane per token, 64 tokens per wave (= one histogram
+//     block): scores in fp32, group limit, top-K kept in registers ordered
+//     by (key descending, index ascending), gate weights; then per expert a
+//     wave ballot gives the block's count and each slot's in-block rank.
 #include "common.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int RK = 32;        // d-chunk per LDS stage
-constexpr int NT = 256;       // threads per workgroup
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-struct Cand {
-  float key;
-  int idx;
-  float s;
-};
+// ---------------------------------------------------------------------------
+// 1. gate split
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void split_gate_kernel(const float* __restrict__ w,
+                                                         bf16_t* __restrict__ planes,
+                                                         int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = w[i];
+  const bf16_t h = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(h);
+  const bf16_t m = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(m);
+  planes[i] = h;
+  planes[n + i] = m;
+  planes[2 * n + i] = f32_to_bf16(r2);
+}
 
+// ---------------------------------------------------------------------------
+// 2a. logits on the matrix cores (bf16 x)
+// ---------------------------------------------------------------------------
+// One wave per (token block, expert block, d-slice) tile; 4 waves per
+// workgroup.  plog[ds][t][e] (row stride ep) receives the partial sum of the
+// ds-th slice of the hidden dimension.
+__global__ __launch_bounds__(256) void logits_mfma_kernel(LogitsArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n_eb = (a.E + 31) / 32, n_tb = (a.T + 31) / 32;
+  if (tile >= n_eb * n_tb * a.ds) return;
+  const int eb = tile % n_eb;
+  const int tb = (tile / n_eb) % n_tb;
+  const int ds = tile / (n_eb * n_tb);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int er = min(eb * 32 + l32, a.E - 1);
+  const int tr = min(tb * 32 + l32, a.T - 1);
+  const int kspan = a.d / a.ds;                      // multiple of 16
+  const int k0 = ds * kspan;
+  const size_t pn = (size_t)a.E * a.d;
+  const bf16_t* xp = a.x + (size_t)tr * a.d + k0 + 8 * hi;
+  const bf16_t* wp = a.planes + (size_t)er * a.d + k0 + 8 * hi;
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  constexpr int U = 4;   // k-steps of 16 per batch (loads of a batch in flight)
+  int k = 0;
+  for (; k + 16 * U <= kspan; k += 16 * U) {
+    bf16x8 xf[U], wh[U], wm[U], wl[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      xf[u] = *reinterpret_cast<const bf16x8*>(xp + k + 16 * u);
+      wh[u] = *reinterpret_cast<const bf16x8*>(wp + k + 16 * u);
+      wm[u] = *reinterpret_cast<const bf16x8*>(wp + pn + k + 16 * u);
+      wl[u] = *reinterpret_cast<const bf16x8*>(wp + 2 * pn + k + 16 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[u], xf[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wm[u], xf[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[u], xf[u], acc, 0, 0, 0);
+    }
+  }
+  for (; k < kspan; k += 16) {
+    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xp + k);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(wp + 2 * pn + k), xf, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(wp + pn + k), xf, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        *reinterpret_cast<const bf16x8*>(wp + k), xf, acc, 0, 0, 0);
+  }
+  // acc[r] = D[e][t]: e = eb*32 + 8*(r/4) + 4*hi + r%4, t = tb*32 + l32
+  const int t = tb * 32 + l32;
+  if (t >= a.T) return;
+  float* row = a.plog + ((size_t)ds * a.T + t) * a.ep;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int e0 = eb * 32 + 8 * g + 4 * hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (e0 + q < a.E) row[e0 + q] = acc[4 * g + q];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2b. logits with fp32 FMA (fp32 x)
+// ---------------------------------------------------------------------------
+// 64 tokens x 64 experts per workgroup, 4 x 4 outputs per thread.
+__global__ __launch_bounds__(256) void logits_f32_kernel(LogitsArgs a) {
+  constexpr int RK = 32;
+  __shared__ float xs[RK][64 + 1];
+  __shared__ float ws[RK][64 + 1];
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int n_eb = (a.E + 63) / 64;
+  const int t0 = (blockIdx.x / n_eb) * 64, e0 = (blockIdx.x % n_eb) * 64;
+  float acc[4][4] = {};
+  for (int d0 = 0; d0 < a.d; d0 += RK) {
+    for (int li = tid; li < 64 * RK; li += 256) {
+      const int r = li / RK, k = li % RK;
+      const bool kin = d0 + k < a.d;
+      xs[k][r] = (kin && t0 + r < a.T) ? a.xf[(size_t)(t0 + r) * a.d + d0 + k] : 0.f;
+      ws[k][r] = (kin && e0 + r < a.E) ? a.w_gate[(size_t)(e0 + r) * a.d + d0 + k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < RK; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = fmaf(xs[k][ty + 16 * i], ws[k][tx + 16 * j], acc[i][j]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + ty + 16 * i, e = e0 + tx + 16 * j;
+      if (t < a.T && e < a.E) a.plog[(size_t)t * a.ep + e] = acc[i][j];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. selection
+// ---------------------------------------------------------------------------
 // Total order of the top-K: larger key first, then smaller expert index.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-__device__ __forceinline__ Cand wave_best(Cand c) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float k2 = __shfl_xor(c.key, off, 64);
-    int i2 = __shfl_xor(c.idx, off, 64);
-    float s2 = __shfl_xor(c.s, off, 64);
-    if (better(k2, i2, c.key, c.idx)) { c.key = k2; c.idx = i2; c.s = s2; }
+template <int KMAX>
+__global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
+  extern __shared__ float lg[];               // [64][E + 1]: logits, then p
+  __shared__ uint64_t masks[MAX_EXPERTS];
+  __shared__ float gsc[64][MAX_GROUPS + 1];
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * 64;
+  const int t = t0 + lane;
+  const bool live = t < a.T;
+  const int E = a.E, K = a.K, ld = E + 1;
+  const int ntok = min(64, a.T - t0);
+
+  // Stage this block's logits: sum of the d-slice partials in slice order,
+  // plus the logit bias (coalesced: the block's rows are contiguous).
+  for (int i = lane; i < ntok * E; i += 64) {
+    const int r = i / E, e = i % E;
+    float v = 0.f;
+    for (int s = 0; s < a.ds; ++s) v += a.plog[((size_t)s * a.T + t0 + r) * a.ep + e];
+    if (a.logit_bias) v += a.logit_bias[e];
+    lg[r * ld + e] = v;
   }
-  return c;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// RT tokens per workgroup; TN experts per thread (16*TN >= E).
-template <typename XT, int RT, int TN>
-__global__ __launch_bounds__(NT) void router_kernel(RouterArgs a) {
-  constexpr int TM = RT / 16;           // tokens per thread
-  constexpr int EP = 16 * TN;           // padded expert count
-  constexpr int V = (EP + 63) / 64;     // experts per lane in selection
-  __shared__ float xs[RK][RT + 1];
-  __shared__ float ws[RK][EP + 1];
-  __shared__ float lg[RT][EP + 1];
-  __shared__ int sel[RT * MAX_TOPK];
-  __shared__ float keybuf[4][EP];
-
-  const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
-  const int t0 = blockIdx.x * RT;
-  const int d = a.d, E = a.E, K = a.K;
-  const XT* x = static_cast<const XT*>(a.x);
-
-  float acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
-
-  for (int d0 = 0; d0 < d; d0 += RK) {
-    // x chunk -> xs[k][t] (fp32)
-    for (int li = tid; li < RT * RK; li += NT) {
-      int t = li / RK, k = li % RK;
-      float v = 0.f;
-      if (t0 + t < a.T && d0 + k < d) v = ld_f32<XT>(x + (size_t)(t0 + t) * d + d0 + k);
-      xs[k][t] = v;
-    }
-    // gate chunk -> ws[k][e]
-    for (int li = tid; li < EP * RK; li += NT) {
-      int e = li / RK, k = li % RK;
-      float v = 0.f;
-      if (e < E && d0 + k < d) v = a.w_gate[(size_t)e * d + d0 + k];
-      ws[k][e] = v;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < RK; ++k) {
-      float xv[TM], wv[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) xv[i] = xs[k][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) wv[j] = ws[k][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      int e = tx + 16 * j;
-      float v = acc[i][j];
-      if (a.logit_bias && e < E) v += a.logit_bias[e];
-      lg[ty + 16 * i][e] = v;
-    }
   __syncthreads();
+  float* my = lg + (live ? lane : 0) * ld;    // dead lanes shadow row 0
 
-  // ---- selection: one wave per token ----
-  const int lane = tid % 64, wave = tid / 64;
-  const int ntok = min(RT, a.T - t0);
-  for (int t = wave; t < ntok; t += 4) {
-    float l[V], s[V], key[V];
-    bool taken[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      int e = lane + 64 * v;
-      l[v] = (e < E) ? lg[t][e] : -INFINITY;
-      taken[v] = false;
+  // scores: softmax p_e = exp(l_e - max) / z (exponentials stored, divided
+  // on use) or sigmoid p_e = 1 / (1 + exp(-l_e)); always in fp32.
+  float z = 1.f;
+  if (a.score == 0) {
+    float mx = -INFINITY;
+    for (int e = 0; e < E; ++e) mx = fmaxf(mx, my[e]);
+    z = 0.f;
+    for (int e = 0; e < E; ++e) {
+      const float v = expf(my[e] - mx);
+      z += v;
+      if (live) my[e] = v;
     }
-    if (a.score == 0) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < V; ++v) m = fmaxf(m, l[v]);
-      m = wave_max(m);
-      float z = 0.f;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        s[v] = (lane + 64 * v < E) ? expf(l[v] - m) : 0.f;
-        z += s[v];
-      }
-      z = wave_sum(z);
-#pragma unroll
-      for (int v = 0; v < V; ++v) s[v] = s[v] / z;
-    } else {
-#pragma unroll
-      for (int v = 0; v < V; ++v) s[v] = 1.f / (1.f + expf(-l[v]));
+  } else {
+    for (int e = 0; e < E; ++e) {
+      const float v = 1.f / (1.f + expf(-my[e]));
+      if (live) my[e] = v;
     }
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      int e = lane + 64 * v;
-      key[v] = (e < E) ? s[v] + (a.select_bias ? a.select_bias[e] : 0.f) : -INFINITY;
-      if (key[v] != key[v]) key[v] = -INFINITY;   // NaN never outranks a score
+  }
+  __syncthreads();
+  auto score = [&](int e) -> float { return a.score == 0 ? my[e] / z : my[e]; };
+  auto key_of = [&](int e, float s) -> float {
+    const float k = s + (a.select_bias ? a.select_bias[e] : 0.f);
+    return (k != k) ? -INFINITY : k;     // NaN never outranks a score
+  };
+
+  // group limit: bitmask of the kept groups
+  uint64_t keep = ~0ull;
+  int gsz = E;
+  if (a.n_groups > 1) {
+    gsz = E / a.n_groups;
+    for (int g = 0; g < a.n_groups; ++g) {
+      float b1 = -INFINITY, b2 = -INFINITY;
+      for (int q = 0; q < gsz; ++q) {
+        const int e = g * gsz + q;
+        const float kv = key_of(e, score(e));
+        if (kv > b1) { b2 = b1; b1 = kv; } else if (kv > b2) { b2 = kv; }
+      }
+      gsc[lane][g] = (gsz > 1) ? b1 + b2 : b1;
     }
-    if (a.n_groups > 1) {
-      const int gsz = E / a.n_groups;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        int e = lane + 64 * v;
-        if (e < E) keybuf[wave][e] = key[v];
+    keep = 0;
+    for (int r = 0; r < a.topk_groups; ++r) {
+      float bk = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int g = 0; g < a.n_groups; ++g) {
+        if ((keep >> g) & 1) continue;
+        const float v = gsc[lane][g];
+        if (better(v, g, bk, bi)) { bk = v; bi = g; }
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      // lane g scores group g: sum of its two highest keys
-      float gscore = -INFINITY;
-      if (lane < a.n_groups) {
-        float b1 = -INFINITY, b2 = -INFINITY;
-        for (int q = 0; q < gsz; ++q) {
-          float kv = keybuf[wave][lane * gsz + q];
-          if (kv > b1) { b2 = b1; b1 = kv; } else if (kv > b2) { b2 = kv; }
-        }
-        gscore = (gsz > 1) ? b1 + b2 : b1;
-      }
-      uint64_t keep = 0;
-      bool gtaken = false;
-      for (int r = 0; r < a.topk_groups; ++r) {
-        Cand c{(lane < a.n_groups && !gtaken) ? gscore : -INFINITY,
-               (lane < a.n_groups && !gtaken) ? lane : 0x7fffffff, 0.f};
-        c = wave_best(c);
-        keep |= (uint64_t)1 << c.idx;
-        if (lane == c.idx) gtaken = true;
-      }
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        int e = lane + 64 * v;
-        if (e < E && !((keep >> (e / gsz)) & 1)) key[v] = -INFINITY;
-      }
-      __builtin_amdgcn_wave_barrier();
+      keep |= 1ull << bi;
     }
-    float gsum = 0.f, my_g = 0.f;
-    int my_id = 0;
-    for (int k = 0; k < K; ++k) {
-      Cand c{-INFINITY, 0x7fffffff, 0.f};
+  }
+
+  // top-K in registers, sorted by (key desc, index asc)
+  float tk[KMAX], ts[KMAX];
+  int ti[KMAX];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        int e = lane + 64 * v;
-        if (e < E && !taken[v] && better(key[v], e, c.key, c.idx)) {
-          c.key = key[v]; c.idx = e; c.s = s[v];
-        }
+  for (int j = 0; j < KMAX; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
+  for (int e = 0; e < E; ++e) {
+    if (!((keep >> (e / gsz)) & 1)) continue;
+    const float s = score(e);
+    float ck = key_of(e, s), cs = s;
+    int ci = e;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
+        const float k2 = tk[j], s2 = ts[j];
+        const int i2 = ti[j];
+        tk[j] = ck; ts[j] = cs; ti[j] = ci;
+        ck = k2; cs = s2; ci = i2;
       }
-      c = wave_best(c);
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (lane + 64 * v == c.idx) taken[v] = true;
-      if (lane == k) { my_g = c.s; my_id = c.idx; }
-      gsum += c.s;
     }
-    if (lane < K) {
-      float g = my_g;
+  }
+  float gsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < K) gsum += ts[j];
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= K) break;
+      float g = ts[j];
       if (a.norm_topk) g = g / gsum;
       g *= a.routed_scale;
-      size_t o = (size_t)(t0 + t) * K + lane;
-      a.topk_idx[o] = my_id;
-      a.topk_w[o] = g;
-      sel[t * K + lane] = my_id;
+      a.topk_idx[(size_t)t * K + j] = ti[j];
+      a.topk_w[(size_t)t * K + j] = g;
     }
   }
+
+  // block histogram and in-block ranks (token order = lane order)
+  for (int e = 0; e < E; ++e) {
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < K) has |= (ti[j] == e);
+    const uint64_t m = __ballot(live && has);
+    if (lane == 0) masks[e] = m;
+  }
   __syncthreads();
-
-  // ---- block histogram and in-block ranks (token order) ----
-  for (int e = tid; e < E; e += NT) {
-    int c = 0;
-    for (int q = 0; q < ntok * K; ++q) c += (sel[q] == e);
-    a.block_counts[(size_t)blockIdx.x * E + e] = c;
+  for (int e = lane; e < E; e += 64)   // layout [E][blocks]
+    a.block_counts[(size_t)e * gridDim.x + blockIdx.x] = __popcll(masks[e]);
+  if (live) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= K) break;
+      a.rank[(size_t)t * K + j] = __popcll(masks[ti[j]] & below);
+    }
   }
-  for (int q = tid; q < ntok * K; q += NT) {
-    const int t = q / K, e = sel[q];
-    int r = 0;
-    for (int p = 0; p < t * K; ++p) r += (sel[p] == e);
-    a.rank[(size_t)t0 * K + q] = r;
-  }
-}
-
-template <typename XT, int RT>
-hipError_t launch_rt(const RouterArgs& a, hipStream_t s) {
-  dim3 grid((a.T + RT - 1) / RT), block(NT);
-  if (a.E <= 16) hipLaunchKernelGGL((router_kernel<XT, RT, 1>), grid, block, 0, s, a);
-  else if (a.E <= 64) hipLaunchKernelGGL((router_kernel<XT, RT, 4>), grid, block, 0, s, a);
-  else if (a.E <= 128) hipLaunchKernelGGL((router_kernel<XT, RT, 8>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((router_kernel<XT, RT, 16>), grid, block, 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-int router_tokens_per_block(int T) {
-  // 64-token workgroups when that still gives one per compute unit (256),
-  // else 16-token ones so small batches spread over more of the chip.
-  return (T >= 64 * 256) ? 64 : 16;
+int router_tokens_per_block(int) { return 64; }
+
+int router_dsplit(int T, int E, int d, int dtype) {
+  if (dtype != 1) return 1;
+  const int tiles = ((T + 31) / 32) * ((E + 31) / 32);
+  int ds = 1;
+  // aim for ~4096 waves; every slice a multiple of 64 columns
+  while (tiles * ds * 2 <= 4096 && (d % (ds * 2 * 64)) == 0 && ds < 16) ds *= 2;
+  return ds;
 }
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
-  const int rt = router_tokens_per_block(a.T);
-  if (a.dtype == 1)
-    return rt == 64 ? launch_rt<bf16_t, 64>(a, s) : launch_rt<bf16_t, 16>(a, s);
-  return rt == 64 ? launch_rt<float, 64>(a, s) : launch_rt<float, 16>(a, s);
+hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
+  // 1 + 2: partial logits
+  LogitsArgs la{};
+  la.T = r.T; la.d = r.d; la.E = r.E; la.ep = r.ep; la.ds = r.ds;
+  la.plog = r.plog;
+  if (r.dtype == 1) {
+    const int64_t n = (int64_t)r.E * r.d;
+    hipLaunchKernelGGL(split_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       r.w_gate, r.planes, n);
+    la.x = static_cast<const bf16_t*>(r.x);
+    la.planes = r.planes;
+    const int tiles = ((r.T + 31) / 32) * ((r.E + 31) / 32) * r.ds;
+    hipLaunchKernelGGL(logits_mfma_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s, la);
+  } else {
+    la.xf = static_cast<const float*>(r.x);
+    la.w_gate = r.w_gate;
+    la.ds = 1;
+    const int nb = ((r.T + 63) / 64) * ((r.E + 63) / 64);
+    hipLaunchKernelGGL(logits_f32_kernel, dim3(nb), dim3(256), 0, s, la);
+  }
+  // 3: selection
+  SelectArgs sa{};
+  sa.plog = r.plog; sa.ep = r.ep; sa.ds = r.dtype == 1 ? r.ds : 1;
+  sa.logit_bias = r.logit_bias; sa.select_bias = r.select_bias;
+  sa.T = r.T; sa.E = r.E; sa.K = r.K; sa.score = r.score;
+  sa.n_groups = r.n_groups; sa.topk_groups = r.topk_groups; sa.norm_topk = r.norm_topk;
+  sa.routed_scale = r.routed_scale;
+  sa.topk_idx = r.topk_idx; sa.topk_w = r.topk_w; sa.rank = r.rank;
+  sa.block_counts = r.block_counts;
+  const dim3 grid((r.T + 63) / 64);
+  const size_t lds = (size_t)64 * (r.E + 1) * sizeof(float);
+  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(64), lds, s, sa);
+  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(64), lds, s, sa);
+  return hipGetLastError();
 }
 
 }  // namespace moe
