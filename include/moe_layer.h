@@ -102,7 +102,9 @@ typedef struct {
   int64_t h_routed;         /* [T * top_k][inner] silu(W1 u) * (W3 u)         */
   int64_t h_shared;         /* [T][n_shared * shared_inner]                   */
   int64_t y_f32;            /* [T * top_k][d] routed expert outputs (fp32)    */
-  int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32)        */
+  int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32); -1 for
+                               bf16 layers, whose combine is fused into the
+                               shared down-projection                         */
   int64_t total_bytes;      /* = moe_layer_workspace_size                     */
 } moe_workspace_layout_t;
 

@@ -115,6 +115,10 @@ struct GemmArgs {
   int d, inner, n_experts;       // inner of the group; n_experts in group
   void* out; int ldo;            // H (dtype) / Y (f32) / S (f32)
   const void* x;                 // DOWN_SHARED residual
+  // DOWN_SHARED with the combine fused (ybuf != NULL): out2[t] =
+  //   x[t] + shared(t) + sum_k gw[t,k] * ybuf[slot_row[t,k]]   (dtype out)
+  const float* ybuf; const float* gw; const int32_t* slot_row; int K;
+  void* out2;
   const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
   int T;                          // rows for shared group
   int bm;

@@ -7,7 +7,8 @@
 //   GATEUP      H = silu(A W1^T) * (A W3^T), gate and up fused in one tile;
 //               routed tiles gather their token rows straight from x
 //   DOWN        Y = H W2^T (routed rows, fp32 out)
-//   DOWN_SHARED S = x + sum_s H_s W2_s^T (all tokens, fp32 out)
+//   DOWN_SHARED S = x + sum_s H_s W2_s^T (all tokens, fp32 out), or with the
+//               combine fused: out = x + sum_s H_s W2_s^T + sum_k g_k Y_k
 //
 // Tiling.  A workgroup (4 waves) owns BM token rows x 256 weight rows with a
 // 64-wide k step.  Both operands are k-contiguous in memory (token rows and
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           *reinterpret_cast<float4*>(orow + n) = v;
         }
     }
-  } else {
+  } else if (a.ybuf == nullptr) {
     float* out = static_cast<float*>(a.out);
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
 #pragma unroll
@@ -367,6 +368,64 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           o.z = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
           o.w = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
           *reinterpret_cast<float4*>(orow + n) = o;
+        }
+    }
+  } else {
+    // Combine fused: out = RNE(x + shared + sum_k g_k Y_k), the same fp32
+    // operations in the same order as the separate combine (residual plus
+    // shared experts first, then the kept experts in slot order).
+    bf16_t* out = static_cast<bf16_t*>(a.out2);
+    const bf16_t* x = static_cast<const bf16_t*>(a.x);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = wm * WM + mb * 32 + l32;
+      if (m >= rows) continue;
+      const int t = row0 + m;
+      const bf16_t* xrow = x + (size_t)t * a.d;
+      float o[NB][4][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
+          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + n);
+          o[nb][g][0] = bf16_to_f32((bf16_t)(xv.x & 0xffff)) + acc[nb][mb][4 * g + 0];
+          o[nb][g][1] = bf16_to_f32((bf16_t)(xv.x >> 16)) + acc[nb][mb][4 * g + 1];
+          o[nb][g][2] = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
+          o[nb][g][3] = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
+        }
+      for (int k = 0; k < a.K; ++k) {
+        const float gk = a.gw[(size_t)t * a.K + k];
+        const float* yrow = a.ybuf + (size_t)a.slot_row[(size_t)t * a.K + k] * a.d;
+        float4 yv[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
+            yv[nb][g] = *reinterpret_cast<const float4*>(yrow + n);
+          }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            o[nb][g][0] = fmaf(gk, yv[nb][g].x, o[nb][g][0]);
+            o[nb][g][1] = fmaf(gk, yv[nb][g].y, o[nb][g][1]);
+            o[nb][g][2] = fmaf(gk, yv[nb][g].z, o[nb][g][2]);
+            o[nb][g][3] = fmaf(gk, yv[nb][g].w, o[nb][g][3]);
+          }
+      }
+      bf16_t* orow = out + (size_t)t * a.d;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+          if (n >= a.d) continue;
+          uint2 v;
+          v.x = pack2(o[nb][g][0], o[nb][g][1]);
+          v.y = pack2(o[nb][g][2], o[nb][g][3]);
+          *reinterpret_cast<uint2*>(orow + n) = v;
         }
     }
   }

@@ -87,7 +87,9 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.h_routed = take(TK * d.inner * esz);
   L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
   L.y = take(TK * d.d * 4);
-  L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
+  // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
+  // layers fuse the combine into the shared down-projection.
+  L.s = (d.n_shared > 0 && d.dtype != MOE_BF16) ? take((int64_t)d.T * d.d * 4) : -1;
   L.ds = router_dsplit(d.T, d.n_routed, d.d, d.dtype == MOE_BF16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
   L.planes = d.dtype == MOE_BF16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
@@ -224,18 +226,26 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.out = at(L.y); g.ldo = d.d;
     MOE_CHECK(gemm(g));
   }
-  // 7. shared down (+ residual, fp32)
+  // 7. shared down (+ residual); for bf16 layers the combine is fused here
   if (!mark(6)) return MOE_ERR_HIP;
+  const bool fused = bf16 && d.n_shared > 0;
   if (d.n_shared > 0) {
     GemmArgs g = base;
     g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;
     g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
     g.out = at(L.s); g.ldo = d.d;
+    if (fused) {
+      g.ybuf = static_cast<const float*>(at(L.y));
+      g.gw = gw;
+      g.slot_row = static_cast<const int32_t*>(at(L.slot_row));
+      g.K = d.top_k;
+      g.out2 = out;
+    }
     MOE_CHECK(gemm(g));
   }
-  // 8. combine
+  // 8. combine (separate when not fused above)
   if (!mark(7)) return MOE_ERR_HIP;
-  {
+  if (!fused) {
     CombineArgs c{};
     c.base = d.n_shared > 0 ? at(L.s) : x;
     c.base_f32 = d.n_shared > 0;

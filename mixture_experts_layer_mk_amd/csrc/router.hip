@@ -173,12 +173,26 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
 
   // Stage this block's logits: sum of the d-slice partials in slice order,
   // plus the logit bias (coalesced: the block's rows are contiguous).
-  for (int i = lane; i < ntok * E; i += 64) {
-    const int r = i / E, e = i % E;
-    float v = 0.f;
-    for (int s = 0; s < a.ds; ++s) v += a.plog[((size_t)s * a.T + t0 + r) * a.ep + e];
-    if (a.logit_bias) v += a.logit_bias[e];
-    lg[r * ld + e] = v;
+  // (rows of ep floats, ep a multiple of 4: float4 loads; the slices are
+  // independent loads, batched so several are in flight.)
+  const int q4 = a.ep / 4;
+  const float4* p4 = reinterpret_cast<const float4*>(a.plog);
+  const size_t slice4 = (size_t)a.T * q4;
+#pragma unroll 4
+  for (int i = lane; i < ntok * q4; i += 64) {
+    const int r = i / q4, c = i % q4;
+    const size_t o = (size_t)(t0 + r) * q4 + c;
+    float4 v = p4[o];
+    for (int s = 1; s < a.ds; ++s) {
+      const float4 w = p4[o + s * slice4];
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 4 * c + j;
+      if (e < E) lg[r * ld + e] = vv[j] + (a.logit_bias ? a.logit_bias[e] : 0.f);
+    }
   }
   __syncthreads();
   float* my = lg + (live ? lane : 0) * ld;    // dead lanes shadow row 0
@@ -240,18 +254,21 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
   int ti[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
-  for (int e = 0; e < E; ++e) {
-    if (!((keep >> (e / gsz)) & 1)) continue;
-    const float s = score(e);
-    float ck = key_of(e, s), cs = s;
-    int ci = e;
+  const int ngr = E / gsz;
+  for (int g = 0; g < ngr; ++g) {
+    if (!((keep >> g) & 1)) continue;
+    for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
+      const float s = score(e);
+      float ck = key_of(e, s), cs = s;
+      int ci = e;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
-        const float k2 = tk[j], s2 = ts[j];
-        const int i2 = ti[j];
-        tk[j] = ck; ts[j] = cs; ti[j] = ci;
-        ck = k2; cs = s2; ci = i2;
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
+          const float k2 = tk[j], s2 = ts[j];
+          const int i2 = ti[j];
+          tk[j] = ck; ts[j] = cs; ti[j] = ci;
+          ck = k2; cs = s2; ci = i2;
+        }
       }
     }
   }
