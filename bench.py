@@ -55,8 +55,43 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, host, n_tokens):
-    """Time the fp64 CPU oracle on the first n_tokens tokens."""
+def summarize_traffic(fetch_csv, write_csv, copy_mb):
+    """Write the traffic summary of the dominant kernel from two rocprofv3
+    --pmc counter files (FETCH_SIZE run, WRITE_SIZE run, both of a bench run
+    with --copy-calibration-mb copy_mb).  Each counter is scaled by what it
+    reads for the plain device copy of copy_mb MiB."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    out = {"source_hash": source_hash(), "kernel": DOMINANT, "copy_calibration_mib": copy_mb}
+    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                                ("write", write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        copy = [v for (k, g), v in vals.items() if "copyBuffer" in k]
+        gemm = [(g, v) for (k, g), v in vals.items() if "gemm_bf16_kernel<0" in k]
+        if not copy or not gemm:
+            raise SystemExit(f"{path}: copy or gate/up kernel missing")
+        scale = (copy_mb * 1024.0) / max(copy)            # KiB per counter KiB
+        g, v = max(gemm)                                   # routed launch: larger grid
+        out[f"{name}_kib_raw"] = v
+        out[f"{name}_scale"] = scale
+        out[f"{name}_bytes"] = v * scale * 1024.0
+    out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def cpu_baseline(cfg, host, n_tokens, reps):
+    """Time the fp64 CPU oracle on the first n_tokens tokens, reps times."""
     import numpy as np
     import threadpoolctl
     import oracle
@@ -67,12 +102,13 @@ def cpu_baseline(cfg, host, n_tokens):
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
-    oracle.moe_forward(x, wg, tuple(w), tuple(ws) if ws else None, cfg.top_k,
-                       n_shared=cfg.n_shared, score=cfg.score)
+    for _ in range(reps):
+        oracle.moe_forward(x, wg, tuple(w), tuple(ws) if ws else None, cfg.top_k,
+                           n_shared=cfg.n_shared, score=cfg.score)
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores),
+    return {"value": n_tokens * reps / dt, "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"first {n_tokens} of {cfg.T} tokens of the same workload "
+            "sample": f"{reps} x the first {n_tokens} of {cfg.T} tokens of the same workload "
                       f"(numpy fp64 oracle, BLAS threads={cores})"}
 
 
@@ -82,12 +118,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="deepseekmoe-16b")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="oracle sample size (0: all tokens of the workload)")
+    ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for "
                          "scaling HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the dominant kernel's traffic summary from two "
+                         "rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        summarize_traffic(*args.traffic_from, args.copy_calibration_mb or 1024)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -169,8 +213,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline on {args.cpu_tokens} tokens")
-        cpu = cpu_baseline(cfg, host, min(args.cpu_tokens, cfg.T))
+        n = min(args.cpu_tokens or cfg.T, cfg.T)
+        log(f"[bench] cpu baseline: {args.cpu_reps} x {n} tokens")
+        cpu = cpu_baseline(cfg, host, n, args.cpu_reps)
 
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s",
