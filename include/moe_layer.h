@@ -87,9 +87,9 @@ typedef struct {
 
 /* Byte offsets of the intermediate buffers inside the workspace, for
  * inspection after a forward call has completed (-1 = not materialised).
- * Element types: *_i32 int32, *_f32 float, others desc->dtype.  Rows of
- * xp / h_routed / y_f32 are in expert-contiguous order (expert ascending, token
- * ascending); row r came from token row_src[r]. */
+ * Element types: *_i32 int32, *_f32 float, y as stated below, others
+ * desc->dtype.  Rows of xp / h_routed / y are in expert-contiguous order
+ * (expert ascending, token ascending); row r came from token row_src[r]. */
 typedef struct {
   int64_t topk_idx_i32;     /* [T][top_k]; written only when topk_idx == NULL */
   int64_t topk_w_f32;       /* [T][top_k]; written only when topk_w == NULL   */
@@ -101,7 +101,12 @@ typedef struct {
                                expert GEMM gathers rows of x directly)        */
   int64_t h_routed;         /* [T * top_k][inner] silu(W1 u) * (W3 u)         */
   int64_t h_shared;         /* [T][n_shared * shared_inner]                   */
-  int64_t y_f32;            /* [T * top_k][d] routed expert outputs (fp32)    */
+  int64_t y;                /* [T * top_k][d] routed expert outputs: float for
+                               fp32 layers; for bf16 layers IEEE half, each
+                               64-column group of a row scaled by a power of
+                               two (value = half * y_scale)                   */
+  int64_t y_scale_f32;      /* [T * top_k][d / 64] those inverse scales (bf16
+                               layers; -1 otherwise)                          */
   int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32); -1 for
                                bf16 layers, whose combine is fused into the
                                shared down-projection                         */

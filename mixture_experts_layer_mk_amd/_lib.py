@@ -44,7 +44,7 @@ class FfnWeights(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "topk_idx_i32", "topk_w_f32", "counts_i32", "offsets_i32",
-        "slot_row_i32", "row_src_i32", "xp", "h_routed", "h_shared", "y_f32",
+        "slot_row_i32", "row_src_i32", "xp", "h_routed", "h_shared", "y", "y_scale_f32",
         "s_f32", "total_bytes")]
 
 

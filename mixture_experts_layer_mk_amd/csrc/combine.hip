@@ -1,7 +1,9 @@
-// Combine: out[t] = base[t] + sum_k g[t,k] * Y[slot_row[t,k]] (Y fp32), summed in slot
+// Combine: out[t] = base[t] + sum_k g[t,k] * Y[slot_row[t,k]], summed in slot
 // order k = 0..K-1 in fp32 and rounded once to the output type.  base is
 // x + (shared experts) in fp32, or x itself when there are no shared experts.
-// Every output element has one owner thread: no atomics, deterministic.
+// Y is fp32 (fp32 layers) or fp16 times a power-of-two inverse scale per 64
+// columns of a row (bf16 layers).  Every output element has one owner
+// thread: no atomics, deterministic.
 //
 // Method: DeepSeekMoE paper abstract and blog post "Shared Expert Isolation
 // (Section 3.2)" -- shared experts always contribute with weight one; routed
@@ -12,8 +14,9 @@ namespace moe {
 
 namespace {
 
-template <typename T, int VEC, bool BASE_F32>
+template <typename T, int VEC, bool BASE_F32, bool Y16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  static_assert(!Y16 || VEC == 8, "fp16 rows are read 8 columns at a time");
   const int per_row = (a.d / VEC + 255) / 256;
   const int t = blockIdx.x / per_row;
   const int n0 = ((blockIdx.x % per_row) * 256 + threadIdx.x) * VEC;
@@ -28,18 +31,33 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = ld_f32<T>(b + v);
   }
-  const float* y = a.y;
   for (int k = 0; k < a.K; ++k) {
     const int q = t * a.K + k;
     const float g = a.topk_w[q];
-    const float4* yr = reinterpret_cast<const float4*>(y + (size_t)a.slot_row[q] * a.d + n0);
+    const size_t row = (size_t)a.slot_row[q];
+    if (Y16) {
+      const uint4 hv = *reinterpret_cast<const uint4*>(
+          static_cast<const uint16_t*>(a.y) + row * a.d + n0);
+      const float inv = a.yscale[row * (a.d / Y_GROUP) + n0 / Y_GROUP];
+      const uint32_t w[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
-    for (int v = 0; v < VEC / 4; ++v) {
-      const float4 yv = yr[v];
-      acc[4 * v + 0] = fmaf(g, yv.x, acc[4 * v + 0]);
-      acc[4 * v + 1] = fmaf(g, yv.y, acc[4 * v + 1]);
-      acc[4 * v + 2] = fmaf(g, yv.z, acc[4 * v + 2]);
-      acc[4 * v + 3] = fmaf(g, yv.w, acc[4 * v + 3]);
+      for (int v = 0; v < 4; ++v) {
+        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[v] & 0xffffu));
+        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[v] >> 16));
+        acc[2 * v + 0] = fmaf(g, lo * inv, acc[2 * v + 0]);
+        acc[2 * v + 1] = fmaf(g, hi * inv, acc[2 * v + 1]);
+      }
+    } else {
+      const float4* yr = reinterpret_cast<const float4*>(static_cast<const float*>(a.y) +
+                                                         row * a.d + n0);
+#pragma unroll
+      for (int v = 0; v < VEC / 4; ++v) {
+        const float4 yv = yr[v];
+        acc[4 * v + 0] = fmaf(g, yv.x, acc[4 * v + 0]);
+        acc[4 * v + 1] = fmaf(g, yv.y, acc[4 * v + 1]);
+        acc[4 * v + 2] = fmaf(g, yv.z, acc[4 * v + 2]);
+        acc[4 * v + 3] = fmaf(g, yv.w, acc[4 * v + 3]);
+      }
     }
   }
   T o[VEC];
@@ -49,18 +67,22 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       *reinterpret_cast<const uint4*>(o);
 }
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool Y16>
 void launch_t(const CombineArgs& a, hipStream_t s) {
   dim3 grid(((a.d / VEC + 255) / 256) * a.T);
-  if (a.base_f32) hipLaunchKernelGGL((combine_kernel<T, VEC, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((combine_kernel<T, VEC, false>), grid, dim3(256), 0, s, a);
+  if (a.base_f32) hipLaunchKernelGGL((combine_kernel<T, VEC, true, Y16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((combine_kernel<T, VEC, false, Y16>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  if (a.dtype == 1) launch_t<bf16_t, 8>(a, s);
-  else launch_t<float, 4>(a, s);
+  if (a.dtype == 1) {
+    if (a.yscale) launch_t<bf16_t, 8, true>(a, s);
+    else launch_t<bf16_t, 8, false>(a, s);
+  } else {
+    launch_t<float, 4, false>(a, s);
+  }
   return hipGetLastError();
 }
 

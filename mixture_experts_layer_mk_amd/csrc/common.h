@@ -41,8 +41,8 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t topk_idx, topk_w, rank, block_counts, block_base, counts, offsets,
-      tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, s, planes,
-      plog, total;
+      tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, y_scale, s,
+      planes, plog, total;
   int32_t ds, ep;     // router: d-slices, logit row stride
   int32_t nblk;       // router workgroups (histogram blocks)
   int32_t bm;         // rows per GEMM M-tile
@@ -113,11 +113,15 @@ struct GemmArgs {
                                  // (gathers token rows of x; NULL = contiguous)
   const void* w1; const void* w3; const void* w2;
   int d, inner, n_experts;       // inner of the group; n_experts in group
-  void* out; int ldo;            // H (dtype) / Y (f32) / S (f32)
+  void* out; int ldo;            // H (dtype) / Y / S (f32)
+  // bf16 layers: routed Y is stored as fp16 scaled by a power of two per 64
+  // columns of a row; yscale[row][d / 64] holds the inverse scales (written
+  // by DOWN, read by the fused combine).  fp32 layers: Y is fp32.
+  float* yscale;
   const void* x;                 // DOWN_SHARED residual
   // DOWN_SHARED with the combine fused (ybuf != NULL): out2[t] =
-  //   x[t] + shared(t) + sum_k gw[t,k] * ybuf[slot_row[t,k]]   (dtype out)
-  const float* ybuf; const float* gw; const int32_t* slot_row; int K;
+  //   x[t] + shared(t) + sum_k gw[t,k] * Y[slot_row[t,k]]   (dtype out)
+  const void* ybuf; const float* gw; const int32_t* slot_row; int K;
   void* out2;
   const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
   int T;                          // rows for shared group
@@ -128,9 +132,14 @@ hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const void* base; bool base_f32;   // S (f32) or x (dtype) when no shared
-  const float* y; const float* topk_w; const int32_t* slot_row;
+  const void* y;                     // fp32 rows, or fp16 rows when yscale != NULL
+  const float* yscale;               // [rows][d / 64] inverse scales of fp16 Y
+  const float* topk_w; const int32_t* slot_row;
   void* out; int dtype; int T, d, K;
 };
+
+// Columns sharing one scale in the fp16 routed-output rows of bf16 layers.
+constexpr int Y_GROUP = 64;
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace moe

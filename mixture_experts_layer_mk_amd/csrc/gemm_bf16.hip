@@ -6,9 +6,10 @@
 // 3.1)").  Stages (same as the fp32 path):
 //   GATEUP      H = silu(A W1^T) * (A W3^T), gate and up fused in one tile;
 //               routed tiles gather their token rows straight from x
-//   DOWN        Y = H W2^T (routed rows, fp32 out)
-//   DOWN_SHARED S = x + sum_s H_s W2_s^T (all tokens, fp32 out), or with the
-//               combine fused: out = x + sum_s H_s W2_s^T + sum_k g_k Y_k
+//   DOWN        Y = H W2^T (routed rows; fp16 scaled by a power of two per
+//               64 columns of a row, inverse scales beside)
+//   DOWN_SHARED with the combine fused:
+//               out = x + sum_s H_s W2_s^T + sum_k g_k Y_k
 //
 // Tiling.  A workgroup (4 waves) owns BM token rows x 256 weight rows with a
 // 64-wide k step.  Both operands are k-contiguous in memory (token rows and
@@ -62,6 +63,29 @@ __device__ __forceinline__ float silu_f(float v) {
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Two floats to packed fp16 (round to nearest even) and back.
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float h_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float h_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Scale of one 64-column group of a routed output row whose largest
+// magnitude is amax: s = 2^(15 - E) with amax = f 2^E, f in [0.5, 1), so
+// every scaled value is below 2^15 (inside fp16's range), and inv = 1 / s.
+// Both are exact powers of two (E clamped so that both stay normal).
+__device__ __forceinline__ void y_scale_of(float amax, float& s, float& inv) {
+  int E = __builtin_amdgcn_frexp_expf(amax);
+  E = min(max(E, -111), 141);
+  s = __int_as_float((142 - E) << 23);
+  inv = __int_as_float((112 + E) << 23);
 }
 
 // Instruction-scheduling groups for one k-step: N_MMA matrix ops with the
@@ -306,6 +330,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     bf16_t* out = static_cast<bf16_t*>(a.out);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
       const int m = wm * WM + mb * 32 + l32;
       if (m >= rows) continue;
       bf16_t* orow = out + (size_t)(row0 + m) * a.ldo + col_off;
@@ -326,94 +351,117 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
         }
     }
   } else if (MODE == 1) {
-    float* out = static_cast<float*>(a.out);
+    // Y rows in fp16, each 64-column group of a row scaled so that its
+    // largest magnitude lands just below 2^15; the inverse scales go to
+    // yscale[row][col / 64].  The group's columns are column blocks
+    // nb = 2 gi, 2 gi + 1 of this lane and of lane ^ 32 (same row).
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int gpr = a.d / Y_GROUP;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
       const int m = wm * WM + mb * 32 + l32;
-      if (m >= rows) continue;
-      float* orow = out + (size_t)(row0 + m) * a.ldo;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int gi = 0; gi < NB / 2; ++gi) {
+        float amax = 0.f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-          if (n >= a.d) continue;
-          float4 v;
-          v.x = acc[nb][mb][4 * g + 0];
-          v.y = acc[nb][mb][4 * g + 1];
-          v.z = acc[nb][mb][4 * g + 2];
-          v.w = acc[nb][mb][4 * g + 3];
-          *reinterpret_cast<float4*>(orow + n) = v;
-        }
-    }
-  } else if (a.ybuf == nullptr) {
-    float* out = static_cast<float*>(a.out);
-    const bf16_t* x = static_cast<const bf16_t*>(a.x);
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = wm * WM + mb * 32 + l32;
-      if (m >= rows) continue;
-      float* orow = out + (size_t)(row0 + m) * a.ldo;
-      const bf16_t* xrow = x + (size_t)(row0 + m) * a.d;
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[nb][mb][r]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        float sc, inv;
+        y_scale_of(amax, sc, inv);
+        if (m >= rows) continue;
+        uint16_t* orow = out + (size_t)(row0 + m) * a.ldo;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-          if (n >= a.d) continue;
-          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + n);
-          float4 o;
-          o.x = bf16_to_f32((bf16_t)(xv.x & 0xffff)) + acc[nb][mb][4 * g + 0];
-          o.y = bf16_to_f32((bf16_t)(xv.x >> 16)) + acc[nb][mb][4 * g + 1];
-          o.z = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
-          o.w = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
-          *reinterpret_cast<float4*>(orow + n) = o;
-        }
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+            if (n >= a.d) continue;
+            uint2 v;
+            v.x = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
+            v.y = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
+            *reinterpret_cast<uint2*>(orow + n) = v;
+          }
+        const int ng = n0 + wn * WN + gi * Y_GROUP;
+        if (hi == 0 && ng < a.d) a.yscale[(size_t)(row0 + m) * gpr + ng / Y_GROUP] = inv;
+      }
     }
   } else {
     // Combine fused: out = RNE(x + shared + sum_k g_k Y_k), the same fp32
     // operations in the same order as the separate combine (residual plus
-    // shared experts first, then the kept experts in slot order).
+    // shared experts first, then the kept experts in slot order, each Y
+    // element decoded as fp16 times its group's inverse scale).  The kept
+    // experts' rows are fetched one slot ahead, their row indices two ahead.
     bf16_t* out = static_cast<bf16_t*>(a.out2);
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
+    const uint16_t* ybuf = static_cast<const uint16_t*>(a.ybuf);
+    const float* ysc = a.yscale;
+    const int gpr = a.d / Y_GROUP;
+    const int K = a.K;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
       const int m = wm * WM + mb * 32 + l32;
       if (m >= rows) continue;
       const int t = row0 + m;
       const bf16_t* xrow = x + (size_t)t * a.d;
+      const int32_t* srt = a.slot_row + (size_t)t * K;
+      const float* gwt = a.gw + (size_t)t * K;
+      int ncol[NB][4];
       float o[NB][4][4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
-          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + n);
+          ncol[nb][g] = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
+          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + ncol[nb][g]);
           o[nb][g][0] = bf16_to_f32((bf16_t)(xv.x & 0xffff)) + acc[nb][mb][4 * g + 0];
           o[nb][g][1] = bf16_to_f32((bf16_t)(xv.x >> 16)) + acc[nb][mb][4 * g + 1];
           o[nb][g][2] = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
           o[nb][g][3] = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
         }
-      for (int k = 0; k < a.K; ++k) {
-        const float gk = a.gw[(size_t)t * a.K + k];
-        const float* yrow = a.ybuf + (size_t)a.slot_row[(size_t)t * a.K + k] * a.d;
-        float4 yv[NB][4];
+      // Scale group of column block nb: columns nb*32 .. nb*32+31 of the
+      // wave's range lie in one 64-column group.
+      int sgrp[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sgrp[nb] = min(n0 + wn * WN + nb * 32, a.d - 1) / Y_GROUP;
+      uint2 ycur[NB][4], ynxt[NB][4];
+      float scur[NB], snxt[NB];
+      auto fetch = [&](uint2 (&y)[NB][4], float (&sc)[NB], int row) {
+        const uint16_t* yr = ybuf + (size_t)row * a.d;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          sc[nb] = ysc[(size_t)row * gpr + sgrp[nb]];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) y[nb][g] = *reinterpret_cast<const uint2*>(yr + ncol[nb][g]);
+        }
+      };
+      fetch(ycur, scur, srt[0]);
+      float gcur = gwt[0];
+      int s1 = srt[min(1, K - 1)];
+      float g1 = gwt[min(1, K - 1)];
+      for (int k = 0; k < K; ++k) {
+        const int s2 = srt[min(k + 2, K - 1)];
+        const float g2 = gwt[min(k + 2, K - 1)];
+        if (k + 1 < K) fetch(ynxt, snxt, s1);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int n = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
-            yv[nb][g] = *reinterpret_cast<const float4*>(yrow + n);
+            o[nb][g][0] = fmaf(gcur, h_lo(ycur[nb][g].x) * scur[nb], o[nb][g][0]);
+            o[nb][g][1] = fmaf(gcur, h_hi(ycur[nb][g].x) * scur[nb], o[nb][g][1]);
+            o[nb][g][2] = fmaf(gcur, h_lo(ycur[nb][g].y) * scur[nb], o[nb][g][2]);
+            o[nb][g][3] = fmaf(gcur, h_hi(ycur[nb][g].y) * scur[nb], o[nb][g][3]);
           }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
+          scur[nb] = snxt[nb];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            o[nb][g][0] = fmaf(gk, yv[nb][g].x, o[nb][g][0]);
-            o[nb][g][1] = fmaf(gk, yv[nb][g].y, o[nb][g][1]);
-            o[nb][g][2] = fmaf(gk, yv[nb][g].z, o[nb][g][2]);
-            o[nb][g][3] = fmaf(gk, yv[nb][g].w, o[nb][g][3]);
-          }
+          for (int g = 0; g < 4; ++g) ycur[nb][g] = ynxt[nb][g];
+        }
+        gcur = g1; g1 = g2; s1 = s2;
       }
       bf16_t* orow = out + (size_t)t * a.d;
 #pragma unroll

@@ -86,7 +86,11 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.xp = -1;   // routed gate/up tiles gather token rows from x directly
   L.h_routed = take(TK * d.inner * esz);
   L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
-  L.y = take(TK * d.d * 4);
+  // Routed expert outputs: fp32 for fp32 layers; for bf16 layers fp16 with a
+  // power-of-two inverse scale per 64 columns of a row.
+  const bool bf16 = d.dtype == MOE_BF16;
+  L.y = take(TK * d.d * (bf16 ? 2 : 4));
+  L.y_scale = bf16 ? take(TK * (d.d / Y_GROUP) * 4) : -1;
   // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
   // layers fuse the combine into the shared down-projection.
   L.s = (d.n_shared > 0 && d.dtype != MOE_BF16) ? take((int64_t)d.T * d.d * 4) : -1;
@@ -224,6 +228,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.mode = 1; g.a = at(L.h_routed); g.lda = d.inner;
     g.w2 = routed.w2; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.y); g.ldo = d.d;
+    g.yscale = bf16 ? static_cast<float*>(at(L.y_scale)) : nullptr;
     MOE_CHECK(gemm(g));
   }
   // 7. shared down (+ residual); for bf16 layers the combine is fused here
@@ -235,7 +240,8 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
     g.out = at(L.s); g.ldo = d.d;
     if (fused) {
-      g.ybuf = static_cast<const float*>(at(L.y));
+      g.ybuf = at(L.y);
+      g.yscale = static_cast<float*>(at(L.y_scale));
       g.gw = gw;
       g.slot_row = static_cast<const int32_t*>(at(L.slot_row));
       g.K = d.top_k;
@@ -249,7 +255,9 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     CombineArgs c{};
     c.base = d.n_shared > 0 ? at(L.s) : x;
     c.base_f32 = d.n_shared > 0;
-    c.y = static_cast<const float*>(at(L.y)); c.topk_w = gw; c.slot_row = static_cast<const int32_t*>(at(L.slot_row));
+    c.y = at(L.y);
+    c.yscale = bf16 ? static_cast<const float*>(at(L.y_scale)) : nullptr;
+    c.topk_w = gw; c.slot_row = static_cast<const int32_t*>(at(L.slot_row));
     c.out = out; c.dtype = bf16 ? 1 : 0; c.T = d.T; c.d = d.d; c.K = d.top_k;
     MOE_CHECK(launch_combine(c, s));
   }
@@ -287,7 +295,8 @@ moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
   out->xp = L.xp;
   out->h_routed = L.h_routed;
   out->h_shared = L.h_shared;
-  out->y_f32 = L.y;
+  out->y = L.y;
+  out->y_scale_f32 = L.y_scale;
   out->s_f32 = L.s;
   out->total_bytes = L.total;
   return MOE_OK;

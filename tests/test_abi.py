@@ -83,7 +83,10 @@ def test_workspace_size_and_layout():
     assert all(o % 256 == 0 for o in offs) and max(offs) < n
     TK = 16384 * 6
     assert lay["xp"] == -1          # token rows are gathered by the GEMM
-    assert lay["y_f32"] - lay["h_routed"] >= TK * 1408 * 2
+    assert lay["y"] - lay["h_routed"] >= TK * 1408 * 2
+    assert lay["y_scale_f32"] - lay["y"] >= TK * 2048 * 2     # fp16 routed outputs
+    f32y = moe.workspace_layout(desc(dtype="f32"))
+    assert f32y["y_scale_f32"] == -1                             # fp32 routed outputs
     assert lay["s_f32"] == -1       # bf16: the combine is fused into the shared GEMM
     f32 = moe.workspace_layout(desc(dtype="f32"))
     assert f32["s_f32"] >= 0 and f32["s_f32"] + 16384 * 2048 * 4 <= f32["total_bytes"]
