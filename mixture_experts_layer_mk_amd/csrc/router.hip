@@ -20,6 +20,8 @@
 //     block): scores in fp32, group limit, top-K kept in registers ordered
 //     by (key descending, index ascending), gate weights; then per expert a
 //     wave ballot gives the block's count and each slot's in-block rank.
+// bf16 layers with at most 64 experts, K <= 8 and no group limit run 2 and 3
+// fused in one kernel per 64-token block (4 below).
 #include "common.h"
 
 namespace moe {
@@ -310,6 +312,234 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// 4. fused logits + selection (bf16 x, at most 64 experts, K <= 8, no
+//    group limit)
+// ---------------------------------------------------------------------------
+// One workgroup (4 waves) per block of 64 tokens (one histogram block):
+//  a. logits: wave q takes the q-th quarter of the hidden dimension and
+//     computes 64 tokens x 64 experts of it on the matrix cores (gate parts
+//     lo, mid, hi as in 2a); the four quarter sums are added in order through
+//     LDS, then the logit bias.
+//  b. selection: four lanes per token, each over a quarter of the experts:
+//     softmax (or sigmoid) with max and sum over the quad, a local top-K,
+//     then K merge rounds; round j's winner (key descending, index
+//     ascending) is the j-th kept expert.
+//  c. block histogram and in-block ranks by ballots over the block's tokens.
+constexpr int FR_TOK = 64;
+constexpr int FR_KMAX = 8;   // largest K the fused path takes
+
+// Exchange with the lane whose index differs in bit 0 / bit 1 (quad permutes).
+__device__ __forceinline__ int quad_xor1i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ int quad_xor2i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+}
+__device__ __forceinline__ float quad_xor1(float v) { return __int_as_float(quad_xor1i(__float_as_int(v))); }
+__device__ __forceinline__ float quad_xor2(float v) { return __int_as_float(quad_xor2i(__float_as_int(v))); }
+
+__global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
+  __shared__ float red[4][FR_TOK][65];          // quarter sums, then logits in red[0]
+  __shared__ int sel[FR_TOK][MAX_TOPK];
+  __shared__ uint64_t masks[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int t0 = blockIdx.x * FR_TOK;
+  const int E = a.E, K = a.K, T = a.T;
+
+  // a. logits of the wave's quarter of the hidden dimension
+  {
+    const bf16_t* x = static_cast<const bf16_t*>(a.x);
+    const int kq = a.d / 4;                      // multiple of 16
+    const int k0 = wave * kq;
+    const size_t pn = (size_t)E * a.d;
+    const bf16_t* xp[2];
+    const bf16_t* wp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      xp[b] = x + (size_t)min(t0 + b * 32 + l32, T - 1) * a.d + k0 + 8 * hi;
+      wp[b] = a.planes + (size_t)min(b * 32 + l32, E - 1) * a.d + k0 + 8 * hi;
+    }
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    constexpr int U = 4;   // k-steps of 16 per batch (32 loads in flight)
+    int k = 0;
+    auto step = [&](const bf16x8 (&xf)[2], const bf16x8 (&w)[2][3]) {
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][2], xf[tb], acc[eb][tb], 0, 0, 0);
+          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][1], xf[tb], acc[eb][tb], 0, 0, 0);
+          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][0], xf[tb], acc[eb][tb], 0, 0, 0);
+        }
+    };
+    for (; k + 16 * U <= kq; k += 16 * U) {
+      bf16x8 xf[U][2], w[U][2][3];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          xf[u][b] = *reinterpret_cast<const bf16x8*>(xp[b] + k + 16 * u);
+#pragma unroll
+          for (int p = 0; p < 3; ++p)
+            w[u][b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + k + 16 * u);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) step(xf[u], w[u]);
+    }
+    for (; k < kq; k += 16) {
+      bf16x8 xf[2], w[2][3];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        xf[b] = *reinterpret_cast<const bf16x8*>(xp[b] + k);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) w[b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + k);
+      }
+      step(xf, w);
+    }
+    // acc[eb][tb][r] = D[e][t]: e = eb*32 + 8*(r/4) + 4*hi + r%4, t = tb*32 + l32
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[wave][tb * 32 + l32][eb * 32 + 8 * (r / 4) + 4 * hi + (r % 4)] = acc[eb][tb][r];
+  }
+  __syncthreads();
+  for (int i = tid; i < FR_TOK * 64; i += 256) {
+    const int tt = i >> 6, e = i & 63;
+    float v = ((red[0][tt][e] + red[1][tt][e]) + red[2][tt][e]) + red[3][tt][e];
+    if (a.logit_bias && e < E) v += a.logit_bias[e];
+    red[0][tt][e] = v;
+  }
+  __syncthreads();
+
+  // b. selection: four lanes per token (16 tokens per wave); lane quarter q
+  // scans experts 16q .. 16q + 15: softmax max and sum over the quad, a
+  // local top-K in registers, then K rounds merging the four lists' heads
+  // with quad permutes (no LDS traffic).
+  {
+    const int tt = wave * 16 + (lane >> 2), q = lane & 3;
+    const int t = t0 + tt;
+    float l[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = q * 16 + i;
+      l[i] = e < E ? red[0][tt][e] : -INFINITY;
+    }
+    float s[16];
+    if (a.score == 0) {
+      float m = l[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, l[i]);
+      m = fmaxf(m, quad_xor1(m));
+      m = fmaxf(m, quad_xor2(m));
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = q * 16 + i < E ? expf(l[i] - m) : 0.f;
+        z += s[i];
+      }
+      z += quad_xor1(z);
+      z += quad_xor2(z);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = s[i] / z;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = q * 16 + i < E ? 1.f / (1.f + expf(-l[i])) : 0.f;
+    }
+    // local top-K, sorted by (key descending, index ascending)
+    float tk[FR_KMAX], ts[FR_KMAX];
+    int ti[FR_KMAX];
+#pragma unroll
+    for (int j = 0; j < FR_KMAX; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = q * 16 + i;
+      if (e >= E) break;
+      float ck = s[i] + (a.select_bias ? a.select_bias[e] : 0.f);
+      if (ck != ck) ck = -INFINITY;             // NaN never outranks a score
+      float cs = s[i];
+      int ci = e;
+#pragma unroll
+      for (int j = 0; j < FR_KMAX; ++j) {
+        if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
+          const float k2 = tk[j], s2 = ts[j];
+          const int i2 = ti[j];
+          tk[j] = ck; ts[j] = cs; ti[j] = ci;
+          ck = k2; cs = s2; ci = i2;
+        }
+      }
+    }
+    // merge: round j takes the best head of the quad's four lists
+    float gsum = 0.f, os[FR_KMAX];
+    int oi[FR_KMAX];
+#pragma unroll
+    for (int j = 0; j < FR_KMAX; ++j) {
+      if (j >= K) break;
+      float bk = tk[0], bs = ts[0];
+      int bi = ti[0];
+      {
+        const float ok = quad_xor1(bk), os1 = quad_xor1(bs);
+        const int oi1 = quad_xor1i(bi);
+        if (better(ok, oi1, bk, bi)) { bk = ok; bi = oi1; bs = os1; }
+      }
+      {
+        const float ok = quad_xor2(bk), os2 = quad_xor2(bs);
+        const int oi2 = quad_xor2i(bi);
+        if (better(ok, oi2, bk, bi)) { bk = ok; bi = oi2; bs = os2; }
+      }
+      oi[j] = bi; os[j] = bs;
+      gsum += bs;
+      if (ti[0] == bi) {                        // this lane's head was taken
+#pragma unroll
+        for (int u = 0; u + 1 < FR_KMAX; ++u) { tk[u] = tk[u + 1]; ts[u] = ts[u + 1]; ti[u] = ti[u + 1]; }
+        tk[FR_KMAX - 1] = -INFINITY; ti[FR_KMAX - 1] = 0x7fffffff; ts[FR_KMAX - 1] = 0.f;
+      }
+    }
+    if (q == 0 && t < T) {
+#pragma unroll
+      for (int j = 0; j < FR_KMAX; ++j) {
+        if (j >= K) break;
+        float g = os[j];
+        if (a.norm_topk) g = g / gsum;
+        g *= a.routed_scale;
+        a.topk_idx[(size_t)t * K + j] = oi[j];
+        a.topk_w[(size_t)t * K + j] = g;
+        sel[tt][j] = oi[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // c. block histogram and in-block ranks (token order = lane order)
+  const int t = t0 + lane;
+  const bool live = t < T;
+  uint64_t mine = 0;
+  if (live)
+    for (int j = 0; j < K; ++j) mine |= 1ull << sel[lane][j];
+  for (int ee = wave; ee < E; ee += 4) {
+    const uint64_t m = __ballot(live && ((mine >> ee) & 1));
+    if (lane == 0) masks[ee] = m;
+  }
+  __syncthreads();
+  if (tid < E) a.block_counts[(size_t)tid * gridDim.x + blockIdx.x] = __popcll(masks[tid]);
+  if (wave == 0 && live) {
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < K; ++j)
+      a.rank[(size_t)t * K + j] = __popcll(masks[sel[lane][j]] & below);
+  }
+}
+
 }  // namespace
 
 int router_tokens_per_block(int) { return 64; }
@@ -323,7 +553,19 @@ int router_dsplit(int T, int E, int d, int dtype) {
   return ds;
 }
 
+bool router_fused(int E, int K, int n_groups, int dtype) {
+  return dtype == 1 && E <= 64 && K <= FR_KMAX && n_groups == 1;
+}
+
 hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
+  if (router_fused(r.E, r.K, r.n_groups, r.dtype)) {
+    const int64_t n = (int64_t)r.E * r.d;
+    hipLaunchKernelGGL(split_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       r.w_gate, r.planes, n);
+    hipLaunchKernelGGL(router_fused_kernel, dim3((r.T + FR_TOK - 1) / FR_TOK), dim3(256), 0, s,
+                       r);
+    return hipGetLastError();
+  }
   // 1 + 2: partial logits
   LogitsArgs la{};
   la.T = r.T; la.d = r.d; la.E = r.E; la.ep = r.ep; la.ds = r.ds;
