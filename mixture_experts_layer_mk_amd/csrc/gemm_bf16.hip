@@ -125,8 +125,14 @@ __host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
 }
 
 // MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED.  WAVES_M x (4 / WAVES_M) waves.
+// One tile: rows [row0, row0 + rows) (at most BM) of the M dimension (expert
+// e for routed tiles) times N-tile nt, through the LDS buffers As0/As1 (at
+// least BM x 128 B each) and Bs0/Bs1.  MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED;
+// WAVES_M x (4 / WAVES_M) waves.
 template <int MODE, int BM, int WAVES_M>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows, int e,
+                                          int nt, u32x4* As0, u32x4* As1, u32x4* Bs0,
+                                          u32x4* Bs1) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -134,40 +140,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int B_LD = BN / 32;     // (B)
   static_assert(MB >= 1 && NB >= 2 && (NB % 2) == 0, "tile shape");
 
-  // Two LDS buffers per operand as distinct objects: accesses name their
-  // buffer statically, so the compiler can tell the direct loads into one
-  // buffer from the operand reads of the other and need not wait between.
-  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
-  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
-  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
-  // one M-tile are adjacent, then the next M-tile (same expert, same weight
-  // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
-  // both its token-row tiles and its weight tiles in L2.
-  const int ndim = n_tiles_of<MODE, BM>(a);
-  int mt, nt;
-  {
-    const int full = ndim / NGRP;
-    const int ntg = L / (mdim * NGRP);
-    const int g = (ntg < full) ? NGRP : ndim - full * NGRP;
-    const int rem = L - ntg * mdim * NGRP;
-    mt = rem / g;
-    nt = ntg * NGRP + rem % g;
-  }
-
-  int row0, rows, e;
-  if (routed) {
-    if (mt >= *a.n_tiles) return;
-    const MTile t = a.tiles[mt];
-    row0 = t.row0; rows = t.rows; e = t.expert;
-  } else {
-    row0 = mt * BM; rows = min(BM, a.T - row0); e = 0;
-  }
 
   // This lane's slot in a wave's 1 KB load block: LDS row lr (of 8) and the
   // global chunk that belongs in slot (lane & 7) of that row.
@@ -476,6 +451,50 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
           *reinterpret_cast<uint2*>(orow + n) = v;
         }
     }
+  }
+}
+
+// The grouped GEMM: one workgroup per tile.  Routed tail tiles of at most
+// BM / 2 rows (an expert's last rows) run the half-height tile layout, which
+// does half the matrix work.
+template <int MODE, int BM, int WAVES_M>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
+  // Two LDS buffers per operand as distinct objects: accesses name their
+  // buffer statically, so the compiler can tell the direct loads into one
+  // buffer from the operand reads of the other and need not wait between.
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
+
+  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
+  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
+  // one M-tile are adjacent, then the next M-tile (same expert, same weight
+  // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
+  // both its token-row tiles and its weight tiles in L2.
+  const int ndim = n_tiles_of<MODE, BM>(a);
+  int mt, nt;
+  {
+    const int full = ndim / NGRP;
+    const int ntg = L / (mdim * NGRP);
+    const int g = (ntg < full) ? NGRP : ndim - full * NGRP;
+    const int rem = L - ntg * mdim * NGRP;
+    mt = rem / g;
+    nt = ntg * NGRP + rem % g;
+  }
+  if (routed) {
+    if (mt >= *a.n_tiles) return;
+    const MTile t = a.tiles[mt];
+    if constexpr (BM >= 128) {
+      if (t.rows <= BM / 2) {
+        gemm_tile<MODE, BM / 2, 1>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1);
+        return;
+      }
+    }
+    gemm_tile<MODE, BM, WAVES_M>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1);
+  } else {
+    const int row0 = mt * BM;
+    gemm_tile<MODE, BM, WAVES_M>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, Bs0, Bs1);
   }
 }
 
