@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--config", default="deepseekmoe-16b")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="oracle sample size (0: all tokens of the workload)")
-    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for "
@@ -211,6 +211,21 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
+    # Attainable bf16 matrix rate on this GPU: the vendor GEMM (torch.matmul,
+    # hipBLASLt) on a square 8192^3 problem, timed with events.
+    a8 = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b8 = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        a8 @ b8
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        a8 @ b8
+    e1.record()
+    torch.cuda.synchronize()
+    attain = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 10 / 1e3) / 1e12
+    del a8, b8
+
     cpu = None
     if not args.no_cpu_baseline:
         n = min(args.cpu_tokens or cfg.T, cfg.T)
@@ -232,6 +247,8 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "events_ms_per_step": round(total_ev, 4),
         "roofline": roofline,
+        "attainable_bf16_tflops": {"value": round(attain, 1),
+                                   "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
