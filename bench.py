@@ -35,11 +35,11 @@ def log(msg):
 
 
 def source_hash() -> str:
+    """Hash of the dominant kernel's sources (its file and the shared header)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_mk_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in ("common.h", "gemm_bf16.hip"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -211,6 +211,27 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
+    # The step after a training forward: the auxiliary-loss-free bias update
+    # on this forward's expert counts (one small kernel), timed on its own.
+    _, rt = moe.moe_layer_forward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k,
+                                  score=cfg.score, norm_topk=cfg.norm_topk,
+                                  n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                                  select_bias=d["select_bias"], logit_bias=d["logit_bias"],
+                                  routed_scale=cfg.routed_scale, workspace=ws,
+                                  return_routing=True)
+    sb = torch.zeros(cfg.n_routed, dtype=torch.float32, device=dev)
+    rel = torch.empty_like(sb)
+    for _ in range(3):
+        moe.moe_bias_update(rt["expert_counts"], 1e-3, sb, rel)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(50):
+        moe.moe_bias_update(rt["expert_counts"], 1e-3, sb, rel)
+    e1.record()
+    torch.cuda.synchronize()
+    bias_us = e0.elapsed_time(e1) / 50 * 1e3
+    max_rel_load = float(rel.max())
+
     # Attainable bf16 matrix rate on this GPU: the vendor GEMM (torch.matmul,
     # hipBLASLt) on a square 8192^3 problem, timed with events.
     a8 = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
@@ -247,6 +268,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "events_ms_per_step": round(total_ev, 4),
         "roofline": roofline,
+        "bias_update": {"us_per_call": round(bias_us, 2), "max_relative_load": round(max_rel_load, 4)},
         "attainable_bf16_tflops": {"value": round(attain, 1),
                                    "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
         "cpu_baseline": cpu,

@@ -171,6 +171,26 @@ moe_status_t moe_layer_forward_traced(
     size_t workspace_bytes, void* stream, void* const* events,
     int32_t n_events);
 
+/* Auxiliary-loss-free load balancing, the step after a training forward pass
+ * (DeepSeek-V3 Technical Report summary, "2. Architecture": the per-expert
+ * selection bias is updated after each step by whether the expert was over-
+ * or underloaded).  With total = sum of counts[0 .. n_routed) (= T * top_k for
+ * a dropless forward) and count_e * n_routed compared with total exactly in
+ * integers:
+ *   select_bias[e] -= gamma  if count_e * n_routed > total  (overloaded)
+ *   select_bias[e] += gamma  if count_e * n_routed < total  (underloaded)
+ *   unchanged otherwise; each update is one fp32 addition.
+ *   rel_load[e] = (float)(count_e * n_routed) / (float)total  (1 = balanced;
+ *                 0 when total is 0)
+ * counts      [n_routed] int32 device (e.g. the forward's expert_counts), read
+ * select_bias [n_routed] float device, updated in place, or NULL
+ * rel_load    [n_routed] float device, written, or NULL
+ * 1 <= n_routed <= 256 (MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED otherwise),
+ * counts non-NULL and gamma finite (MOE_ERR_INVALID_ARG).  Asynchronous on
+ * `stream`; allocates nothing. */
+moe_status_t moe_bias_update(const int32_t* counts, int32_t n_routed, float gamma,
+                             float* select_bias, float* rel_load, void* stream);
+
 /* Static description of a status code. */
 const char* moe_strerror(moe_status_t status);
 

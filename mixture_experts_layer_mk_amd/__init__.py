@@ -6,7 +6,7 @@ C ABI of ``include/moe_layer.h``); this package is its Python binding.
 from ._lib import (MOE_BF16, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_OK,
                    HipEvents, MoeError, MoeLayerDesc, header_functions,
-                   load_library, make_desc, moe_layer_forward, strerror,
+                   load_library, make_desc, moe_bias_update, moe_layer_forward, strerror,
                    trace_stage_names, validate, workspace_layout,
                    workspace_size)
 
@@ -14,6 +14,6 @@ __all__ = [
     "MOE_BF16", "MOE_ERR_ALIAS", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG",
     "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_OK",
     "HipEvents", "MoeError", "MoeLayerDesc", "header_functions",
-    "load_library", "make_desc", "moe_layer_forward", "strerror",
+    "load_library", "make_desc", "moe_bias_update", "moe_layer_forward", "strerror",
     "trace_stage_names", "validate", "workspace_layout", "workspace_size",
 ]

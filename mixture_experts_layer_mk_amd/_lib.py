@@ -83,6 +83,8 @@ def load_library():
     lib.moe_layer_trace_stage_count.restype = ctypes.c_int32
     lib.moe_layer_trace_stage_name.argtypes = [ctypes.c_int32]
     lib.moe_layer_trace_stage_name.restype = ctypes.c_char_p
+    lib.moe_bias_update.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, P]
+    lib.moe_bias_update.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -233,6 +235,33 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
     if return_routing:
         return out, {"topk_idx": idx, "topk_w": wts, "expert_counts": cnt}
     return out
+
+
+def moe_bias_update(counts, gamma: float, select_bias=None, rel_load=None, stream=None):
+    """Auxiliary-loss-free bias update after a step: ``select_bias`` [E] fp32
+    (updated in place, or None) moves by ``gamma`` down for overloaded and up
+    for underloaded experts, judged from ``counts`` [E] int32 (e.g. the
+    forward's expert_counts).  Returns the relative loads [E] fp32."""
+    import torch
+    lib = load_library()
+    dev = counts.device
+    if dev.type != "cuda":
+        raise ValueError("counts must be a GPU tensor")
+    E = counts.shape[0]
+    _check_tensor("counts", counts, torch.int32, (E,), dev)
+    if select_bias is not None:
+        _check_tensor("select_bias", select_bias, torch.float32, (E,), dev)
+    if rel_load is None:
+        rel_load = torch.empty((E,), dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("rel_load", rel_load, torch.float32, (E,), dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.moe_bias_update(_ptr(counts), E, float(gamma), _ptr(select_bias),
+                             _ptr(rel_load), stream)
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return rel_load
 
 
 class HipEvents:

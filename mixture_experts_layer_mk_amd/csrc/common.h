@@ -140,6 +140,12 @@ struct CombineArgs {
   void* out; int dtype; int T, d, K;
 };
 
+struct BiasUpdateArgs {
+  const int32_t* counts; int n; float gamma;
+  float* bias; float* rel_load;       // either may be NULL
+};
+hipError_t launch_bias_update(const BiasUpdateArgs& a, hipStream_t s);
+
 // Columns sharing one scale in the fp16 routed-output rows of bf16 layers.
 constexpr int Y_GROUP = 64;
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -334,6 +334,17 @@ moe_status_t moe_layer_forward_traced(
                       stream, events);
 }
 
+moe_status_t moe_bias_update(const int32_t* counts, int32_t n_routed, float gamma,
+                             float* select_bias, float* rel_load, void* stream) {
+  if (!counts || n_routed < 1 || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  if (n_routed > MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  BiasUpdateArgs a{};
+  a.counts = counts; a.n = n_routed; a.gamma = gamma;
+  a.bias = select_bias; a.rel_load = rel_load;
+  if (launch_bias_update(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 const char* moe_strerror(moe_status_t status) {
   switch (status) {
     case MOE_OK: return "success";

@@ -5,13 +5,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 shares no code with it; the product path fails loudly when its compiled
 library is missing instead of falling back to anything here.
 """
-from .moe_oracle import (Dispatch, Routing, activated_macs_per_token, dispatch,
+from .moe_oracle import (Dispatch, Routing, activated_macs_per_token, bias_update, dispatch,
                          expert_flops_per_token, gate_logits, gate_scores,
                          group_scores, moe_forward, moe_forward_bruteforce,
                          route, select_experts, silu, swiglu_ffn)
 
 __all__ = [
-    "Dispatch", "Routing", "activated_macs_per_token", "dispatch",
+    "Dispatch", "Routing", "activated_macs_per_token", "bias_update", "dispatch",
     "expert_flops_per_token", "gate_logits", "gate_scores", "group_scores",
     "moe_forward", "moe_forward_bruteforce", "route", "select_experts", "silu",
     "swiglu_ffn",

@@ -357,3 +357,32 @@ def expert_flops_per_token(d: int, top_k: int, inner: int, n_shared: int,
                            shared_inner: int) -> int:
     """FLOPs of the activated expert FFNs per token (2 per multiply-add)."""
     return 2 * 3 * d * (top_k * inner + n_shared * shared_inner)
+
+
+def bias_update(counts, bias, gamma: float):
+    """Auxiliary-loss-free load balancing, the step after a training forward
+    pass (DeepSeek-V3 Technical Report summary, "2. Architecture": the
+    per-expert bias is updated after each step by whether the expert was
+    overloaded or underloaded).
+
+    Reading of that sentence: with ``total`` tokens routed over ``n`` experts
+    the balanced load is ``total / n``; an expert above it is overloaded and
+    its bias goes down by ``gamma``, one below it is underloaded and its bias
+    goes up by ``gamma``, one exactly at it keeps its bias.  The comparison
+    ``count * n`` vs ``total`` is made on Python integers (exact); each update
+    is a single fp32 addition.  Also returns the relative load
+    ``count * n / total`` (1 = balanced), the exact quotient rounded to fp32.
+    """
+    counts = [int(c) for c in counts]
+    n = len(counts)
+    total = sum(counts)
+    new = np.array(bias, dtype=np.float32).copy()
+    g = np.float32(gamma)
+    rel = np.zeros(n, dtype=np.float32)
+    for e, c in enumerate(counts):
+        if c * n > total:
+            new[e] = np.float32(new[e] - g)
+        elif c * n < total:
+            new[e] = np.float32(new[e] + g)
+        rel[e] = np.float32(c * n / total) if total > 0 else np.float32(0.0)
+    return new, rel
