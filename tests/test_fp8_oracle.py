@@ -32,6 +32,23 @@ def test_code_order_and_round_trip():
     assert np.array_equal(fp8.e4m3_encode(fp8.e4m3_decode(codes)), codes)
 
 
+def test_encode_is_the_nearest_value_brute_force():
+    """The encoder against a plain search of the 127 finite magnitudes: the
+    nearest one, the even code on a tie."""
+    mags = fp8.e4m3_decode(np.arange(0x7F))
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.uniform(-448, 448, 4000),
+                        rng.uniform(-0.05, 0.05, 4000),
+                        (mags[1:] + mags[:-1]) / 2,                 # every midpoint
+                        -(mags[1:] + mags[:-1]) / 2])
+    got = fp8.e4m3_encode(v)
+    for x, c in zip(v, got):
+        dist = np.abs(mags - abs(x))
+        best = np.flatnonzero(dist == dist.min())
+        want = best[0] if best.size == 1 else [b for b in best if b % 2 == 0][0]
+        assert (int(c) & 0x7F) == want and (int(c) >> 7) == int(np.signbit(x)), x
+
+
 def test_round_to_nearest_ties_to_even():
     enc = lambda x: int(fp8.e4m3_encode([x])[0])
     assert enc(1.0625) == 0x38            # midpoint of 1 (0x38) and 1.125 (0x39): even
@@ -146,3 +163,48 @@ def test_fp8_layer_error_against_bf16_layer_is_quantisation_sized():
     y, _ = oracle.moe_forward(x, wg, (w1, w3, w2), None, K)
     rel = np.sqrt(np.mean((y8 - y) ** 2)) / np.sqrt(np.mean((y - x) ** 2))
     assert 0.01 < rel < 0.15       # E4M3 keeps 3 mantissa bits: a few percent
+
+
+def _requant(h):
+    return fp8.dequantize_1x128(*fp8.quantize_1x128(h))
+
+
+def test_requantisation_spread_bounds_every_move():
+    """``requantisation_spread`` against brute force: random moves of every
+    value by at most margin x its group's maximum never change the quantised
+    value by more than the spread; moving a whole group by +/- the margin
+    reaches it where the scale cannot change; zero margin gives zero."""
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((6, 384)) * np.exp(rng.uniform(-6, 6, (6, 1)))
+    h[0, :128] *= 56.0 / np.abs(h[0, :128]).max()         # max exactly 448 x 2^-3
+    h[1, 128:256] = 0.0                                   # a group of zeros ...
+    h[1, 130] = 1e-3                                      # ... but one tiny value
+    h[2, 256:] *= 1e-4                                    # tiny values: subnormal codes
+    v = _requant(h)
+    assert np.array_equal(fp8.requantisation_spread(h, 0.0), np.zeros_like(h))
+    margin = 1e-3
+    spread = fp8.requantisation_spread(h, margin)
+    R, C = h.shape
+    gmax = np.abs(h.reshape(R, C // 128, 128)).max(2)
+    delta = np.repeat(margin * gmax, 128, axis=1)
+    worst = np.zeros_like(h)
+    moves = [np.full_like(h, 1.0), np.full_like(h, -1.0)]
+    moves += [rng.uniform(-1, 1, h.shape) for _ in range(300)]
+    moves += [np.sign(rng.uniform(-1, 1, h.shape)) for _ in range(100)]
+    for m in moves:
+        dev = np.abs(_requant(h + m * delta) - v)
+        assert np.all(dev <= spread * (1 + 1e-12)), np.argwhere(dev > spread)[0]
+        worst = np.maximum(worst, dev)
+    # the group on the scale boundary: moving up changes its scale
+    assert fp8.quantize_1x128(h + delta)[1][0, 0] == fp8.quantize_1x128(h)[1][0, 0] + 1
+    # where the scale is fixed the two uniform moves attain the spread
+    E = lambda a: np.repeat(fp8.quantize_1x128(a)[1], 128, axis=1)
+    fixed = (E(h + delta) == E(h)) & (E(h - delta) == E(h))
+    fixed &= np.repeat(np.abs(gmax) * (1 + margin) < 448.0 * np.exp2(
+        fp8.quantize_1x128(h)[1].astype(np.int64) - 127), 128, axis=1)
+    fixed &= np.repeat(np.abs(gmax) * (1 - margin) > 224.0 * np.exp2(
+        fp8.quantize_1x128(h)[1].astype(np.int64) - 127), 128, axis=1)
+    assert fixed.sum() > 0.5 * h.size
+    np.testing.assert_array_equal(worst[fixed], spread[fixed])
+    # tiny values near zero: a move can flip the sign of a subnormal code
+    assert spread[1, 131] > 0 and spread[1, 131] <= 2 * margin * 1e-3
