@@ -52,7 +52,13 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed     */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+/* Layer precision.  MOE_FP8: x and out bf16, router fp32 as for bf16; the
+ * expert GEMMs take FP8 operands: weights given as OCP E4M3 codes with one
+ * power-of-two scale per 128 x 128 block (see moe_ffn_weights_t), token rows
+ * and SwiGLU activations quantised inside the call per 1 x 128 along the
+ * reduction dimension (DeepSeek-V3 Technical Report summary, "3.3 FP8
+ * Training" and "B.2 Discussion About Block-Wise Quantization"). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype_t;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_t;
 
 /* Shape and routing options of one MoE layer. */
@@ -71,18 +77,25 @@ typedef struct {
   int32_t score;        /* moe_score_t                                          */
   int32_t norm_topk;    /* 1: kept gate weights renormalised to sum to 1       */
   float routed_scale;   /* factor on the routed gate weights (1.0 = none)      */
-  int32_t dtype;        /* moe_dtype_t of x, out and all expert weights        */
+  int32_t dtype;        /* moe_dtype_t: of x, out and all expert weights for
+                           F32 / BF16; MOE_FP8 see above                        */
 } moe_layer_desc_t;
 
 /* One set of expert weights, stacked over E experts (E = n_routed or
  * n_shared), in the output-major layout of a linear layer's weight:
  *   w1, w3 : [E][inner][d]   (gate and up projections, d -> inner)
  *   w2     : [E][d][inner]   (down projection, inner -> d)
- * dtype = desc->dtype. */
+ * Element type desc->dtype (F32, BF16) or one E4M3 byte (FP8).  FP8 only:
+ *   s1, s3 : [E][inner / 128][d / 128] and s2 : [E][d / 128][inner / 128]
+ *   scale bytes b of the 128 x 128 blocks (block value = code x 2^(b - 127));
+ *   NULL for F32 / BF16.  moe_quantize_fp8_blocks produces this format. */
 typedef struct {
   const void* w1;
   const void* w3;
   const void* w2;
+  const uint8_t* s1;
+  const uint8_t* s3;
+  const uint8_t* s2;
 } moe_ffn_weights_t;
 
 /* Byte offsets of the intermediate buffers inside the workspace, for
@@ -108,14 +121,20 @@ typedef struct {
   int64_t y_scale_f32;      /* [T * top_k][d / 64] those inverse scales (bf16
                                layers; -1 otherwise)                          */
   int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32); -1 for
-                               bf16 layers, whose combine is fused into the
-                               shared down-projection                         */
+                               bf16 / FP8 layers, whose combine is fused into
+                               the shared down-projection                     */
+  int64_t x_q;              /* FP8: [T][d] E4M3 token rows (-1 otherwise)     */
+  int64_t x_scale;          /* FP8: [T][d / 128] their scale bytes            */
+  int64_t h_routed_scale;   /* FP8: [T * top_k][inner / 128] scale bytes of
+                               h_routed (E4M3 codes for FP8 layers)           */
+  int64_t h_shared_scale;   /* FP8: [T][n_shared * shared_inner / 128]        */
   int64_t total_bytes;      /* = moe_layer_workspace_size                     */
 } moe_workspace_layout_t;
 
 /* Host-only check of a descriptor; no device call.  Returns MOE_OK,
  * MOE_ERR_INVALID_ARG (including desc == NULL) or MOE_ERR_UNSUPPORTED
- * (bf16 needs d, inner and shared_inner to be multiples of 64; fp32 needs
+ * (bf16 needs d, inner and shared_inner to be multiples of 64, FP8 multiples
+ * of 128 with d, inner and n_shared * shared_inner at most 8192; fp32 needs
  * multiples of 4; row counts times widths must stay below 2^31). */
 moe_status_t moe_layer_validate(const moe_layer_desc_t* desc);
 
@@ -170,6 +189,17 @@ moe_status_t moe_layer_forward_traced(
     int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
     size_t workspace_bytes, void* stream, void* const* events,
     int32_t n_events);
+
+/* Weights to the FP8 layer's format: `src` [batch][rows][cols] (src_dtype
+ * MOE_F32 or MOE_BF16, device) to E4M3 `codes` (same shape, one byte each)
+ * and `scales` [batch][rows / 128][cols / 128]: each 128 x 128 block gets the
+ * smallest power of two 2^E with max|v| <= 448 * 2^E (byte E + 127, 127 for
+ * an all-zero block) and each value the E4M3 code nearest to v * 2^-E, ties
+ * to even.  rows and cols multiples of 128 (MOE_ERR_UNSUPPORTED otherwise);
+ * asynchronous on `stream`; allocates nothing. */
+moe_status_t moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t batch,
+                                     int32_t rows, int32_t cols, uint8_t* codes,
+                                     uint8_t* scales, void* stream);
 
 /* Auxiliary-loss-free load balancing, the step after a training forward pass
  * (DeepSeek-V3 Technical Report summary, "2. Architecture": the per-expert

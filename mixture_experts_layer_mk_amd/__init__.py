@@ -3,17 +3,19 @@
 The compute lives in ``libmoe_layer.so`` (hand-written HIP kernels behind the
 C ABI of ``include/moe_layer.h``); this package is its Python binding.
 """
-from ._lib import (MOE_BF16, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG,
+from ._lib import (MOE_BF16, MOE_FP8, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_OK,
                    HipEvents, MoeError, MoeLayerDesc, header_functions,
-                   load_library, make_desc, moe_bias_update, moe_layer_forward, strerror,
+                   load_library, make_desc, moe_bias_update, moe_layer_forward,
+                   quantize_fp8_blocks, strerror,
                    trace_stage_names, validate, workspace_layout,
                    workspace_size)
 
 __all__ = [
-    "MOE_BF16", "MOE_ERR_ALIAS", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG",
+    "MOE_BF16", "MOE_FP8", "MOE_ERR_ALIAS", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG",
     "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_OK",
     "HipEvents", "MoeError", "MoeLayerDesc", "header_functions",
-    "load_library", "make_desc", "moe_bias_update", "moe_layer_forward", "strerror",
+    "load_library", "make_desc", "moe_bias_update", "moe_layer_forward",
+    "quantize_fp8_blocks", "strerror",
     "trace_stage_names", "validate", "workspace_layout", "workspace_size",
 ]

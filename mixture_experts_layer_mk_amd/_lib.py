@@ -22,7 +22,7 @@ MOE_ERR_UNSUPPORTED = -3
 MOE_ERR_ALIAS = -4
 MOE_ERR_HIP = -5
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 
@@ -38,14 +38,15 @@ class MoeLayerDesc(ctypes.Structure):
 
 class FfnWeights(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
-                ("w2", ctypes.c_void_p)]
+                ("w2", ctypes.c_void_p), ("s1", ctypes.c_void_p),
+                ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "topk_idx_i32", "topk_w_f32", "counts_i32", "offsets_i32",
         "slot_row_i32", "row_src_i32", "xp", "h_routed", "h_shared", "y", "y_scale_f32",
-        "s_f32", "total_bytes")]
+        "s_f32", "x_q", "x_scale", "h_routed_scale", "h_shared_scale", "total_bytes")]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +84,9 @@ def load_library():
     lib.moe_layer_trace_stage_count.restype = ctypes.c_int32
     lib.moe_layer_trace_stage_name.argtypes = [ctypes.c_int32]
     lib.moe_layer_trace_stage_name.restype = ctypes.c_char_p
+    lib.moe_quantize_fp8_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.c_int32, P, P, P]
+    lib.moe_quantize_fp8_blocks.restype = ctypes.c_int
     lib.moe_bias_update.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, P]
     lib.moe_bias_update.restype = ctypes.c_int
     lib.moe_strerror.argtypes = [ctypes.c_int]
@@ -113,7 +117,7 @@ def make_desc(T, d, n_routed, top_k, inner, n_shared=0, shared_inner=0, *,
         score={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score]
         if isinstance(score, str) else int(score),
         norm_topk=int(bool(norm_topk)), routed_scale=float(routed_scale),
-        dtype={"bf16": MOE_BF16, "f32": MOE_F32}[dtype]
+        dtype={"bf16": MOE_BF16, "f32": MOE_F32, "fp8": MOE_FP8}[dtype]
         if isinstance(dtype, str) else int(dtype))
 
 
@@ -164,12 +168,16 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
                       n_groups: int = 1, topk_groups: int = 1, select_bias=None,
                       logit_bias=None, routed_scale: float = 1.0,
                       return_routing: bool = False, out=None, workspace=None,
-                      stream=None, trace_events=None):
+                      stream=None, trace_events=None, expert_scales=None,
+                      shared_scales=None):
     """DeepSeekMoE layer forward on the GPU.
 
     x [T, d] (bf16 or fp32), W_gate [E, d] fp32, experts = (w1 [E, I, d],
     w3 [E, I, d], w2 [E, d, I]), shared = same with K_s experts or None,
-    K routed experts kept per token.  Returns out [T, d] (and, with
+    K routed experts kept per token.  FP8 layer: x bf16, the weights uint8
+    E4M3 codes and ``expert_scales`` / ``shared_scales`` = (s1 [E, I/128,
+    d/128], s3 same, s2 [E, d/128, I/128]) uint8 block scale bytes (see
+    ``quantize_fp8_blocks``).  Returns out [T, d] (and, with
     ``return_routing``, a dict with topk_idx [T, K] int32, topk_w [T, K] fp32
     and expert_counts [E] int32).  ``workspace`` (uint8, >= workspace_size)
     may be passed to reuse one buffer; ``trace_events`` (a list of n + 1 raw
@@ -186,22 +194,34 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
     w1, w3, w2 = experts
     E, I = w1.shape[0], w1.shape[1]
     Ks, Is = (shared[0].shape[0], shared[0].shape[1]) if shared is not None else (0, 0)
+    fp8 = expert_scales is not None
+    if fp8 and dt != torch.bfloat16:
+        raise ValueError("FP8 layers take bf16 x")
+    wdt = torch.uint8 if fp8 else dt
     _check_tensor("x", x, dt, (T, d), dev)
     _check_tensor("W_gate", W_gate, torch.float32, (E, d), dev)
-    _check_tensor("experts.w1", w1, dt, (E, I, d), dev)
-    _check_tensor("experts.w3", w3, dt, (E, I, d), dev)
-    _check_tensor("experts.w2", w2, dt, (E, d, I), dev)
+    _check_tensor("experts.w1", w1, wdt, (E, I, d), dev)
+    _check_tensor("experts.w3", w3, wdt, (E, I, d), dev)
+    _check_tensor("experts.w2", w2, wdt, (E, d, I), dev)
     if shared is not None:
-        _check_tensor("shared.w1", shared[0], dt, (Ks, Is, d), dev)
-        _check_tensor("shared.w3", shared[1], dt, (Ks, Is, d), dev)
-        _check_tensor("shared.w2", shared[2], dt, (Ks, d, Is), dev)
+        _check_tensor("shared.w1", shared[0], wdt, (Ks, Is, d), dev)
+        _check_tensor("shared.w3", shared[1], wdt, (Ks, Is, d), dev)
+        _check_tensor("shared.w2", shared[2], wdt, (Ks, d, Is), dev)
+    if fp8:
+        for name, sc, n, r, c in (("expert_scales", expert_scales, E, I, d),) + (
+                (("shared_scales", shared_scales, Ks, Is, d),) if shared is not None else ()):
+            if sc is None:
+                raise ValueError(f"{name} required for an FP8 layer")
+            _check_tensor(name + "[0]", sc[0], torch.uint8, (n, r // 128, c // 128), dev)
+            _check_tensor(name + "[1]", sc[1], torch.uint8, (n, r // 128, c // 128), dev)
+            _check_tensor(name + "[2]", sc[2], torch.uint8, (n, c // 128, r // 128), dev)
     for name, b in (("select_bias", select_bias), ("logit_bias", logit_bias)):
         if b is not None:
             _check_tensor(name, b, torch.float32, (E,), dev)
     desc = make_desc(T, d, E, K, I, Ks, Is, n_groups=n_groups,
                      topk_groups=topk_groups, score=score, norm_topk=norm_topk,
                      routed_scale=routed_scale,
-                     dtype="bf16" if dt == torch.bfloat16 else "f32")
+                     dtype="fp8" if fp8 else "bf16" if dt == torch.bfloat16 else "f32")
     st = lib.moe_layer_validate(ctypes.byref(desc))
     if st != MOE_OK:
         raise MoeError(st, strerror(st))
@@ -219,9 +239,12 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
         cnt = torch.empty((E,), dtype=torch.int32, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    ffn_r = FfnWeights(w1.data_ptr(), w3.data_ptr(), w2.data_ptr())
-    ffn_s = (FfnWeights(shared[0].data_ptr(), shared[1].data_ptr(), shared[2].data_ptr())
-             if shared is not None else FfnWeights(None, None, None))
+    sr = tuple(t.data_ptr() for t in expert_scales) if fp8 else (None, None, None)
+    ss = tuple(t.data_ptr() for t in shared_scales) if fp8 and shared is not None \
+        else (None, None, None)
+    ffn_r = FfnWeights(w1.data_ptr(), w3.data_ptr(), w2.data_ptr(), *sr)
+    ffn_s = (FfnWeights(shared[0].data_ptr(), shared[1].data_ptr(), shared[2].data_ptr(), *ss)
+             if shared is not None else FfnWeights(None, None, None, None, None, None))
     args = [ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias),
             _ptr(select_bias), ffn_r, ffn_s, _ptr(out), _ptr(idx), _ptr(wts),
             _ptr(cnt), workspace.data_ptr(), workspace.numel(), stream]
@@ -235,6 +258,28 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
     if return_routing:
         return out, {"topk_idx": idx, "topk_w": wts, "expert_counts": cnt}
     return out
+
+
+def quantize_fp8_blocks(w, stream=None):
+    """FP8 layer weight format: ``w`` [batch, rows, cols] (bf16 or fp32, GPU;
+    rows, cols multiples of 128) to (E4M3 codes uint8 [batch, rows, cols],
+    block scale bytes uint8 [batch, rows/128, cols/128])."""
+    import torch
+    lib = load_library()
+    if w.device.type != "cuda" or not w.is_contiguous() or w.dim() != 3:
+        raise ValueError("w must be a contiguous 3-d GPU tensor")
+    if w.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {w.dtype}")
+    B, R, C = w.shape
+    codes = torch.empty((B, R, C), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((B, R // 128, C // 128), dtype=torch.uint8, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    st = lib.moe_quantize_fp8_blocks(w.data_ptr(), MOE_BF16 if w.dtype == torch.bfloat16 else MOE_F32,
+                                     B, R, C, codes.data_ptr(), scales.data_ptr(), stream)
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return codes, scales
 
 
 def moe_bias_update(counts, gamma: float, select_bias=None, rel_load=None, stream=None):

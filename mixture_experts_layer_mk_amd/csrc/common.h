@@ -42,7 +42,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) {
 struct Layout {
   int64_t topk_idx, topk_w, rank, block_counts, block_base, counts, offsets,
       tiles, n_tiles, slot_row, row_src, xp, h_routed, h_shared, y, y_scale, s,
-      planes, plog, total;
+      planes, plog, x_q, x_scale, h_routed_scale, h_shared_scale, total;
   int32_t ds, ep;     // router: d-slices, logit row stride
   int32_t nblk;       // router workgroups (histogram blocks)
   int32_t bm;         // rows per GEMM M-tile
@@ -128,8 +128,27 @@ struct GemmArgs {
   const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
   int T;                          // rows for shared group
   int bm;
+  // FP8 layers (E4M3 operands, power-of-two scales stored as bytes b, value
+  // 2^(b - 127)): a_scale[row][k / 128] of the activation rows (rows of x for
+  // gathered tiles), weight scales per 128 x 128 block (s1, s3
+  // [E][inner / 128][d / 128], s2 [E][d / 128][inner / 128]), and GATEUP's
+  // output scales out_scale[row][col / 128].
+  const uint8_t* a_scale; int lda_s;
+  const uint8_t* s1; const uint8_t* s3; const uint8_t* s2;
+  uint8_t* out_scale; int ldo_s;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s);
+
+// E4M3 quantisation with power-of-two scales: rows of `src` [R][C] (bf16 or
+// f32) per 1 x 128 (quant_rows), or [batch][R][C] per 128 x 128 block.
+struct QuantArgs {
+  const void* src; int src_f32;
+  int64_t batch; int rows, cols;
+  uint8_t* codes; uint8_t* scales;
+};
+hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant_blocks(const QuantArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 struct CombineArgs {

@@ -1,0 +1,101 @@
+// Device helpers shared by the grouped expert GEMMs (bf16 and FP8): LDS
+// swizzle, XCD-aware tile order, SwiGLU, output packing, the fp16 routed-output
+// scales, instruction-scheduling groups and wait-count encodings.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace gemm {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+constexpr int BN = 256;   // weight rows per workgroup
+
+// XOR applied to the chunk index of LDS row `row` (8 chunks per row):
+// 8 consecutive rows, and 16 rows split by bank half, hit distinct banks.
+__device__ __forceinline__ int swz_x(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, j = b >> 3, q = n >> 3, r = n & 7;
+  return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v), evaluated as v * rcp(1 + 2^(-v log2 e))
+// with the hardware base-2 exponential and reciprocal (about 1 ulp each; the
+// result is rounded to bf16 right after).  Large |v| saturates correctly:
+// 2^+big = inf gives rcp = 0, 2^-big = 0 gives rcp(1) = 1.
+__device__ __forceinline__ float silu_f(float v) {
+  const float e = __builtin_amdgcn_exp2f(v * -1.4426950408889634f);
+  return v * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Two floats to packed fp16 (round to nearest even) and back.
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ float h_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float h_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Scale of one 64-column group of a routed output row whose largest
+// magnitude is amax: s = 2^(15 - E) with amax = f 2^E, f in [0.5, 1), so
+// every scaled value is below 2^15 (inside fp16's range), and inv = 1 / s.
+// Both are exact powers of two (E clamped so that both stay normal).
+__device__ __forceinline__ void y_scale_of(float amax, float& s, float& inv) {
+  int E = __builtin_amdgcn_frexp_expf(amax);
+  E = min(max(E, -111), 141);
+  s = __int_as_float((142 - E) << 23);
+  inv = __int_as_float((112 + E) << 23);
+}
+
+// Instruction-scheduling groups for one k-step: N_MMA matrix ops with the
+// N_DS LDS reads (of the next k-step) spread over the first half, so they
+// land well before use, and N_VM global->LDS loads spread over all of them.
+template <int N_MMA, int N_DS, int N_VM, int I = 0>
+__device__ __forceinline__ void sched_groups() {
+  if constexpr (I < N_MMA) {
+    constexpr int S = (N_MMA / 2 > 0) ? N_MMA / 2 : 1;
+    constexpr int ds = (I < S) ? (I + 1) * N_DS / S - I * N_DS / S : 0;
+    constexpr int vm = (I + 1) * N_VM / N_MMA - I * N_VM / N_MMA;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // matrix op
+    if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // LDS read
+    if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM
+    sched_groups<N_MMA, N_DS, N_VM, I + 1>();
+  }
+}
+
+constexpr int NGRP = 4;   // N-tiles per tile-order group
+
+// s_waitcnt immediate that waits until at most N vector-memory operations
+// are outstanding (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],
+// vmcnt[5:4] in bits [15:14]; the other counters left at their maximum).
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
+}
+
+// N-tiles of one GEMM stage (GATEUP: 128 inner columns per tile, for each
+// expert of the shared group; DOWN: 256 output columns per tile).
+template <int MODE, int BM>
+__host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
+  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
+  if (MODE == 0) return ((a.inner + BN / 2 - 1) / (BN / 2)) * (routed ? 1 : a.n_experts);
+  return (a.d + BN - 1) / BN;
+}
+
+}  // namespace gemm
+}  // namespace moe

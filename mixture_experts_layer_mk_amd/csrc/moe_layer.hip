@@ -20,12 +20,17 @@ const char* const kStageNames[kStages] = {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-int elem_size(const moe_layer_desc_t& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
+// Bytes per element of x / out (bf16 for bf16 and FP8 layers) and of the
+// SwiGLU activations H (one E4M3 byte for FP8 layers).
+int elem_size(const moe_layer_desc_t& d) { return d.dtype == MOE_F32 ? 4 : 2; }
+int h_elem_size(const moe_layer_desc_t& d) {
+  return d.dtype == MOE_FP8 ? 1 : d.dtype == MOE_BF16 ? 2 : 4;
+}
 
 // Rows per routed M-tile: large tiles when experts receive many rows, smaller
 // ones when the average expert group is short (weight-streaming regime).
 int choose_bm(const moe_layer_desc_t& d) {
-  if (d.dtype != MOE_BF16) return 64;
+  if (d.dtype == MOE_F32) return 64;
   const int64_t avg = (int64_t)d.T * d.top_k / d.n_routed;
   if (avg >= 192) return 256;
   if (avg >= 96) return 128;
@@ -44,11 +49,15 @@ moe_status_t validate(const moe_layer_desc_t* d) {
   if (d->score != MOE_SCORE_SOFTMAX && d->score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (d->norm_topk != 0 && d->norm_topk != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d->routed_scale)) return MOE_ERR_INVALID_ARG;
-  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8)
+    return MOE_ERR_INVALID_ARG;
   if (d->n_routed > MAX_EXPERTS || d->top_k > MAX_TOPK || d->n_groups > MAX_GROUPS)
     return MOE_ERR_UNSUPPORTED;
-  const int q = d->dtype == MOE_BF16 ? 64 : 4;
+  const int q = d->dtype == MOE_FP8 ? 128 : d->dtype == MOE_BF16 ? 64 : 4;
   if (d->d % q || d->inner % q || (d->n_shared > 0 && d->shared_inner % q))
+    return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_FP8 &&   // scale bytes of a tile are staged in LDS
+      (d->d > 8192 || d->inner > 8192 || (int64_t)d->n_shared * d->shared_inner > 8192))
     return MOE_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)d->T * d->top_k;
   const int64_t lim = int64_t(1) << 31;
@@ -84,20 +93,27 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.slot_row = take(TK * 4);
   L.row_src = take(TK * 4);
   L.xp = -1;   // routed gate/up tiles gather token rows from x directly
-  L.h_routed = take(TK * d.inner * esz);
-  L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * d.n_shared * d.shared_inner * esz) : -1;
+  const int64_t hsz = h_elem_size(d);
+  const bool fp8 = d.dtype == MOE_FP8;
+  const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
+  L.h_routed = take(TK * d.inner * hsz);
+  L.h_shared = d.n_shared > 0 ? take((int64_t)d.T * ksi * hsz) : -1;
+  L.h_routed_scale = fp8 ? take(TK * (d.inner / 128)) : -1;
+  L.h_shared_scale = (fp8 && d.n_shared > 0) ? take((int64_t)d.T * (ksi / 128)) : -1;
+  L.x_q = fp8 ? take((int64_t)d.T * d.d) : -1;
+  L.x_scale = fp8 ? take((int64_t)d.T * (d.d / 128)) : -1;
   // Routed expert outputs: fp32 for fp32 layers; for bf16 layers fp16 with a
   // power-of-two inverse scale per 64 columns of a row.
-  const bool bf16 = d.dtype == MOE_BF16;
+  const bool bf16 = d.dtype != MOE_F32;   // bf16 activations (bf16, FP8)
   L.y = take(TK * d.d * (bf16 ? 2 : 4));
   L.y_scale = bf16 ? take(TK * (d.d / Y_GROUP) * 4) : -1;
   // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
   // layers fuse the combine into the shared down-projection.
-  L.s = (d.n_shared > 0 && d.dtype != MOE_BF16) ? take((int64_t)d.T * d.d * 4) : -1;
-  L.ds = router_dsplit(d.T, d.n_routed, d.d, d.dtype == MOE_BF16 ? 1 : 0);
+  L.s = (d.n_shared > 0 && d.dtype == MOE_F32) ? take((int64_t)d.T * d.d * 4) : -1;
+  L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
-  L.planes = d.dtype == MOE_BF16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
-  L.plog = router_fused(d.n_routed, d.top_k, d.n_groups, d.dtype == MOE_BF16 ? 1 : 0)
+  L.planes = bf16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
+  L.plog = router_fused(d.n_routed, d.top_k, d.n_groups, bf16 ? 1 : 0)
                ? -1 : take((int64_t)L.ds * d.T * L.ep * 4);
   L.total = off;
   return L;
@@ -122,6 +138,9 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   const moe_layer_desc_t& d = *desc;
   if (!w_gate || !routed.w1 || !routed.w3 || !routed.w2) return MOE_ERR_INVALID_ARG;
   if (d.n_shared > 0 && (!shared.w1 || !shared.w3 || !shared.w2)) return MOE_ERR_INVALID_ARG;
+  if (d.dtype == MOE_FP8 && (!routed.s1 || !routed.s3 || !routed.s2 ||
+                             (d.n_shared > 0 && (!shared.s1 || !shared.s3 || !shared.s2))))
+    return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!x || !out)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream_ptr);
   auto mark = [&](int i) -> bool {
@@ -143,7 +162,8 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
   int32_t* idx = topk_idx ? topk_idx : static_cast<int32_t*>(at(L.topk_idx));
   float* gw = topk_w ? topk_w : static_cast<float*>(at(L.topk_w));
-  const bool bf16 = d.dtype == MOE_BF16;
+  const bool bf16 = d.dtype != MOE_F32;   // bf16 activations (bf16, FP8)
+  const bool fp8 = d.dtype == MOE_FP8;
   hipError_t err;
 #define MOE_CHECK(call)                      \
   do {                                       \
@@ -167,6 +187,13 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     r.rank = static_cast<int32_t*>(at(L.rank));
     r.block_counts = static_cast<int32_t*>(at(L.block_counts));
     MOE_CHECK(launch_router(r, s));
+    if (fp8) {   // the token rows in E4M3, per 1 x 128 of the hidden dimension
+      QuantArgs q{};
+      q.src = x; q.src_f32 = 0; q.batch = 1; q.rows = d.T; q.cols = d.d;
+      q.codes = static_cast<uint8_t*>(at(L.x_q));
+      q.scales = static_cast<uint8_t*>(at(L.x_scale));
+      MOE_CHECK(launch_quant_rows(q, s));
+    }
   }
   // 2. scan + tile schedule
   if (!mark(1)) return MOE_ERR_HIP;
@@ -198,8 +225,9 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     MOE_CHECK(launch_permute(p, s));
   }
   auto gemm = [&](const GemmArgs& g) {
-    return bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+    return fp8 ? launch_gemm_fp8(g, s) : bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
   };
+  const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
   GemmArgs base{};
   base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
   base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
@@ -211,6 +239,12 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.a_rows = static_cast<const int32_t*>(at(L.row_src));
     g.w1 = routed.w1; g.w3 = routed.w3; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.h_routed); g.ldo = d.inner;
+    if (fp8) {
+      g.a = at(L.x_q);
+      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
+      g.s1 = routed.s1; g.s3 = routed.s3;
+      g.out_scale = static_cast<uint8_t*>(at(L.h_routed_scale)); g.ldo_s = d.inner / 128;
+    }
     MOE_CHECK(gemm(g));
   }
   // 5. shared gate/up
@@ -220,6 +254,12 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
     g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
     g.out = at(L.h_shared); g.ldo = d.n_shared * d.shared_inner;
+    if (fp8) {
+      g.a = at(L.x_q);
+      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
+      g.s1 = shared.s1; g.s3 = shared.s3;
+      g.out_scale = static_cast<uint8_t*>(at(L.h_shared_scale)); g.ldo_s = (int)(ksi / 128);
+    }
     MOE_CHECK(gemm(g));
   }
   // 6. routed down
@@ -230,6 +270,10 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.w2 = routed.w2; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.y); g.ldo = d.d;
     g.yscale = bf16 ? static_cast<float*>(at(L.y_scale)) : nullptr;
+    if (fp8) {
+      g.a_scale = static_cast<const uint8_t*>(at(L.h_routed_scale)); g.lda_s = d.inner / 128;
+      g.s2 = routed.s2;
+    }
     MOE_CHECK(gemm(g));
   }
   // 7. shared down (+ residual); for bf16 layers the combine is fused here
@@ -240,6 +284,10 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;
     g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
     g.out = at(L.s); g.ldo = d.d;
+    if (fp8) {
+      g.a_scale = static_cast<const uint8_t*>(at(L.h_shared_scale)); g.lda_s = (int)(ksi / 128);
+      g.s2 = shared.s2;
+    }
     if (fused) {
       g.ybuf = at(L.y);
       g.yscale = static_cast<float*>(at(L.y_scale));
@@ -298,6 +346,10 @@ moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
   out->h_shared = L.h_shared;
   out->y = L.y;
   out->y_scale_f32 = L.y_scale;
+  out->x_q = L.x_q;
+  out->x_scale = L.x_scale;
+  out->h_routed_scale = L.h_routed_scale;
+  out->h_shared_scale = L.h_shared_scale;
   out->s_f32 = L.s;
   out->total_bytes = L.total;
   return MOE_OK;
@@ -332,6 +384,22 @@ moe_status_t moe_layer_forward_traced(
   return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
                       topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
                       stream, events);
+}
+
+moe_status_t moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t batch,
+                                     int32_t rows, int32_t cols, uint8_t* codes,
+                                     uint8_t* scales, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows % 128 || cols % 128) return MOE_ERR_UNSUPPORTED;
+  if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)rows * cols >= (int64_t(1) << 40) / batch) return MOE_ERR_UNSUPPORTED;
+  QuantArgs q{};
+  q.src = src; q.src_f32 = src_dtype == MOE_F32; q.batch = batch; q.rows = rows; q.cols = cols;
+  q.codes = codes; q.scales = scales;
+  if (launch_quant_blocks(q, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 moe_status_t moe_bias_update(const int32_t* counts, int32_t n_routed, float gamma,

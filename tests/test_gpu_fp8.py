@@ -1,0 +1,156 @@
+"""GPU parity of the FP8 layer (E4M3 expert GEMMs with power-of-two scales)
+against the oracle of the FP8 layer, and of the quantisers against the
+oracle's, bitwise.
+
+Sizes: the FP8 workloads at reduced T with full hidden/inner/expert shapes
+(several tiles, ragged tails), the full 16B-shaped layer on sampled tokens in
+the launch configuration the benchmark times, and the edge cases (no shared
+expert, the dense reduction, a weight block of zeros, large and tiny scales).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.fp8 as ofp8
+import workloads
+from parity import FP8_H_MARGIN, Case, check_case
+
+pytestmark = pytest.mark.gpu
+
+C = workloads.CONFIGS
+F8 = C["deepseekmoe-16b-fp8"]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_weight_quantiser_bitwise():
+    import mixture_experts_layer_mk_amd as moe
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((3, 256, 384)).astype(np.float32)
+    w[0, :128, :128] = 0.0                                  # a block of zeros
+    w[1, 128:, 256:] *= 2.0 ** 40                           # large scale
+    w[2, :128, 128:256] *= 2.0 ** -60                       # tiny scale
+    w[2, 5, 7] = -3e-20
+    for dt in (torch.float32, torch.bfloat16):
+        t = torch.from_numpy(w).to(dt)
+        codes, scales = moe.quantize_fp8_blocks(t.cuda())
+        torch.cuda.synchronize()
+        host = t.float().numpy()
+        for b in range(3):
+            oc, os_ = ofp8.quantize_blocks(host[b])
+            assert np.array_equal(codes[b].cpu().numpy(), oc), (dt, b)
+            assert np.array_equal(scales[b].cpu().numpy(), os_), (dt, b)
+
+
+REDUCED = {
+    "16b-fp8-T2600": F8.replace(T=2600),
+    "16b-fp8-T1000": F8.replace(T=1000, seed=1),
+    "2b-fp8-T2000": C["deepseekmoe-2b"].replace(T=2000, dtype="fp8"),
+    "v3-fp8-d512-T700": C["deepseek-v3"].replace(T=700, d=512, inner=256, shared_inner=256,
+                                                  seed=2, dtype="fp8"),
+    "skewed-fp8": C["skewed-16b-small"].replace(dtype="fp8"),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_fp8_reduced_all_tokens(name):
+    cfg = REDUCED[name]
+    say(f"[fp8] {name}: {cfg}")
+    info = check_case(Case(cfg))
+    say(f"[fp8] {name}: {info}")
+
+
+def test_fp8_token_rows_quantised_bitwise():
+    """The E4M3 token rows and their scales, read back from the workspace."""
+    from mixture_experts_layer_mk_amd import make_desc, workspace_layout, workspace_size
+    cfg = F8.replace(T=777, seed=3)
+    case = Case(cfg)
+    desc = make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner, cfg.n_shared,
+                     cfg.shared_inner, dtype="fp8")
+    lay = workspace_layout(desc)
+    ws = torch.empty(workspace_size(desc), dtype=torch.uint8, device="cuda")
+    case.run_gpu(workspace=ws)
+    torch.cuda.synchronize()
+    xq = ws[lay["x_q"]:lay["x_q"] + cfg.T * cfg.d].cpu().numpy().reshape(cfg.T, cfg.d)
+    G = cfg.d // 128
+    xs = ws[lay["x_scale"]:lay["x_scale"] + cfg.T * G].cpu().numpy().reshape(cfg.T, G)
+    oc, os_ = ofp8.quantize_1x128(case.x)
+    assert np.array_equal(xq, oc) and np.array_equal(xs, os_)
+    # the shared experts' SwiGLU activations [T][Ks * Is] with their 1x128
+    # scales, against the oracle's exact H: the GPU's dequantised value must
+    # lie within the spread re-quantisation allows when H moves by the
+    # margin (codes equal elsewhere)
+    ksi = cfg.n_shared * cfg.shared_inner
+    hq = ws[lay["h_shared"]:lay["h_shared"] + cfg.T * ksi].cpu().numpy().reshape(cfg.T, ksi)
+    hs = ws[lay["h_shared_scale"]:lay["h_shared_scale"] + cfg.T * ksi // 128].cpu().numpy()
+    hs = hs.reshape(cfg.T, ksi // 128)
+    xd = ofp8.dequantize_1x128(oc, os_)
+    (c1, s1), (c3, s3), _ = case.ora_q["shared"]
+    n_codes = n_scales = 0
+    for si in range(cfg.n_shared):
+        W1 = ofp8.dequantize_blocks(c1[si], s1[si])
+        W3 = ofp8.dequantize_blocks(c3[si], s3[si])
+        h = oracle.silu(xd @ W1.T) * (xd @ W3.T)
+        hc, hsc = ofp8.quantize_1x128(h)
+        spread = ofp8.requantisation_spread(h, FP8_H_MARGIN)
+        cols = slice(si * cfg.shared_inner, (si + 1) * cfg.shared_inner)
+        gcols = slice(si * cfg.shared_inner // 128, (si + 1) * cfg.shared_inner // 128)
+        g_c, g_s = hq[:, cols], hs[:, gcols]
+        n_codes += int((g_c != hc).sum())
+        n_scales += int((g_s != hsc).sum())
+        dev = np.abs(ofp8.dequantize_1x128(g_c, g_s) - ofp8.dequantize_1x128(hc, hsc))
+        bad = dev > spread
+        assert not bad.any(), (f"shared {si}: {bad.sum()} activations outside the spread, "
+                               f"e.g. {np.argwhere(bad)[0]}")
+        assert n_codes <= 1e-2 * hc.size * (si + 1)          # differences stay rare
+    say(f"[fp8] shared H: {n_codes} of {cfg.T * ksi} codes and {n_scales} scales differ")
+
+
+@pytest.mark.parametrize("Ks", [0, 1])
+def test_fp8_no_shared_and_dense(Ks):
+    if Ks == 0:
+        cfg = F8.replace(T=333, n_routed=8, top_k=8, n_shared=0, d=256, inner=128)
+    else:
+        cfg = F8.replace(T=500, n_routed=1, top_k=1, n_shared=0, d=512, inner=384)
+    info = check_case(Case(cfg))
+    say(f"[fp8] Ks={Ks}: {info}")
+
+
+def test_fp8_full_size_sampled():
+    say("[fp8-full] generating")
+    case = Case(F8)
+    say("[fp8-full] running")
+    rows = np.sort(np.random.default_rng(7).choice(F8.T, 256, replace=False))
+    rows[0], rows[-1] = 0, F8.T - 1
+    info = check_case(case, rows=rows)
+    say(f"[fp8-full] {info}")
+
+
+def test_fp8_error_against_bf16_layer():
+    """What FP8 costs: the FP8 layer against the bf16-exact oracle of the same
+    layer (informational bound: quantisation-sized, a few percent of the
+    expert contribution)."""
+    cfg = F8.replace(T=512, seed=9)
+    case = Case(cfg)
+    out, routing = case.run_gpu()
+    torch.cuda.synchronize()
+    rows = np.arange(cfg.T)
+    idx = routing["topk_idx"].cpu().numpy()
+    y, _ = oracle.moe_forward(case.x, case.w_gate, case.routed, case.shared, cfg.top_k,
+                              forced_idx=idx, **case.oracle_kw())
+    g = out.float().cpu().numpy()
+    rel = np.sqrt(np.mean((g - y) ** 2)) / np.sqrt(np.mean((y - case.x) ** 2))
+    say(f"[fp8] rms error vs bf16-exact layer, relative to the expert contribution: {rel:.4f}")
+    assert rel < 0.1

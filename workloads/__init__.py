@@ -67,7 +67,8 @@ class LayerConfig:
     topk_groups: int = 1     # groups kept per token
     select_bias_range: float = 0.0   # U(-r, r) selection-only bias (0 = none)
     zipf_s: float = 0.0      # Zipf exponent of the logit log-bias (0 = none)
-    dtype: str = "bf16"      # "bf16" | "f32": x, out and expert weights
+    dtype: str = "bf16"      # "bf16" | "f32": x, out and expert weights; "fp8":
+                             # generated as bf16 (the FP8 layer quantises them)
     routed_scale: float = 1.0
     seed: int = 0
 
@@ -104,6 +105,11 @@ CONFIGS = {
                                shared_inner=2048, score="sigmoid",
                                norm_topk=True, n_groups=8, topk_groups=4,
                                select_bias_range=0.1),
+    # The 16B-shaped layer with FP8 expert GEMMs (the same generated values;
+    # the layer quantises the weights and activations to E4M3).
+    "deepseekmoe-16b-fp8": LayerConfig("deepseekmoe-16b-fp8", T=16384, d=2048,
+                                       n_routed=64, inner=1408, top_k=6, n_shared=2,
+                                       shared_inner=1408, dtype="fp8"),
     # Skewed small batch on the 16B shapes: Zipf(1.2) logit log-bias.
     "skewed-16b-small": LayerConfig("skewed-16b-small", T=128, d=2048,
                                     n_routed=64, inner=1408, top_k=6,
@@ -143,7 +149,7 @@ class Inputs:
         return np.random.default_rng([self.seed, *words])
 
     def _act(self, a: np.ndarray) -> np.ndarray:
-        return _round_bf16(a) if self.cfg.dtype == "bf16" else a
+        return _round_bf16(a) if self.cfg.dtype in ("bf16", "fp8") else a
 
     # -- token hidden states --------------------------------------------
     def x_rows(self, rows) -> np.ndarray:
@@ -215,7 +221,7 @@ class Inputs:
         """
         import torch
         cfg = self.cfg
-        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        tdt = torch.bfloat16 if cfg.dtype in ("bf16", "fp8") else torch.float32
 
         def stack(get, n, inner):
             w1 = torch.empty((n, inner, cfg.d), dtype=tdt)
