@@ -8,7 +8,9 @@ fp32 router, seeded synthetic inputs resident in HBM before timing starts.
 Prints one JSON line with tokens/s, activated TFLOP/s and the fraction of
 the bf16 matrix peak, per-stage times from HIP events recorded on the
 layer's stream during the timed steps, a roofline entry for the dominant
-kernel, and the CPU oracle timed on a bounded token sample.
+kernel, the FP8 variant of the same layer (E4M3 expert GEMMs, its own
+stage times and roofline against the fp8 matrix peak), and the CPU oracle
+timed on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -26,40 +28,51 @@ METRIC = ("MoE layer fwd tokens/s + activated TFLOP/s (% bf16 MFMA peak), "
           "16B-shape, 1 GPU")
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (TFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (GB/s)
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 matrix peak (TFLOP/s)
 DOMINANT = "gemm_gateup_routed"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_routed.json")
+# The dominant kernel of each variant: (name prefix in a trace, sources,
+# committed traffic summary).
+GATEUP = {
+    "bf16": ("gemm_bf16_kernel<0", ("common.h", "gemm_common.h", "gemm_bf16.hip"),
+             os.path.join(ROOT, "profiles", "traffic_gemm_gateup_routed.json")),
+    "fp8": ("gemm_fp8_kernel<0", ("common.h", "gemm_common.h", "gemm_fp8.hip"),
+            os.path.join(ROOT, "profiles", "traffic_gemm_fp8_gateup_routed.json")),
+}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    """Hash of the dominant kernel's sources (its file and the shared header)."""
+def source_hash(kind: str = "bf16") -> str:
+    """Hash of a dominant kernel's sources (its file and the headers it uses)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_layer_mk_amd", "csrc")
-    for f in ("common.h", "gemm_bf16.hip"):
+    for f in GATEUP[kind][1]:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on other sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kind: str = "bf16"):
+    """HBM bytes per launch of a dominant kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on other sources."""
+    path = GATEUP[kind][2]
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
+    if t.get("source_hash") != source_hash(kind):
         return None
     return t.get("bytes_per_launch")
 
 
 def summarize_traffic(fetch_csv, write_csv, copy_mb):
-    """Write the traffic summary of the dominant kernel from two rocprofv3
-    --pmc counter files (FETCH_SIZE run, WRITE_SIZE run, both of a bench run
-    with --copy-calibration-mb copy_mb).  Each counter is scaled by what it
-    reads for the plain device copy of copy_mb MiB."""
+    """Write the traffic summaries of the dominant kernels (routed gate/up
+    launch of the bf16 and of the FP8 variant) from two rocprofv3 --pmc
+    counter files (FETCH_SIZE run, WRITE_SIZE run, both of a bench run with
+    --copy-calibration-mb copy_mb).  Each counter is scaled by what it reads
+    for the plain device copy of copy_mb MiB; of the launches of a kernel the
+    one with the largest grid is the routed gate/up launch."""
     import csv
     import collections
 
@@ -70,24 +83,30 @@ def summarize_traffic(fetch_csv, write_csv, copy_mb):
                 acc[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
-    out = {"source_hash": source_hash(), "kernel": DOMINANT, "copy_calibration_mib": copy_mb}
-    for name, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
-                                ("write", write_csv, "WRITE_SIZE")):
-        vals = per_kernel(path, counter)
-        copy = [v for (k, g), v in vals.items() if "copyBuffer" in k]
-        gemm = [(g, v) for (k, g), v in vals.items() if "gemm_bf16_kernel<0" in k]
-        if not copy or not gemm:
-            raise SystemExit(f"{path}: copy or gate/up kernel missing")
-        scale = (copy_mb * 1024.0) / max(copy)            # KiB per counter KiB
-        g, v = max(gemm)                                   # routed launch: larger grid
-        out[f"{name}_kib_raw"] = v
-        out[f"{name}_scale"] = scale
-        out[f"{name}_bytes"] = v * scale * 1024.0
-    out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out))
+    vals = {"fetch": per_kernel(fetch_csv, "FETCH_SIZE"),
+            "write": per_kernel(write_csv, "WRITE_SIZE")}
+    for kind, (prefix, _, path) in GATEUP.items():
+        out = {"source_hash": source_hash(kind), "kernel": prefix + ">, routed gate/up launch",
+               "copy_calibration_mib": copy_mb}
+        for name in ("fetch", "write"):
+            v_all = vals[name]
+            copy = [v for (k, g), v in v_all.items() if "copyBuffer" in k]
+            gemm = [(g, v) for (k, g), v in v_all.items() if prefix in k]
+            if not copy or not gemm:
+                print(f"{kind}: copy or gate/up kernel missing in the {name} counters",
+                      file=sys.stderr)
+                break
+            scale = (copy_mb * 1024.0) / max(copy)            # KiB per counter KiB
+            g, v = max(gemm)
+            out[f"{name}_kib_raw"] = v
+            out[f"{name}_scale"] = scale
+            out[f"{name}_bytes"] = v * scale * 1024.0
+        else:
+            out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
+            os.makedirs(os.path.dirname(path), exist_ok=True)
+            with open(path, "w") as f:
+                json.dump(out, f, indent=1)
+            print(json.dumps(out))
 
 
 def cpu_baseline(cfg, host, n_tokens, reps):
@@ -112,6 +131,65 @@ def cpu_baseline(cfg, host, n_tokens, reps):
                       f"(numpy fp64 oracle, BLAS threads={cores})"}
 
 
+def time_fp8(moe, cfg, d, steps, warmup, fpt):
+    """The FP8 variant of the same layer (E4M3 expert GEMMs with power-of-two
+    block scales): weights quantised once beforehand (the layer's weight
+    format), then ``steps`` timed forwards, stage times from HIP events."""
+    import torch
+    q = {k: [moe.quantize_fp8_blocks(w) for w in d[k]] for k in ("routed", "shared")}
+    codes = {k: tuple(c for c, _ in v) for k, v in q.items()}
+    scales = {k: tuple(s for _, s in v) for k, v in q.items()}
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner,
+                         cfg.n_shared, cfg.shared_inner, n_groups=cfg.n_groups,
+                         topk_groups=cfg.topk_groups, score=cfg.score,
+                         norm_topk=cfg.norm_topk, routed_scale=cfg.routed_scale,
+                         dtype="fp8")
+    ws = torch.empty(moe.workspace_size(desc), dtype=torch.uint8, device=d["x"].device)
+    out = torch.empty_like(d["x"])
+    names = moe.trace_stage_names()
+    nst = len(names)
+    events = [moe.HipEvents(nst + 1) for _ in range(steps)]
+
+    def step(ev=None):
+        moe.moe_layer_forward(d["x"], d["w_gate"], codes["routed"], codes["shared"], cfg.top_k,
+                              score=cfg.score, norm_topk=cfg.norm_topk,
+                              n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                              select_bias=d["select_bias"], logit_bias=d["logit_bias"],
+                              routed_scale=cfg.routed_scale, out=out, workspace=ws,
+                              expert_scales=scales["routed"], shared_scales=scales["shared"],
+                              trace_events=None if ev is None else ev.handles)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {n: sum(ev.elapsed_ms(i, i + 1) for ev in events) / steps
+                for i, n in enumerate(names)}
+    for ev in events:
+        ev.close()
+    tflops = fpt * cfg.T / (ms / 1e3) / 1e12
+    dom_flops = 2.0 * cfg.T * cfg.top_k * cfg.d * 2 * cfg.inner
+    dom_ms = stage_ms[DOMINANT]
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    return {
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+        "activated_tflops": round(tflops, 1),
+        "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": {"kernel": "gemm_fp8_kernel<GATEUP> (routed launch)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic("fp8"), "flops_per_launch": dom_flops,
+                     "avg_launch_ms": round(dom_ms, 4)},
+        "recipe": "E4M3 codes; token rows and SwiGLU activations per 1x128, weights per "
+                  "128x128 block, power-of-two scales; fp32 accumulation across instructions",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +200,8 @@ def main():
                     help="oracle sample size (0: all tokens of the workload)")
     ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 (E4M3) variant of the same workload")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for "
                          "scaling HBM byte counters)")
@@ -200,7 +280,7 @@ def main():
     roofline = {"kernel": "gemm_bf16_kernel<GATEUP> (routed launch)", "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(),
+                "traffic": measured_traffic("bf16"),
                 "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)}
 
     if args.copy_calibration_mb:
@@ -247,6 +327,11 @@ def main():
     attain = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 10 / 1e3) / 1e12
     del a8, b8
 
+    fp8 = None
+    if not args.no_fp8 and cfg.dtype == "bf16":
+        log(f"[bench] fp8 variant: {args.steps} steps")
+        fp8 = time_fp8(moe, cfg, d, args.steps, args.warmup, fpt)
+
     cpu = None
     if not args.no_cpu_baseline:
         n = min(args.cpu_tokens or cfg.T, cfg.T)
@@ -271,6 +356,7 @@ def main():
         "bias_update": {"us_per_call": round(bias_us, 2), "max_relative_load": round(max_rel_load, 4)},
         "attainable_bf16_tflops": {"value": round(attain, 1),
                                    "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
+        "fp8": fp8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
