@@ -131,6 +131,36 @@ def cpu_baseline(cfg, host, n_tokens, reps):
                       f"(numpy fp64 oracle, BLAS threads={cores})"}
 
 
+def per_call_ms(step, reps, cold_cache, dev):
+    """Each of ``reps`` calls timed alone between two events on the current
+    stream; with ``cold_cache`` a 1 GiB buffer is overwritten (untimed) before
+    every call, evicting the weights from L2 and the 256 MB MALL."""
+    import torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if cold_cache else None
+    out = []
+    for _ in range(reps):
+        if scratch is not None:
+            scratch.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def layer_hbm_bytes(cfg, counts):
+    """Algorithmic HBM bytes of one forward: the weights of every routed expert
+    that receives a token and of the shared experts, x read, out written and
+    the fp32 gate read."""
+    b = 2
+    nonempty = int((counts > 0).sum())
+    w = 3 * cfg.d * (nonempty * cfg.inner + cfg.n_shared * cfg.shared_inner) * b
+    return w + 2 * cfg.T * cfg.d * b + cfg.n_routed * cfg.d * 4, nonempty
+
+
 def time_fp8(moe, cfg, d, steps, warmup, fpt):
     """The FP8 variant of the same layer (E4M3 expert GEMMs with power-of-two
     block scales): weights quantised once beforehand (the layer's weight
@@ -200,6 +230,11 @@ def main():
                     help="oracle sample size (0: all tokens of the workload)")
     ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="weight-streaming report: overwrite a 1 GiB buffer before "
+                         "each timed call so that no weights stay in L2 / MALL")
+    ap.add_argument("--reps", type=int, default=50,
+                    help="calls timed one by one for the per-call statistics")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3) variant of the same workload")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -312,6 +347,32 @@ def main():
     bias_us = e0.elapsed_time(e1) / 50 * 1e3
     max_rel_load = float(rel.max())
 
+    # Per-call statistics and the whole layer against the HBM roofline: the
+    # weights of the experts that receive tokens, x and out.  Layers with few
+    # rows per expert stream their weights, and that is their roofline.
+    import numpy as np
+    counts = rt["expert_counts"].cpu().numpy()
+    hbm_bytes, nonempty = layer_hbm_bytes(cfg, counts)
+    log(f"[bench] {args.reps} calls timed one by one (cold cache: {args.cold_cache})")
+    calls = per_call_ms(step, args.reps, args.cold_cache, dev)
+    med = float(np.median(calls))
+    p10, p90 = (float(v) for v in np.percentile(calls, [10, 90]))
+    per_call = {"median_ms": round(med, 4), "p10_ms": round(p10, 4), "p90_ms": round(p90, 4),
+                "reps": args.reps, "cold_cache": bool(args.cold_cache)}
+    layer_gbs = hbm_bytes / (med / 1e3) / 1e9
+    layer_hbm = {"bytes": hbm_bytes, "nonempty_experts": nonempty,
+                 "achieved_gbs": round(layer_gbs, 1), "peak_gbs": PEAK_HBM_GBS,
+                 "frac": round(layer_gbs / PEAK_HBM_GBS, 4)}
+    streaming = cfg.T * cfg.top_k / cfg.n_routed < 512
+    if streaming:
+        roofline = {"kernel": "whole layer forward (weight streaming)", "bound": "hbm",
+                    "achieved": round(layer_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(layer_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "bytes_per_launch": hbm_bytes, "avg_launch_ms": round(med, 4)}
+        ms = med
+        tok_s = cfg.T / (ms / 1e3)
+        act_tflops = fpt * cfg.T / (ms / 1e3) / 1e12
+
     # Attainable bf16 matrix rate on this GPU: the vendor GEMM (torch.matmul,
     # hipBLASLt) on a square 8192^3 problem, timed with events.
     a8 = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
@@ -328,13 +389,13 @@ def main():
     del a8, b8
 
     fp8 = None
-    if not args.no_fp8 and cfg.dtype == "bf16":
+    if not args.no_fp8 and cfg.dtype == "bf16" and not args.cold_cache:
         log(f"[bench] fp8 variant: {args.steps} steps")
         fp8 = time_fp8(moe, cfg, d, args.steps, args.warmup, fpt)
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = min(args.cpu_tokens or cfg.T, cfg.T)
+        n = min(args.cpu_tokens or (min(cfg.T, 512) if streaming else cfg.T), cfg.T)
         log(f"[bench] cpu baseline: {args.cpu_reps} x {n} tokens")
         cpu = cpu_baseline(cfg, host, n, args.cpu_reps)
 
@@ -345,7 +406,12 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": (f"{cfg.name} MoE layer: T={cfg.T}, d={cfg.d}, "
                                 f"{cfg.n_routed} routed (inner {cfg.inner}, top-{cfg.top_k}, "
-                                f"{cfg.score}) + {cfg.n_shared} shared (inner {cfg.shared_inner})"),
+                                f"{cfg.score}"
+                                + (f", {cfg.n_groups} groups keep {cfg.topk_groups}, selection bias"
+                                   if cfg.n_groups > 1 else "")
+                                + (f", Zipf({cfg.zipf_s}) logit bias" if cfg.zipf_s else "")
+                                + f") + {cfg.n_shared} shared (inner {cfg.shared_inner})"
+                                + (", cold cache" if args.cold_cache else "")),
                    "tokens": cfg.T, "parallelism": "single-gpu"},
         "activated_tflops": round(act_tflops, 1),
         "frac_bf16_peak": round(act_tflops / PEAK_BF16_TFLOPS, 4),
@@ -353,6 +419,8 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "events_ms_per_step": round(total_ev, 4),
         "roofline": roofline,
+        "per_call": per_call,
+        "layer_hbm": layer_hbm,
         "bias_update": {"us_per_call": round(bias_us, 2), "max_relative_load": round(max_rel_load, 4)},
         "attainable_bf16_tflops": {"value": round(attain, 1),
                                    "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
