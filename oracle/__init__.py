@@ -9,10 +9,13 @@ from .moe_oracle import (Dispatch, Routing, activated_macs_per_token, bias_updat
                          expert_flops_per_token, gate_logits, gate_scores,
                          group_scores, moe_forward, moe_forward_bruteforce,
                          route, select_experts, silu, swiglu_ffn)
+from .moe_backward import (Grads, dsilu, exact_scores, expert_backward, moe_backward,
+                           moe_forward_exact)
 
 __all__ = [
     "Dispatch", "Routing", "activated_macs_per_token", "bias_update", "dispatch",
     "expert_flops_per_token", "gate_logits", "gate_scores", "group_scores",
     "moe_forward", "moe_forward_bruteforce", "route", "select_experts", "silu",
-    "swiglu_ffn",
+    "swiglu_ffn", "Grads", "dsilu", "exact_scores", "expert_backward", "moe_backward",
+    "moe_forward_exact",
 ]
