@@ -98,6 +98,15 @@ typedef struct {
   const uint8_t* s2;
 } moe_ffn_weights_t;
 
+/* Weight gradients of a group of experts (backward pass), fp32, written (not
+ * accumulated): dw1, dw3 [E][inner][d] and dw2 [E][d][inner], the layout of
+ * the weights. */
+typedef struct {
+  float* dw1;
+  float* dw3;
+  float* dw2;
+} moe_ffn_grads_t;
+
 /* Byte offsets of the intermediate buffers inside the workspace, for
  * inspection after a forward call has completed (-1 = not materialised).
  * Element types: *_i32 int32, *_f32 float, y as stated below, others
@@ -189,6 +198,39 @@ moe_status_t moe_layer_forward_traced(
     int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
     size_t workspace_bytes, void* stream, void* const* events,
     int32_t n_events);
+
+/* Backward pass of a bf16 layer.  The pages train these layers (DeepSeek-V3
+ * Technical Report summary, "3.2.1 DualPipe": the chunks' backward for
+ * inputs and backward for weights) and print no formula for it: this is the
+ * gradient of the layer's forward function (moe_layer_forward with the same
+ * desc and inputs) with the expert choice held fixed -- the top-K choice is
+ * piecewise constant, and the selection bias is set by the load rule, not by
+ * gradients.  For L = sum(dout * out):
+ *   dx          [T][d] bf16: dL/dx (residual, shared and routed experts, and
+ *               the gate through the scores)
+ *   dw_gate     [n_routed][d] fp32: dL/dW_gate
+ *   dlogit_bias [n_routed] fp32 or NULL: dL/d logit_bias
+ *   d_routed, d_shared: the experts' weight gradients (moe_ffn_grads_t;
+ *               d_shared ignored when n_shared = 0); experts that receive no
+ *               token get zeros
+ *   topk_idx    [T][top_k] int32 or NULL: receives the expert choice used
+ *               (recomputed from the inputs; the forward's own choice, as the
+ *               router is deterministic)
+ * x, w_gate, logit_bias, select_bias, routed, shared: as in the forward;
+ * dout [T][d] bf16.  Every product accumulates in fp32; the SwiGLU
+ * pre-activations are recomputed rather than stored.  dx must not overlap x
+ * or dout (MOE_ERR_ALIAS).  dtype must be MOE_BF16 (MOE_ERR_UNSUPPORTED
+ * otherwise).  The workspace (moe_layer_backward_workspace_size bytes,
+ * 256-byte aligned) is the caller's; nothing is allocated.  Asynchronous on
+ * `stream`; bitwise reproducible. */
+moe_status_t moe_layer_backward_workspace_size(const moe_layer_desc_t* desc, size_t* bytes);
+moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, const void* x,
+                                const float* w_gate, const float* logit_bias,
+                                const float* select_bias, moe_ffn_weights_t routed,
+                                moe_ffn_weights_t shared, const void* dout, void* dx,
+                                float* dw_gate, float* dlogit_bias, moe_ffn_grads_t d_routed,
+                                moe_ffn_grads_t d_shared, int32_t* topk_idx, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Weights to the FP8 layer's format: `src` [batch][rows][cols] (src_dtype
  * MOE_F32 or MOE_BF16, device) to E4M3 `codes` (same shape, one byte each)

@@ -42,6 +42,11 @@ class FfnWeights(ctypes.Structure):
                 ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
 
 
+class FfnGrads(ctypes.Structure):
+    """moe_ffn_grads_t: fp32 weight gradients of a group of experts."""
+    _fields_ = [("dw1", ctypes.c_void_p), ("dw3", ctypes.c_void_p), ("dw2", ctypes.c_void_p)]
+
+
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "topk_idx_i32", "topk_w_f32", "counts_i32", "offsets_i32",
@@ -84,6 +89,11 @@ def load_library():
     lib.moe_layer_trace_stage_count.restype = ctypes.c_int32
     lib.moe_layer_trace_stage_name.argtypes = [ctypes.c_int32]
     lib.moe_layer_trace_stage_name.restype = ctypes.c_char_p
+    lib.moe_layer_backward_workspace_size.argtypes = [D, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_layer_backward_workspace_size.restype = ctypes.c_int
+    lib.moe_layer_backward.argtypes = [D, P, P, P, P, FfnWeights, FfnWeights, P, P, P, P,
+                                       FfnGrads, FfnGrads, P, P, ctypes.c_size_t, P]
+    lib.moe_layer_backward.restype = ctypes.c_int
     lib.moe_quantize_fp8_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_int32, P, P, P]
     lib.moe_quantize_fp8_blocks.restype = ctypes.c_int
@@ -100,7 +110,7 @@ def header_functions() -> list:
     import re
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def strerror(status: int) -> str:
@@ -161,6 +171,104 @@ def _check_tensor(name, t, dtype, shape, device):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def backward_workspace_size(desc: MoeLayerDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().moe_layer_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return n.value
+
+
+def moe_layer_backward(x, W_gate, experts: Sequence, shared: Optional[Sequence], K: int,
+                       dout, *, score: str = "softmax", norm_topk: bool = False,
+                       n_groups: int = 1, topk_groups: int = 1, select_bias=None,
+                       logit_bias=None, routed_scale: float = 1.0, workspace=None,
+                       stream=None, grads=None):
+    """Backward pass of the bf16 layer (``moe_layer_backward`` in the C ABI):
+    gradients of sum(dout * out) for the forward on the same inputs, the
+    expert choice held fixed.  Returns a dict: dx [T, d] bf16, dw_gate [E, d],
+    dlogit_bias [E] (or None without a logit bias), routed = (dw1, dw3, dw2),
+    shared = same or None (fp32), topk_idx [T, K] int32.  ``grads`` (a dict of
+    that form) may be passed to write into existing tensors."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    if dev.type != "cuda" or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bf16 GPU tensor")
+    T, d = x.shape
+    w1, w3, w2 = experts
+    E, I = w1.shape[0], w1.shape[1]
+    Ks, Is = (shared[0].shape[0], shared[0].shape[1]) if shared is not None else (0, 0)
+    bf = torch.bfloat16
+    _check_tensor("x", x, bf, (T, d), dev)
+    _check_tensor("dout", dout, bf, (T, d), dev)
+    _check_tensor("W_gate", W_gate, torch.float32, (E, d), dev)
+    _check_tensor("experts.w1", w1, bf, (E, I, d), dev)
+    _check_tensor("experts.w3", w3, bf, (E, I, d), dev)
+    _check_tensor("experts.w2", w2, bf, (E, d, I), dev)
+    if shared is not None:
+        _check_tensor("shared.w1", shared[0], bf, (Ks, Is, d), dev)
+        _check_tensor("shared.w3", shared[1], bf, (Ks, Is, d), dev)
+        _check_tensor("shared.w2", shared[2], bf, (Ks, d, Is), dev)
+    for name, b in (("select_bias", select_bias), ("logit_bias", logit_bias)):
+        if b is not None:
+            _check_tensor(name, b, torch.float32, (E,), dev)
+    desc = make_desc(T, d, E, K, I, Ks, Is, n_groups=n_groups, topk_groups=topk_groups,
+                     score=score, norm_topk=norm_topk, routed_scale=routed_scale,
+                     dtype="bf16")
+    st = lib.moe_layer_validate(ctypes.byref(desc))
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    f32 = torch.float32
+    if grads is None:
+        grads = {
+            "dx": torch.empty_like(x),
+            "dw_gate": torch.empty((E, d), dtype=f32, device=dev),
+            "dlogit_bias": torch.empty((E,), dtype=f32, device=dev) if logit_bias is not None
+            else None,
+            "routed": (torch.empty((E, I, d), dtype=f32, device=dev),
+                       torch.empty((E, I, d), dtype=f32, device=dev),
+                       torch.empty((E, d, I), dtype=f32, device=dev)),
+            "shared": ((torch.empty((Ks, Is, d), dtype=f32, device=dev),
+                        torch.empty((Ks, Is, d), dtype=f32, device=dev),
+                        torch.empty((Ks, d, Is), dtype=f32, device=dev))
+                       if shared is not None else None),
+            "topk_idx": torch.empty((T, K), dtype=torch.int32, device=dev),
+        }
+    _check_tensor("dx", grads["dx"], bf, (T, d), dev)
+    _check_tensor("dw_gate", grads["dw_gate"], f32, (E, d), dev)
+    nbytes = backward_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ffn_r = FfnWeights(w1.data_ptr(), w3.data_ptr(), w2.data_ptr(), None, None, None)
+    ffn_s = (FfnWeights(shared[0].data_ptr(), shared[1].data_ptr(), shared[2].data_ptr(),
+                        None, None, None)
+             if shared is not None else FfnWeights(None, None, None, None, None, None))
+    gr = grads["routed"]
+    for name, t, shp in (("dw1", gr[0], (E, I, d)), ("dw3", gr[1], (E, I, d)),
+                         ("dw2", gr[2], (E, d, I))):
+        _check_tensor("routed." + name, t, f32, shp, dev)
+    g_r = FfnGrads(gr[0].data_ptr(), gr[1].data_ptr(), gr[2].data_ptr())
+    if shared is not None:
+        gs = grads["shared"]
+        for name, t, shp in (("dw1", gs[0], (Ks, Is, d)), ("dw3", gs[1], (Ks, Is, d)),
+                             ("dw2", gs[2], (Ks, d, Is))):
+            _check_tensor("shared." + name, t, f32, shp, dev)
+        g_s = FfnGrads(gs[0].data_ptr(), gs[1].data_ptr(), gs[2].data_ptr())
+    else:
+        g_s = FfnGrads(None, None, None)
+    st = lib.moe_layer_backward(
+        ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias), _ptr(select_bias),
+        ffn_r, ffn_s, _ptr(dout), _ptr(grads["dx"]), _ptr(grads["dw_gate"]),
+        _ptr(grads["dlogit_bias"]), g_r, g_s, _ptr(grads.get("topk_idx")),
+        workspace.data_ptr(), workspace.numel(), stream)
+    if st != MOE_OK:
+        raise MoeError(st, strerror(st))
+    return grads
 
 
 def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],

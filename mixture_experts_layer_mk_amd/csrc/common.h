@@ -84,6 +84,8 @@ struct SelectArgs {
   int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+// Partial logits only (bf16 x: the gate planes must already be split).
+hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
 int router_tokens_per_block(int T);   // tokens per histogram block
 int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 // True when logits and selection run fused (no partial-logit buffer).
@@ -108,7 +110,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 //  DOWN   : Y[r][n] = H W2^T                     routed rows (fp32 out)
 //  DOWN_SHARED : S[t][n] = x[t][n] + sum_s H_s W2_s^T   (fp32)
 struct GemmArgs {
-  int mode;           // 0 GATEUP, 1 DOWN, 2 DOWN_SHARED
+  int mode;           // 0 GATEUP, 1 DOWN, 2 DOWN_SHARED, 3 GATEUP_BWD
   bool shared;        // GATEUP: the shared-expert group (rows = tokens)
   const void* a; int lda;        // activation rows
   const int32_t* a_rows;         // optional: source row of each tile row
@@ -136,8 +138,76 @@ struct GemmArgs {
   const uint8_t* a_scale; int lda_s;
   const uint8_t* s1; const uint8_t* s3; const uint8_t* s2;
   uint8_t* out_scale; int ldo_s;
+  // GATEUP_BWD (bf16): the gate/up pre-activations a1, a3 are recomputed
+  // and the SwiGLU backward applied in the epilogue, from gin[row][col]
+  // (fp32, = dy W2 of the row, before the gate weight) and the row's gate
+  // weight row_g[row] (NULL: 1, the shared experts):
+  //   out[row][col] = g h  (bf16),  da[row][col] = g gin a3 silu'(a1),
+  //   da[row][col + inner] = g gin silu(a1)  (bf16, per expert of the group
+  //   at 2 inner columns per expert), dg_part[row][tile] = sum gin h over
+  //   the tile's inner columns (fp32, routed rows only).
+  const float* gin; int ldgin;
+  const float* row_g;
+  bf16_t* da; int ldda;
+  float* dg_part; int n_part;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+
+// Grouped GEMMs of the backward pass (bf16 operands, fp32 results), C = A B
+// with either operand k-major (rows of the operand hold consecutive k) or
+// mn-major (rows hold consecutive m or n; read through LDS transpose loads).
+//   KIND 0  G  = dy W2          M = rows of an expert, N = inner, K = d
+//   KIND 1  dX = dA [W1; W3]    M = rows,  N = d,  K = 2 inner (per expert)
+//   KIND 2  dW2 = dy^T Hg       M = d,     N = inner, K = rows of the expert
+//   KIND 3  [dW1; dW3] = dA^T X M = 2 inner, N = d, K = rows of the expert
+// Routed groups are the experts (rows from the tile list / offsets, token
+// rows through row_src); the shared group has all T tokens in order and
+// n_experts experts side by side (KIND 0, 2, 3: one expert per group index;
+// KIND 1: all shared experts along k).
+struct BwdGemmArgs {
+  int kind;
+  bool shared;
+  int T, d, inner, n_experts;       // inner of the group's experts
+  const MTile* tiles; const int32_t* n_tiles; int max_mtiles;   // routed KIND 0/1
+  const int32_t* offsets;           // routed KIND 2/3: rows of expert e
+  const int32_t* row_src;           // routed: token of each row
+  const bf16_t* dy;                 // [T][d]
+  const bf16_t* x;                  // [T][d]
+  const bf16_t* w1; const bf16_t* w3; const bf16_t* w2;   // the group's weights
+  const bf16_t* da; int ldda;       // [rows][2 inner] (shared: per expert blocks)
+  const bf16_t* hg; int ldhg;       // [rows][inner] g h (shared: per expert blocks)
+  const bf16_t* zero;               // >= 512 zero bytes (k rows past the end)
+  float* c; int ldc;                // KIND 0: G [rows][ldc]; KIND 1: dX [rows][d]
+  float* dw1; float* dw3; float* dw2;   // KIND 2/3 outputs [experts][..][..]
+};
+hipError_t launch_gemm_bwd(const BwdGemmArgs& a, hipStream_t s);
+
+// Backward helpers (backward.hip).
+struct BwdAuxArgs {
+  int T, d, E, K, score, norm_topk;
+  float routed_scale;
+  const float* plog; int ds, ep;    // partial logits [ds][T][ep]
+  const float* logit_bias;
+  const float* w_gate;              // [E][d]
+  const int32_t* topk_idx; const float* topk_w; const int32_t* slot_row;
+  const float* dg_part; int n_part; // [rows][n_part]
+  float* row_g;                     // [T K] gate weight of each row
+  float* dg;                        // [T][K]
+  float* dl;                        // [T][E] logit gradient
+  float* dlogit_bias;               // [E] or NULL
+  const bf16_t* x; const bf16_t* dy;
+  float* dwg_part; int n_chunk;     // [n_chunk][E][d] partial gate gradients
+  float* dw_gate;                   // [E][d]
+  const float* dx_rows;             // [T K][d]
+  const float* dx_shared;           // [T][d] or NULL
+  bf16_t* dx;                       // [T][d]
+  bf16_t* zero; int n_zero;         // zero-filled at the start
+};
+hipError_t launch_bwd_prep(const BwdAuxArgs& a, hipStream_t s);      // row_g, zero
+hipError_t launch_router_bwd(const BwdAuxArgs& a, hipStream_t s);    // dg, dl, dlogit_bias
+hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s);     // dw_gate
+hipError_t launch_dx_combine(const BwdAuxArgs& a, hipStream_t s);    // dx
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s);
 
 // E4M3 quantisation with power-of-two scales: rows of `src` [R][C] (bf16 or

@@ -10,6 +10,8 @@
 //               64 columns of a row, inverse scales beside)
 //   DOWN_SHARED with the combine fused:
 //               out = x + sum_s H_s W2_s^T + sum_k g_k Y_k
+//   GATEUP_BWD  the gate/up tile recomputed for the backward pass, with the
+//               SwiGLU backward in the epilogue (see GemmArgs)
 //
 // Tiling.  A workgroup (4 waves) owns BM token rows x 256 weight rows with a
 // 64-wide k step.  Both operands are k-contiguous in memory (token rows and
@@ -38,15 +40,15 @@ using namespace gemm;
 
 constexpr int BK = 64;    // k per stage (8 chunks of 16 B)
 
-// MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED.  WAVES_M x (4 / WAVES_M) waves.
 // One tile: rows [row0, row0 + rows) (at most BM) of the M dimension (expert
 // e for routed tiles) times N-tile nt, through the LDS buffers As0/As1 (at
-// least BM x 128 B each) and Bs0/Bs1.  MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED;
-// WAVES_M x (4 / WAVES_M) waves.
+// least BM x 128 B each) and Bs0/Bs1.  MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED,
+// 3 GATEUP_BWD; WAVES_M x (4 / WAVES_M) waves.  `red` (4 x BM floats of LDS)
+// carries GATEUP_BWD's row sums across the waves of a tile.
 template <int MODE, int BM, int WAVES_M>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows, int e,
                                           int nt, u32x4* As0, u32x4* As1, u32x4* Bs0,
-                                          u32x4* Bs1) {
+                                          u32x4* Bs1, float* red) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -56,7 +58,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
-  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
+  constexpr bool GU = is_gateup<MODE>();
+  const bool routed = !(MODE == 2 || (GU && a.shared));
 
   // This lane's slot in a wave's 1 KB load block: LDS row lr (of 8) and the
   // global chunk that belongs in slot (lane & 7) of that row.
@@ -80,7 +83,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   const bf16_t* B3 = nullptr;
   uint32_t boff[B_LD];
   int kdim, n0 = 0, grp = 0, inner0 = 0;
-  if (MODE == 0) {
+  if (GU) {
     const int half = WN / 2;                       // inner columns per wave
     const int per_wg = WAVES_N * half;             // inner columns per tile
     const int tiles_per = (a.inner + per_wg - 1) / per_wg;
@@ -126,7 +129,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
 #pragma unroll
     for (int j = 0; j < B_LD; ++j) {
       const bf16_t* base = B1;
-      if (MODE == 0) {
+      if (GU) {
         const int r = (wave * B_LD + j) * 8;        // uniform: W1 or W3 half
         if ((r % WN) >= WN / 2) base = B3;
       }
@@ -238,6 +241,75 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
           v.y = pack2(h[2], h[3]);
           *reinterpret_cast<uint2*>(orow + inner) = v;
         }
+    }
+  } else if (MODE == 3) {
+    // SwiGLU backward on the recomputed pre-activations a1 (W1 half) and a3:
+    //   h = silu(a1) a3, dh = g gin,
+    //   da1 = dh a3 sig(a1) (1 + a1 (1 - sig(a1))), da3 = dh silu(a1),
+    // and the row's share of dg = sum gin h over this tile's inner columns,
+    // summed over the lane's columns, the two lane halves and the tile's
+    // waves in a fixed order.
+    constexpr int HALF_NB = NB / 2;
+    const int col_off = routed ? 0 : grp * a.inner;          // H and gin columns
+    const int da_off = routed ? 0 : grp * 2 * a.inner;       // dA columns
+    bf16_t* out = static_cast<bf16_t*>(a.out);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = wm * WM + mb * 32 + l32;
+      const bool live = m < rows;
+      const int row = row0 + min(m, rows - 1);
+      const float g = (routed && a.row_g) ? a.row_g[row] : 1.f;
+      const float* grow = a.gin + (size_t)row * a.ldgin + col_off;
+      bf16_t* orow = out + (size_t)row * a.ldo + col_off;
+      bf16_t* darow = a.da + (size_t)row * a.ldda + da_off;
+      float part = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < HALF_NB; ++nb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int inner = inner0 + wn * (WN / 2) + nb * 32 + 8 * q4 + 4 * hi;
+          if (inner >= a.inner) continue;
+          const float4 gv = *reinterpret_cast<const float4*>(grow + inner);
+          const float gi[4] = {gv.x, gv.y, gv.z, gv.w};
+          float hv[4], d1[4], d3[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float a1 = acc[nb][mb][4 * q4 + q];
+            const float a3 = acc[nb + HALF_NB][mb][4 * q4 + q];
+            const float sg = __builtin_amdgcn_rcpf(
+                1.f + __builtin_amdgcn_exp2f(a1 * -1.4426950408889634f));
+            const float sl = a1 * sg;
+            hv[q] = sl * a3;
+            part = fmaf(gi[q], hv[q], part);
+            const float dh = g * gi[q];
+            d1[q] = dh * a3 * (sg * (1.f + a1 * (1.f - sg)));
+            d3[q] = dh * sl;
+          }
+          if (!live) continue;
+          uint2 v;
+          v.x = pack2(g * hv[0], g * hv[1]);
+          v.y = pack2(g * hv[2], g * hv[3]);
+          *reinterpret_cast<uint2*>(orow + inner) = v;
+          v.x = pack2(d1[0], d1[1]);
+          v.y = pack2(d1[2], d1[3]);
+          *reinterpret_cast<uint2*>(darow + inner) = v;
+          v.x = pack2(d3[0], d3[1]);
+          v.y = pack2(d3[2], d3[3]);
+          *reinterpret_cast<uint2*>(darow + a.inner + inner) = v;
+        }
+      if (routed && a.dg_part) {
+        part += __shfl_xor(part, 32);
+        if (hi == 0) red[wn * BM + m] = part;
+      }
+    }
+    if (routed && a.dg_part) {
+      __syncthreads();
+      for (int m = threadIdx.x; m < rows; m += 256) {
+        float sum = 0.f;
+        for (int w = 0; w < WAVES_N; ++w) sum += red[w * BM + m];
+        a.dg_part[(size_t)(row0 + m) * a.n_part + nt] = sum;
+      }
     }
   } else if (MODE == 1) {
     // Y rows in fp16, each 64-column group of a row scaled so that its
@@ -378,8 +450,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // buffer from the operand reads of the other and need not wait between.
   __shared__ u32x4 As0[BM * 8], As1[BM * 8];
   __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
+  // Row sums of GATEUP_BWD (the A buffers are free by the epilogue, but a
+  // separate array keeps the buffers' accesses static).
+  __shared__ float red[MODE == 3 ? 4 * BM : 1];
 
-  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
+  const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
@@ -401,20 +476,20 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const MTile t = a.tiles[mt];
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
-        gemm_tile<MODE, BM / 2, 1>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1);
+        gemm_tile<MODE, BM / 2, 1>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, red);
         return;
       }
     }
-    gemm_tile<MODE, BM, WAVES_M>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1);
+    gemm_tile<MODE, BM, WAVES_M>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, red);
   } else {
     const int row0 = mt * BM;
-    gemm_tile<MODE, BM, WAVES_M>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, Bs0, Bs1);
+    gemm_tile<MODE, BM, WAVES_M>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, Bs0, Bs1, red);
   }
 }
 
 template <int MODE, int BM, int WAVES_M>
 void launch_mode(const GemmArgs& a, hipStream_t s) {
-  const bool routed = !(a.mode == 2 || (a.mode == 0 && a.shared));
+  const bool routed = !(a.mode == 2 || ((a.mode == 0 || a.mode == 3) && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
   const int ndim = n_tiles_of<MODE, BM>(a);
   hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WAVES_M>), dim3(mdim * ndim),
@@ -425,7 +500,8 @@ template <int BM, int WAVES_M>
 void launch_bm(const GemmArgs& a, hipStream_t s) {
   if (a.mode == 0) launch_mode<0, BM, WAVES_M>(a, s);
   else if (a.mode == 1) launch_mode<1, BM, WAVES_M>(a, s);
-  else launch_mode<2, BM, WAVES_M>(a, s);
+  else if (a.mode == 2) launch_mode<2, BM, WAVES_M>(a, s);
+  else launch_mode<3, BM, WAVES_M>(a, s);
 }
 
 }  // namespace

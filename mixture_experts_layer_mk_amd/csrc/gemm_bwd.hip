@@ -1,0 +1,332 @@
+// Grouped GEMMs of the layer's backward pass on gfx950 matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation, fp32 results).
+//
+// The backward needs products whose reduction runs along the strided
+// dimension of an operand: the weights in the input gradients (dy W2, dA W1)
+// and the token rows in the weight gradients (dy^T H, dA^T X).  Such an
+// operand is "mn-major": a row in memory holds consecutive m (or n) for one
+// k.  Its tiles go global -> LDS unchanged (64 k-rows of 256 values, 16-byte
+// direct loads), and the matrix operand fragments come out of LDS through
+// the transpose loads (ds_read_b64_tr_b16): in each group of 16 lanes,
+// source lane 4j + q reads 4 consecutive m of k-row j, and lane i receives
+// the 4 values of k-rows 0..3 at m = 4 (i / 4) + i % 4 -- one 16 (m) x 4 (k)
+// block turned into the k-consecutive layout the matrix op wants.  Two such
+// loads give a lane its 8 k-values.  k-major operands (rows hold consecutive
+// k) use the same tiles as the forward GEMMs.
+//
+// Tile: 256 (M) x 256 (N) per workgroup of 4 waves (2 x 2, 128 x 128 each),
+// k in steps of 64, LDS double-buffered (2 x 64 KB), operand fragments
+// double-buffered in registers as in the forward kernels.
+#include "gemm_common.h"
+
+namespace moe {
+
+namespace {
+
+using namespace gemm;
+
+constexpr int TM = 256;     // tile rows (M)
+constexpr int TK = 64;      // k per stage
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Chunk swizzle of mn-major LDS rows (32 chunks of 16 B per k-row): the four
+// k-rows one transpose load touches fall on different chunk columns.
+__device__ __forceinline__ int swz_mn(int k) { return (k & 7) << 1; }
+
+// A 32 (mn) x 16 (k) operand fragment for the matrix op from an mn-major
+// LDS tile (64 k-rows x 32 chunks): lanes 0-31 hold mn = base + lane % 32 at
+// k = 16 kk + 0..7, lanes 32-63 the same mn at k + 8.
+__device__ __forceinline__ bf16x8 frag_mn(const u32x4* T, int base, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int mn = base + 16 * (g & 1) + 4 * (s & 3);
+  const int chunk = mn >> 3, half = (mn >> 2) & 1;
+  const int k0 = kk * 16 + 8 * (g >> 1) + (s >> 2);
+  const char* t = reinterpret_cast<const char*>(T);
+  const int o0 = k0 * 512 + ((chunk ^ swz_mn(k0)) << 4) + half * 8;
+  const int k1 = k0 + 4;
+  const int o1 = k1 * 512 + ((chunk ^ swz_mn(k1)) << 4) + half * 8;
+  const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + o0));
+  const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + o1));
+  const v4s r[2] = {r0, r1};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Where one tile's operands and results live.
+struct TileDesc {
+  int m0, n0;           // tile origin in the group's M x N
+  int mval, nval;       // valid extent of M and N in the group (masks)
+  int K;                // reduction length (k-rows for mn-major operands)
+  int grp;              // expert (routed) or shared expert / 0
+  int row0;             // KIND 0/1: first row of the tile (expert-contiguous)
+  int koff;             // KIND 2/3 routed: first row of the expert
+};
+
+template <int KIND>
+__device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (KIND == 0 || KIND == 1) {
+    const int per = (KIND == 0) ? (a.inner + BN - 1) / BN : (a.d + BN - 1) / BN;
+    const int ndim = (KIND == 0 && a.shared) ? per * a.n_experts : per;
+    const int mt = L / ndim, nt = L % ndim;
+    if (!a.shared) {
+      if (mt >= *a.n_tiles) return false;
+      const MTile m = a.tiles[mt];
+      t.row0 = m.row0; t.mval = m.rows; t.grp = m.expert;
+    } else {
+      t.row0 = mt * TM; t.mval = min(TM, a.T - t.row0); t.grp = (KIND == 0) ? nt / per : 0;
+    }
+    t.m0 = 0;
+    t.n0 = (nt % per) * BN;
+    t.nval = (KIND == 0) ? a.inner : a.d;
+    t.K = (KIND == 0) ? a.d : (a.shared ? 2 * a.inner * a.n_experts : 2 * a.inner);
+    t.koff = 0;
+  } else {
+    const int M = (KIND == 2) ? a.d : 2 * a.inner;
+    const int N = (KIND == 2) ? a.inner : a.d;
+    const int mdim = (M + TM - 1) / TM, ndim = (N + BN - 1) / BN;
+    t.grp = L / (mdim * ndim);
+    const int rem = L % (mdim * ndim);
+    t.m0 = (rem / ndim) * TM; t.n0 = (rem % ndim) * BN;
+    t.mval = M; t.nval = N;
+    if (a.shared) { t.koff = 0; t.K = a.T; }
+    else { t.koff = a.offsets[t.grp]; t.K = a.offsets[t.grp + 1] - t.koff; }
+    t.row0 = 0;
+  }
+  return true;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
+  __shared__ u32x4 As0[2048], As1[2048];   // 32 KB each: 256 x 8 or 64 x 32 chunks
+  __shared__ u32x4 Bs0[2048], Bs1[2048];
+
+  TileDesc t;
+  if (!decode<KIND>(a, t)) return;
+
+  constexpr bool AK = (KIND == 0 || KIND == 1);   // A k-major; B is always mn-major
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int nk = (t.K + TK - 1) / TK;
+
+  // ---- k-major A (KIND 0, 1): 256 rows x 8 chunks per stage ----
+  // Lane slot: LDS row (wave * 8 + j) * 8 + lr, chunk (lane & 7) after the
+  // row swizzle, as in the forward kernels.
+  const int lr = lane >> 3;
+  const int cg0 = (lane & 7) ^ lr, cg1 = cg0 ^ 1;
+  const bf16_t* arow[8];
+  if constexpr (AK) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = wave * 8 + j;
+      const int r = min(blk * 8 + lr, t.mval - 1);
+      const int row = t.row0 + r;
+      const bf16_t* p;
+      if (KIND == 0) {
+        const int tok = a.shared ? row : a.row_src[row];
+        p = a.dy + (size_t)tok * a.d;
+      } else {
+        p = a.da + (size_t)row * a.ldda;
+      }
+      arow[j] = p + ((blk & 1) ? cg1 : cg0) * 8;
+    }
+  }
+
+  // ---- mn-major operands: 64 k-rows x 32 chunks per stage ----
+  // Lane slot: k-row 2 (wave * 8 + j) + (lane >> 5), chunk (lane & 31).
+  const int ks = lane >> 5, cs = lane & 31;
+  // global pointer of k-row k (absolute in [0, K)) of operand A / B, at this
+  // lane's chunk, or the zero row when k is past the end
+  auto a_row = [&](int k) -> const bf16_t* {
+    const int kr = k & (TK - 1);
+    int c = cs ^ swz_mn(kr);
+    if (t.m0 + c * 8 >= t.mval) c = 0;
+    if (k >= t.K) return a.zero + cs * 8;
+    if (KIND == 2) {
+      const int tok = a.shared ? k : a.row_src[t.koff + k];
+      return a.dy + (size_t)tok * a.d + t.m0 + c * 8;
+    } else {   // KIND 3
+      const int row = t.koff + k;
+      const size_t off = a.shared ? (size_t)t.grp * 2 * a.inner : 0;
+      return a.da + (size_t)row * a.ldda + off + t.m0 + c * 8;
+    }
+  };
+  auto b_row = [&](int k) -> const bf16_t* {
+    const int kr = k & (TK - 1);
+    int c = cs ^ swz_mn(kr);
+    if (t.n0 + c * 8 >= t.nval) c = 0;
+    if (k >= t.K) return a.zero + cs * 8;
+    const int n = t.n0 + c * 8;
+    if (KIND == 0) {            // W2 of the group: [d][inner]
+      return a.w2 + ((size_t)t.grp * a.d + k) * a.inner + n;
+    } else if (KIND == 1) {     // W1 / W3 rows along k
+      const int per = 2 * a.inner;
+      const int e = a.shared ? k / per : t.grp;
+      const int r = a.shared ? k % per : k;
+      const bf16_t* w = (r < a.inner) ? a.w1 : a.w3;
+      return w + ((size_t)e * a.inner + (r % a.inner)) * a.d + n;
+    } else if (KIND == 2) {     // g h rows
+      const int row = t.koff + k;
+      const size_t off = a.shared ? (size_t)t.grp * a.inner : 0;
+      return a.hg + (size_t)row * a.ldhg + off + n;
+    } else {                    // token rows of x
+      const int tok = a.shared ? k : a.row_src[t.koff + k];
+      return a.x + (size_t)tok * a.d + n;
+    }
+  };
+
+  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
+    const int k0 = kb * TK;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = wave * 8 + j;
+      if constexpr (AK) {
+        __builtin_amdgcn_global_load_lds((const glb_void*)(arow[j] + k0),
+                                         (lds_void*)&Ab[blk * 64], 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((const glb_void*)a_row(k0 + 2 * blk + ks),
+                                         (lds_void*)&Ab[blk * 64], 16, 0, 0);
+      }
+      __builtin_amdgcn_global_load_lds((const glb_void*)b_row(k0 + 2 * blk + ks),
+                                       (lds_void*)&Bb[blk * 64], 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto load_frags = [&](bf16x8* fa, bf16x8* fb, const u32x4* Ab, const u32x4* Bb, int kk) {
+    const int c = 2 * kk + hi;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if constexpr (AK) {
+        const int r = wm * 128 + mb * 32 + l32;
+        fa[mb] = __builtin_bit_cast(bf16x8, Ab[r * 8 + (c ^ swz_x(r))]);
+      } else {
+        fa[mb] = frag_mn(Ab, wm * 128 + mb * 32, kk, lane);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) fb[nb] = frag_mn(Bb, wn * 128 + nb * 32, kk, lane);
+  };
+  auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb],
+                                                             0, 0, 0);
+  };
+  constexpr int N_DS = (AK ? 4 : 8) + 8;
+  auto sched_ds = [&]() { sched_groups<16, N_DS, 0>(); };
+  auto sched_ds_vm = [&]() { sched_groups<16, N_DS, 16>(); };
+
+  // Same pipeline as the forward kernels: block kb from (Ac, Bc) while kb+1
+  // streams into (An, Bn); kb+2 is issued into (Ac, Bc) once every wave
+  // holds its last fragments of kb.  Blocks past the end re-load the last.
+  auto block = [&](int next2, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
+    load_frags(fa1, fb1, Ac, Bc, 1);
+    mma(fa0, fb0);
+    sched_ds();
+    load_frags(fa0, fb0, Ac, Bc, 2);
+    mma(fa1, fb1);
+    sched_ds();
+    load_frags(fa1, fb1, Ac, Bc, 3);
+    mma(fa0, fb0);
+    sched_ds();
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(next2, Ac, Bc);
+    load_frags(fa0, fb0, An, Bn, 0);
+    mma(fa1, fb1);
+    sched_ds_vm();
+  };
+
+  if (nk > 0) {
+    issue(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<16>());
+    __syncthreads();
+    load_frags(fa0, fb0, As0, Bs0, 0);
+    int kb = 0;
+    for (; kb + 2 <= nk; kb += 2) {
+      block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
+      block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+    }
+    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load left in flight
+  }
+
+  // ---- epilogue: acc[nb][mb][r] = C[m][n], m = mb*32 + l32 and
+  // n = nb*32 + 8*(r/4) + 4*hi + r%4 inside the wave's 128 x 128 ----
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = t.m0 + wm * 128 + mb * 32 + l32;
+    if (m >= t.mval) continue;
+    float* crow;
+    if (KIND == 0) {
+      const size_t col = a.shared ? (size_t)t.grp * a.inner : 0;
+      crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
+    } else if (KIND == 1) {
+      crow = a.c + (size_t)(t.row0 + m) * a.ldc;
+    } else if (KIND == 2) {
+      crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
+    } else {
+      crow = (m < a.inner) ? a.dw1 + ((size_t)t.grp * a.inner + m) * a.d
+                           : a.dw3 + ((size_t)t.grp * a.inner + (m - a.inner)) * a.d;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = t.n0 + wn * 128 + nb * 32 + 8 * g + 4 * hi;
+        if (n >= t.nval) continue;
+        float4 v;
+        v.x = acc[nb][mb][4 * g + 0];
+        v.y = acc[nb][mb][4 * g + 1];
+        v.z = acc[nb][mb][4 * g + 2];
+        v.w = acc[nb][mb][4 * g + 3];
+        *reinterpret_cast<float4*>(crow + n) = v;
+      }
+  }
+}
+
+template <int KIND>
+void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
+  int grid;
+  if (KIND == 0 || KIND == 1) {
+    const int per = (KIND == 0) ? (a.inner + BN - 1) / BN : (a.d + BN - 1) / BN;
+    const int ndim = (KIND == 0 && a.shared) ? per * a.n_experts : per;
+    const int mdim = a.shared ? (a.T + TM - 1) / TM : a.max_mtiles;
+    grid = mdim * ndim;
+  } else {
+    const int M = (KIND == 2) ? a.d : 2 * a.inner;
+    const int N = (KIND == 2) ? a.inner : a.d;
+    grid = a.n_experts * ((M + TM - 1) / TM) * ((N + BN - 1) / BN);
+  }
+  if (grid <= 0) return;
+  hipLaunchKernelGGL(gemm_bwd_kernel<KIND>, dim3(grid), dim3(256), 0, s, a);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bwd(const BwdGemmArgs& a, hipStream_t s) {
+  switch (a.kind) {
+    case 0: launch_kind<0>(a, s); break;
+    case 1: launch_kind<1>(a, s); break;
+    case 2: launch_kind<2>(a, s); break;
+    case 3: launch_kind<3>(a, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -88,12 +88,16 @@ constexpr int vmcnt_imm() {
   return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
 }
 
+// Stages whose tiles are gate/up tiles (GATEUP and its backward).
+template <int MODE>
+constexpr bool is_gateup() { return MODE == 0 || MODE == 3; }
+
 // N-tiles of one GEMM stage (GATEUP: 128 inner columns per tile, for each
 // expert of the shared group; DOWN: 256 output columns per tile).
 template <int MODE, int BM>
 __host__ __device__ __forceinline__ int n_tiles_of(const GemmArgs& a) {
-  const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
-  if (MODE == 0) return ((a.inner + BN / 2 - 1) / (BN / 2)) * (routed ? 1 : a.n_experts);
+  const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
+  if (is_gateup<MODE>()) return ((a.inner + BN / 2 - 1) / (BN / 2)) * (routed ? 1 : a.n_experts);
   return (a.d + BN - 1) / BN;
 }
 

@@ -125,6 +125,79 @@ bool overlaps(const void* a, const void* b, size_t n) {
   return pa < pb + n && pb < pa + n;
 }
 
+// Router, per-expert scan and tile schedule, and the row maps (steps 1-3
+// of the forward; the backward re-runs them to recover the same expert
+// choice).  mark(i) records trace event i before step i.
+template <class Mark>
+moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws,
+                            const void* x, const float* w_gate, const float* logit_bias,
+                            const float* select_bias, int32_t* idx, float* gw,
+                            int32_t* expert_counts, hipStream_t s, Mark mark) {
+  auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
+  const bool bf16 = d.dtype != MOE_F32;
+  const bool fp8 = d.dtype == MOE_FP8;
+  hipError_t err;
+#define MOE_CHECK(call)                      \
+  do {                                       \
+    err = (call);                            \
+    if (err != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+  // 1. router
+  if (!mark(0)) return MOE_ERR_HIP;
+  {
+    RouterArgs r{};
+    r.x = x; r.dtype = bf16 ? 1 : 0;
+    r.w_gate = w_gate; r.logit_bias = logit_bias; r.select_bias = select_bias;
+    r.T = d.T; r.d = d.d; r.E = d.n_routed; r.K = d.top_k; r.score = d.score;
+    r.n_groups = d.n_groups; r.topk_groups = d.topk_groups; r.norm_topk = d.norm_topk;
+    r.routed_scale = d.routed_scale;
+    r.ds = L.ds; r.ep = L.ep;
+    r.planes = static_cast<bf16_t*>(at(L.planes));
+    r.plog = static_cast<float*>(at(L.plog));
+    r.topk_idx = idx; r.topk_w = gw;
+    r.rank = static_cast<int32_t*>(at(L.rank));
+    r.block_counts = static_cast<int32_t*>(at(L.block_counts));
+    MOE_CHECK(launch_router(r, s));
+    if (fp8) {   // the token rows in E4M3, per 1 x 128 of the hidden dimension
+      QuantArgs q{};
+      q.src = x; q.src_f32 = 0; q.batch = 1; q.rows = d.T; q.cols = d.d;
+      q.codes = static_cast<uint8_t*>(at(L.x_q));
+      q.scales = static_cast<uint8_t*>(at(L.x_scale));
+      MOE_CHECK(launch_quant_rows(q, s));
+    }
+  }
+  // 2. scan + tile schedule
+  if (!mark(1)) return MOE_ERR_HIP;
+  {
+    ScanArgs c{};
+    c.block_counts = static_cast<const int32_t*>(at(L.block_counts));
+    c.block_base = static_cast<int32_t*>(at(L.block_base));
+    c.counts = static_cast<int32_t*>(at(L.counts));
+    c.user_counts = expert_counts;
+    c.offsets = static_cast<int32_t*>(at(L.offsets));
+    c.tiles = static_cast<MTile*>(at(L.tiles));
+    c.n_tiles = static_cast<int32_t*>(at(L.n_tiles));
+    c.nblk = L.nblk; c.E = d.n_routed; c.bm = L.bm;
+    MOE_CHECK(launch_scan(c, s));
+  }
+  // 3. permute
+  if (!mark(2)) return MOE_ERR_HIP;
+  {
+    PermuteArgs p{};
+    p.x = x; p.dtype = bf16 ? 1 : 0; p.T = d.T; p.d = d.d; p.K = d.top_k;
+    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
+    p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
+    p.block_base = static_cast<const int32_t*>(at(L.block_base));
+    p.offsets = static_cast<const int32_t*>(at(L.offsets));
+    p.slot_row = static_cast<int32_t*>(at(L.slot_row));
+    p.row_src = static_cast<int32_t*>(at(L.row_src));
+    p.xp = nullptr;
+    MOE_CHECK(launch_permute(p, s));
+  }
+#undef MOE_CHECK
+  return MOE_OK;
+}
+
 moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
                           const float* w_gate, const float* logit_bias,
                           const float* select_bias, moe_ffn_weights_t routed,
@@ -171,59 +244,11 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     if (err != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
-  // 1. router
-  if (!mark(0)) return MOE_ERR_HIP;
-  {
-    RouterArgs r{};
-    r.x = x; r.dtype = bf16 ? 1 : 0;
-    r.w_gate = w_gate; r.logit_bias = logit_bias; r.select_bias = select_bias;
-    r.T = d.T; r.d = d.d; r.E = d.n_routed; r.K = d.top_k; r.score = d.score;
-    r.n_groups = d.n_groups; r.topk_groups = d.topk_groups; r.norm_topk = d.norm_topk;
-    r.routed_scale = d.routed_scale;
-    r.ds = L.ds; r.ep = L.ep;
-    r.planes = static_cast<bf16_t*>(at(L.planes));
-    r.plog = static_cast<float*>(at(L.plog));
-    r.topk_idx = idx; r.topk_w = gw;
-    r.rank = static_cast<int32_t*>(at(L.rank));
-    r.block_counts = static_cast<int32_t*>(at(L.block_counts));
-    MOE_CHECK(launch_router(r, s));
-    if (fp8) {   // the token rows in E4M3, per 1 x 128 of the hidden dimension
-      QuantArgs q{};
-      q.src = x; q.src_f32 = 0; q.batch = 1; q.rows = d.T; q.cols = d.d;
-      q.codes = static_cast<uint8_t*>(at(L.x_q));
-      q.scales = static_cast<uint8_t*>(at(L.x_scale));
-      MOE_CHECK(launch_quant_rows(q, s));
-    }
-  }
-  // 2. scan + tile schedule
-  if (!mark(1)) return MOE_ERR_HIP;
+  st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
+                      s, mark);
+  if (st != MOE_OK) return st;
   MTile* tiles = static_cast<MTile*>(at(L.tiles));
   int32_t* n_tiles = static_cast<int32_t*>(at(L.n_tiles));
-  {
-    ScanArgs c{};
-    c.block_counts = static_cast<const int32_t*>(at(L.block_counts));
-    c.block_base = static_cast<int32_t*>(at(L.block_base));
-    c.counts = static_cast<int32_t*>(at(L.counts));
-    c.user_counts = expert_counts;
-    c.offsets = static_cast<int32_t*>(at(L.offsets));
-    c.tiles = tiles; c.n_tiles = n_tiles;
-    c.nblk = L.nblk; c.E = d.n_routed; c.bm = L.bm;
-    MOE_CHECK(launch_scan(c, s));
-  }
-  // 3. permute
-  if (!mark(2)) return MOE_ERR_HIP;
-  {
-    PermuteArgs p{};
-    p.x = x; p.dtype = bf16 ? 1 : 0; p.T = d.T; p.d = d.d; p.K = d.top_k;
-    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
-    p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
-    p.block_base = static_cast<const int32_t*>(at(L.block_base));
-    p.offsets = static_cast<const int32_t*>(at(L.offsets));
-    p.slot_row = static_cast<int32_t*>(at(L.slot_row));
-    p.row_src = static_cast<int32_t*>(at(L.row_src));
-    p.xp = nullptr;
-    MOE_CHECK(launch_permute(p, s));
-  }
   auto gemm = [&](const GemmArgs& g) {
     return fp8 ? launch_gemm_fp8(g, s) : bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
   };
@@ -315,6 +340,227 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   return MOE_OK;
 }
 
+// Backward workspace: the forward's regions (routing, row maps; the H
+// regions hold g h for the weight gradients), then the backward's own.
+struct BwdLayout {
+  Layout f;
+  int64_t plog, g_r, g_s, da_r, da_s, dx_rows, dx_s, row_g, dg_part, dg, dl, dwg_part, zero,
+      total;
+  int32_t n_part, n_chunk;
+};
+
+constexpr int kGateGradChunks = 16;
+
+BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
+  BwdLayout B;
+  B.f = layout_of(d);
+  int64_t off = B.f.total;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t TK = (int64_t)d.T * d.top_k;
+  const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
+  B.n_part = (d.inner + 127) / 128;
+  B.n_chunk = kGateGradChunks;
+  B.plog = take((int64_t)B.f.ds * d.T * B.f.ep * 4);
+  B.g_r = take(TK * d.inner * 4);
+  B.g_s = d.n_shared > 0 ? take((int64_t)d.T * ksi * 4) : -1;
+  B.da_r = take(TK * 2 * d.inner * 2);
+  B.da_s = d.n_shared > 0 ? take((int64_t)d.T * 2 * ksi * 2) : -1;
+  B.dx_rows = take(TK * d.d * 4);
+  B.dx_s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
+  B.row_g = take(TK * 4);
+  B.dg_part = take(TK * B.n_part * 4);
+  B.dg = take(TK * 4);
+  B.dl = take((int64_t)d.T * d.n_routed * 4);
+  const int64_t colsum = (int64_t)((d.T + 255) / 256) * d.n_routed;
+  B.dwg_part = take(std::max<int64_t>((int64_t)B.n_chunk * d.n_routed * d.d, colsum) * 4);
+  B.zero = take(1024);
+  B.total = off;
+  return B;
+}
+
+moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const float* w_gate,
+                           const float* logit_bias, const float* select_bias,
+                           moe_ffn_weights_t routed, moe_ffn_weights_t shared,
+                           const void* dout, void* dx, float* dw_gate, float* dlogit_bias,
+                           moe_ffn_grads_t d_routed, moe_ffn_grads_t d_shared,
+                           int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                           void* stream_ptr) {
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const moe_layer_desc_t& d = *desc;
+  if (d.dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (!w_gate || !routed.w1 || !routed.w3 || !routed.w2 || !dw_gate) return MOE_ERR_INVALID_ARG;
+  if (!d_routed.dw1 || !d_routed.dw3 || !d_routed.dw2) return MOE_ERR_INVALID_ARG;
+  if (d.n_shared > 0 && (!shared.w1 || !shared.w3 || !shared.w2 || !d_shared.dw1 ||
+                         !d_shared.dw3 || !d_shared.dw2))
+    return MOE_ERR_INVALID_ARG;
+  if (d.T > 0 && (!x || !dout || !dx)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  const int64_t I = d.inner, Is = d.shared_inner, Ks = d.n_shared, E = d.n_routed;
+  if (d.T == 0) {   // no tokens: every parameter gradient is zero
+    hipError_t e = launch_fill_zero(dw_gate, E * d.d, s);
+    if (e == hipSuccess && dlogit_bias) e = launch_fill_zero(dlogit_bias, E, s);
+    if (e == hipSuccess) e = launch_fill_zero(d_routed.dw1, E * I * d.d, s);
+    if (e == hipSuccess) e = launch_fill_zero(d_routed.dw3, E * I * d.d, s);
+    if (e == hipSuccess) e = launch_fill_zero(d_routed.dw2, E * I * d.d, s);
+    if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw1, Ks * Is * d.d, s);
+    if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw3, Ks * Is * d.d, s);
+    if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw2, Ks * Is * d.d, s);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  const BwdLayout B = bwd_layout_of(d);
+  const Layout& L = B.f;
+  if (!workspace || workspace_bytes < (size_t)B.total ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return MOE_ERR_WORKSPACE;
+  const size_t xbytes = (size_t)d.T * d.d * 2;
+  if (overlaps(dx, dout, xbytes) || overlaps(dx, x, xbytes)) return MOE_ERR_ALIAS;
+
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
+  int32_t* idx = topk_idx ? topk_idx : static_cast<int32_t*>(at(L.topk_idx));
+  float* gw = static_cast<float*>(at(L.topk_w));
+  auto no_mark = [](int) { return true; };
+  st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, nullptr, s,
+                      no_mark);
+  if (st != MOE_OK) return st;
+  hipError_t err;
+#define MOE_CHECK(call)                      \
+  do {                                       \
+    err = (call);                            \
+    if (err != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* dyb = static_cast<const bf16_t*>(dout);
+  const int32_t* slot_row = static_cast<const int32_t*>(at(L.slot_row));
+  const int32_t* row_src = static_cast<const int32_t*>(at(L.row_src));
+
+  BwdAuxArgs aux{};
+  aux.T = d.T; aux.d = d.d; aux.E = d.n_routed; aux.K = d.top_k; aux.score = d.score;
+  aux.norm_topk = d.norm_topk; aux.routed_scale = d.routed_scale;
+  aux.plog = static_cast<const float*>(at(B.plog)); aux.ds = L.ds; aux.ep = L.ep;
+  aux.logit_bias = logit_bias; aux.w_gate = w_gate;
+  aux.topk_idx = idx; aux.topk_w = gw; aux.slot_row = slot_row;
+  aux.dg_part = static_cast<const float*>(at(B.dg_part)); aux.n_part = B.n_part;
+  aux.row_g = static_cast<float*>(at(B.row_g));
+  aux.dg = static_cast<float*>(at(B.dg));
+  aux.dl = static_cast<float*>(at(B.dl));
+  aux.dlogit_bias = dlogit_bias;
+  aux.x = xb; aux.dy = dyb;
+  aux.dwg_part = static_cast<float*>(at(B.dwg_part)); aux.n_chunk = B.n_chunk;
+  aux.dw_gate = dw_gate;
+  aux.dx_rows = static_cast<const float*>(at(B.dx_rows));
+  aux.dx_shared = static_cast<const float*>(at(B.dx_s));
+  aux.dx = static_cast<bf16_t*>(dx);
+  aux.zero = static_cast<bf16_t*>(at(B.zero)); aux.n_zero = 512;
+  MOE_CHECK(launch_bwd_prep(aux, s));
+
+  BwdGemmArgs rb{};
+  rb.T = d.T; rb.d = d.d; rb.inner = d.inner; rb.n_experts = d.n_routed; rb.shared = false;
+  rb.tiles = static_cast<const MTile*>(at(L.tiles));
+  rb.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); rb.max_mtiles = L.max_mtiles;
+  rb.offsets = static_cast<const int32_t*>(at(L.offsets)); rb.row_src = row_src;
+  rb.dy = dyb; rb.x = xb;
+  rb.w1 = static_cast<const bf16_t*>(routed.w1);
+  rb.w3 = static_cast<const bf16_t*>(routed.w3);
+  rb.w2 = static_cast<const bf16_t*>(routed.w2);
+  rb.da = static_cast<const bf16_t*>(at(B.da_r)); rb.ldda = 2 * d.inner;
+  rb.hg = static_cast<const bf16_t*>(at(L.h_routed)); rb.ldhg = d.inner;
+  rb.zero = static_cast<const bf16_t*>(at(B.zero));
+  rb.dw1 = d_routed.dw1; rb.dw3 = d_routed.dw3; rb.dw2 = d_routed.dw2;
+  BwdGemmArgs sb = rb;
+  if (Ks > 0) {
+    sb.shared = true; sb.inner = d.shared_inner; sb.n_experts = d.n_shared;
+    sb.w1 = static_cast<const bf16_t*>(shared.w1);
+    sb.w3 = static_cast<const bf16_t*>(shared.w3);
+    sb.w2 = static_cast<const bf16_t*>(shared.w2);
+    sb.da = static_cast<const bf16_t*>(at(B.da_s)); sb.ldda = (int)(2 * Ks * Is);
+    sb.hg = static_cast<const bf16_t*>(at(L.h_shared)); sb.ldhg = (int)(Ks * Is);
+    sb.dw1 = d_shared.dw1; sb.dw3 = d_shared.dw3; sb.dw2 = d_shared.dw2;
+  }
+
+  // 1. G = dy W2 of every row (before the gate weight)
+  {
+    BwdGemmArgs g = rb;
+    g.kind = 0; g.c = static_cast<float*>(at(B.g_r)); g.ldc = d.inner;
+    MOE_CHECK(launch_gemm_bwd(g, s));
+    if (Ks > 0) {
+      g = sb;
+      g.kind = 0; g.c = static_cast<float*>(at(B.g_s)); g.ldc = (int)(Ks * Is);
+      MOE_CHECK(launch_gemm_bwd(g, s));
+    }
+  }
+  // 2. gate/up recomputed with the SwiGLU backward: dA, g h, dg row sums
+  {
+    GemmArgs g{};
+    g.mode = 3; g.d = d.d; g.tiles = static_cast<const MTile*>(at(L.tiles));
+    g.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); g.max_mtiles = L.max_mtiles;
+    g.T = d.T; g.bm = L.bm; g.x = x;
+    g.shared = false; g.a = x; g.lda = d.d; g.a_rows = row_src;
+    g.w1 = routed.w1; g.w3 = routed.w3; g.inner = d.inner; g.n_experts = d.n_routed;
+    g.out = at(L.h_routed); g.ldo = d.inner;
+    g.gin = static_cast<const float*>(at(B.g_r)); g.ldgin = d.inner;
+    g.row_g = static_cast<const float*>(at(B.row_g));
+    g.da = static_cast<bf16_t*>(at(B.da_r)); g.ldda = 2 * d.inner;
+    g.dg_part = static_cast<float*>(at(B.dg_part)); g.n_part = B.n_part;
+    MOE_CHECK(launch_gemm_bf16(g, s));
+    if (Ks > 0) {
+      g.shared = true; g.a_rows = nullptr;
+      g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+      g.out = at(L.h_shared); g.ldo = (int)(Ks * Is);
+      g.gin = static_cast<const float*>(at(B.g_s)); g.ldgin = (int)(Ks * Is);
+      g.row_g = nullptr;
+      g.da = static_cast<bf16_t*>(at(B.da_s)); g.ldda = (int)(2 * Ks * Is);
+      g.dg_part = nullptr; g.n_part = 0;
+      MOE_CHECK(launch_gemm_bf16(g, s));
+    }
+  }
+  // 3. router: logits again (partial sums), scores, dg, dl, logit-bias and
+  // gate gradients
+  {
+    LogitsArgs la{};
+    la.x = xb; la.planes = static_cast<const bf16_t*>(at(L.planes));
+    la.T = d.T; la.d = d.d; la.E = d.n_routed; la.ep = L.ep; la.ds = L.ds;
+    la.plog = static_cast<float*>(at(B.plog));
+    MOE_CHECK(launch_logits(la, s));
+    MOE_CHECK(launch_router_bwd(aux, s));
+    MOE_CHECK(launch_gate_grad(aux, s));
+  }
+  // 4. input gradient of every row and of the shared experts, then dx
+  {
+    BwdGemmArgs g = rb;
+    g.kind = 1; g.c = static_cast<float*>(at(B.dx_rows)); g.ldc = d.d;
+    MOE_CHECK(launch_gemm_bwd(g, s));
+    if (Ks > 0) {
+      g = sb;
+      g.kind = 1; g.c = static_cast<float*>(at(B.dx_s)); g.ldc = d.d;
+      MOE_CHECK(launch_gemm_bwd(g, s));
+    }
+    MOE_CHECK(launch_dx_combine(aux, s));
+  }
+  // 5. weight gradients
+  {
+    BwdGemmArgs g = rb;
+    g.kind = 2;
+    MOE_CHECK(launch_gemm_bwd(g, s));
+    g.kind = 3;
+    MOE_CHECK(launch_gemm_bwd(g, s));
+    if (Ks > 0) {
+      g = sb;
+      g.kind = 2;
+      MOE_CHECK(launch_gemm_bwd(g, s));
+      g.kind = 3;
+      MOE_CHECK(launch_gemm_bwd(g, s));
+    }
+  }
+#undef MOE_CHECK
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +630,27 @@ moe_status_t moe_layer_forward_traced(
   return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
                       topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
                       stream, events);
+}
+
+moe_status_t moe_layer_backward_workspace_size(const moe_layer_desc_t* desc, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  if (desc->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  *bytes = (size_t)bwd_layout_of(*desc).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, const void* x,
+                                const float* w_gate, const float* logit_bias,
+                                const float* select_bias, moe_ffn_weights_t routed,
+                                moe_ffn_weights_t shared, const void* dout, void* dx,
+                                float* dw_gate, float* dlogit_bias, moe_ffn_grads_t d_routed,
+                                moe_ffn_grads_t d_shared, int32_t* topk_idx, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return backward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, dout, dx,
+                       dw_gate, dlogit_bias, d_routed, d_shared, topk_idx, workspace,
+                       workspace_bytes, stream);
 }
 
 moe_status_t moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t batch,

@@ -557,6 +557,13 @@ bool router_fused(int E, int K, int n_groups, int dtype) {
   return dtype == 1 && E <= 64 && K <= FR_KMAX && n_groups == 1;
 }
 
+hipError_t launch_logits(const LogitsArgs& la, hipStream_t s) {
+  if (la.T == 0) return hipSuccess;
+  const int tiles = ((la.T + 31) / 32) * ((la.E + 31) / 32) * la.ds;
+  hipLaunchKernelGGL(logits_mfma_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s, la);
+  return hipGetLastError();
+}
+
 hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
   if (router_fused(r.E, r.K, r.n_groups, r.dtype)) {
     const int64_t n = (int64_t)r.E * r.d;

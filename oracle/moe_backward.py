@@ -45,10 +45,12 @@ def dsilu(a: np.ndarray) -> np.ndarray:
     return sg * (1.0 + a * (1.0 - sg))
 
 
-def expert_backward(u, dY, w1, w3, w2):
+def expert_backward(u, dY, w1, w3, w2, magnitudes: bool = False):
     """One SwiGLU expert on rows ``u`` [R, d] with output gradient ``dY``
     [R, d].  Returns (du [R, d], dW1 [I, d], dW3 [I, d], dW2 [d, I], y [R, d]),
-    fp64."""
+    fp64.  With ``magnitudes`` also the sums of the absolute values of the
+    terms of du, dW1, dW3 and dW2 (same shapes): the scale of each result's
+    rounding error when one factor of every term is rounded."""
     u = np.asarray(u, np.float64)
     dY = np.asarray(dY, np.float64)
     w1, w3, w2 = (np.asarray(w, np.float64) for w in (w1, w3, w2))
@@ -59,7 +61,12 @@ def expert_backward(u, dY, w1, w3, w2):
     dh = dY @ w2
     da1 = dh * a3 * dsilu(a1)
     da3 = dh * silu(a1)
-    return da1 @ w1 + da3 @ w3, da1.T @ u, da3.T @ u, dW2, h @ w2.T
+    out = (da1 @ w1 + da3 @ w3, da1.T @ u, da3.T @ u, dW2, h @ w2.T)
+    if not magnitudes:
+        return out
+    A1, A3, U = np.abs(da1), np.abs(da3), np.abs(u)
+    mag = (A1 @ np.abs(w1) + A3 @ np.abs(w3), A1.T @ U, A3.T @ U, np.abs(dY).T @ np.abs(h))
+    return out + (mag,)
 
 
 @dataclasses.dataclass
@@ -72,6 +79,11 @@ class Grads:
     dg: np.ndarray                  # [T, K] gradient of the gate weights
     dlogits: np.ndarray             # [T, E]
     idx: np.ndarray                 # [T, K] the expert choice used
+    # with magnitudes=True: sums of |terms| of the experts' products (dx's
+    # expert part; routed / shared (dW1, dW3, dW2)), else None
+    dx_mag: Optional[np.ndarray] = None
+    routed_mag: Optional[tuple] = None
+    shared_mag: Optional[tuple] = None
 
 
 def gate_weight_backward(s, idx, dg, norm_topk: bool, routed_scale: float):
@@ -115,10 +127,12 @@ def exact_scores(x, w_gate, logit_bias, score: str) -> np.ndarray:
 def moe_backward(x, w_gate, routed, shared, top_k: int, dy, *, n_shared: int = 0,
                  score: str = "softmax", logit_bias=None, select_bias=None,
                  n_groups: int = 1, topk_groups: int = 1, norm_topk: bool = False,
-                 routed_scale: float = 1.0, forced_idx=None) -> Grads:
+                 routed_scale: float = 1.0, forced_idx=None,
+                 magnitudes: bool = False) -> Grads:
     """Gradients of ``sum(dy * y)`` for the layer forward of ``moe_forward``
     (same arguments), the expert choice held at the forward's (or
-    ``forced_idx``)."""
+    ``forced_idx``).  ``magnitudes`` adds the sums of |terms| of the experts'
+    products (see ``expert_backward``; routed terms weighted by |g|)."""
     x64 = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
     T, d = x64.shape
@@ -134,13 +148,19 @@ def moe_backward(x, w_gate, routed, shared, top_k: int, dy, *, n_shared: int = 0
     g = g * float(routed_scale)
 
     dx = dy.copy()                                      # residual
-    shared_g = None
+    dx_mag = np.zeros((T, d)) if magnitudes else None
+    shared_g = shared_m = None
     if n_shared > 0:
         fn = _as_expert_fn(shared)
-        outs = [expert_backward(x64, dy, *fn(si)) for si in range(n_shared)]
+        outs = [expert_backward(x64, dy, *fn(si), magnitudes=magnitudes)
+                for si in range(n_shared)]
         for o in outs:
             dx += o[0]
         shared_g = tuple(np.stack([o[i] for o in outs]) for i in (1, 2, 3))
+        if magnitudes:
+            for o in outs:
+                dx_mag += o[5][0]
+            shared_m = tuple(np.stack([o[5][i] for o in outs]) for i in (1, 2, 3))
 
     fn = _as_expert_fn(routed)
     w1_0 = np.asarray(fn(0)[0])
@@ -150,21 +170,31 @@ def moe_backward(x, w_gate, routed, shared, top_k: int, dy, *, n_shared: int = 0
     dW2 = np.zeros((E, d, I))
     dg = np.zeros((T, top_k))
     dx_routed = np.zeros((T, top_k, d))
+    routed_m = tuple(np.zeros_like(a) for a in (dW1, dW3, dW2)) if magnitudes else None
+    dx_routed_m = np.zeros((T, top_k, d)) if magnitudes else None
     for e in np.unique(idx):
         tt, kk = np.nonzero(idx == e)
-        du, d1, d3, d2, y_e = expert_backward(x64[tt], g[tt, kk, None] * dy[tt], *fn(int(e)))
+        o = expert_backward(x64[tt], g[tt, kk, None] * dy[tt], *fn(int(e)),
+                            magnitudes=magnitudes)
+        du, d1, d3, d2, y_e = o[:5]
         dW1[e], dW3[e], dW2[e] = d1, d3, d2
         dx_routed[tt, kk] = du
         dg[tt, kk] = (dy[tt] * y_e).sum(axis=1)
+        if magnitudes:
+            dx_routed_m[tt, kk] = o[5][0]
+            for j in range(3):
+                routed_m[j][e] = o[5][j + 1]
     for k in range(top_k):
         dx += dx_routed[:, k]
+        if magnitudes:
+            dx_mag += dx_routed_m[:, k]
 
     ds = gate_weight_backward(s, idx, dg, norm_topk, routed_scale)
     dl = score_backward(s, ds, score)
     dx += dl @ wg
     return Grads(dx=dx, dw_gate=dl.T @ x64, dlogit_bias=dl.sum(axis=0),
                  routed=(dW1, dW3, dW2), shared=shared_g, dg=dg, dlogits=dl,
-                 idx=r.idx)
+                 idx=r.idx, dx_mag=dx_mag, routed_mag=routed_m, shared_mag=shared_m)
 
 
 def moe_forward_exact(x, w_gate, routed, shared, top_k: int, *, n_shared: int = 0,

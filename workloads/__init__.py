@@ -47,6 +47,7 @@ TAG_LOGIT_BIAS = 3
 TAG_SELECT_BIAS = 4
 TAG_ROUTED = (10, 11, 12)   # W1, W3, W2 of routed expert e
 TAG_SHARED = (20, 21, 22)   # W1, W3, W2 of shared expert s
+TAG_DOUT = 30               # gradient of the layer output (backward inputs)
 X_CHUNK = 1024              # tokens per x stream
 
 
@@ -172,6 +173,12 @@ class Inputs:
 
     def x(self) -> np.ndarray:
         return self.x_rows(np.arange(self.cfg.T))
+
+    def dout(self) -> np.ndarray:
+        """Gradient of the layer output for the backward pass, [T, d] fp32
+        values (N(0, 1), rounded like the activations)."""
+        a = self._rng(TAG_DOUT).standard_normal((self.cfg.T, self.cfg.d), np.float32)
+        return self._act(a)
 
     # -- router parameters ----------------------------------------------
     def w_gate(self) -> np.ndarray:
