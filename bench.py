@@ -9,8 +9,9 @@ Prints one JSON line with tokens/s, activated TFLOP/s and the fraction of
 the bf16 matrix peak, per-stage times from HIP events recorded on the
 layer's stream during the timed steps, a roofline entry for the dominant
 kernel, the FP8 variant of the same layer (E4M3 expert GEMMs, its own
-stage times and roofline against the fp8 matrix peak), and the CPU oracle
-timed on a bounded token sample.
+stage times and roofline against the fp8 matrix peak), the layer backward on
+the same workload (stage times, matrix TFLOP/s, the roofline of its slowest
+GEMM stage), and the CPU oracle timed on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -220,6 +221,89 @@ def time_fp8(moe, cfg, d, steps, warmup, fpt):
     }
 
 
+BWD_KERNEL = {
+    "dh_routed": "gemm_bwd_kernel<0> (routed dy W2)",
+    "dh_shared": "gemm_bwd_kernel<0> (shared dy W2)",
+    "gateup_bwd_routed": "gemm_bf16_kernel<GATEUP_BWD> (routed)",
+    "gateup_bwd_shared": "gemm_bf16_kernel<GATEUP_BWD> (shared)",
+    "dx_routed": "gemm_bwd_kernel<1> (routed dA [W1; W3])",
+    "dx_shared": "gemm_bwd_kernel<1> (shared dA [W1; W3])",
+    "dw2_routed": "gemm_bwd_kernel<2> (routed dW2)",
+    "dw13_routed": "gemm_bwd_kernel<3> (routed dW1, dW3)",
+    "dw2_shared": "gemm_bwd_kernel<2> (shared dW2)",
+    "dw13_shared": "gemm_bwd_kernel<3> (shared dW1, dW3)",
+}
+
+
+def backward_stage_flops(cfg):
+    """Matrix FLOPs of each GEMM stage of the backward (the recomputed
+    gate/up included): R = T K routed rows, S = K_s I_s shared columns."""
+    R, T, d, I = cfg.T * cfg.top_k, cfg.T, cfg.d, cfg.inner
+    S = cfg.n_shared * cfg.shared_inner
+    return {"dh_routed": 2.0 * R * d * I, "dh_shared": 2.0 * T * d * S,
+            "gateup_bwd_routed": 4.0 * R * d * I, "gateup_bwd_shared": 4.0 * T * d * S,
+            "dx_routed": 4.0 * R * d * I, "dx_shared": 4.0 * T * d * S,
+            "dw2_routed": 2.0 * R * d * I, "dw13_routed": 4.0 * R * d * I,
+            "dw2_shared": 2.0 * T * d * S, "dw13_shared": 4.0 * T * d * S}
+
+
+def time_backward(moe, cfg, d, steps, warmup):
+    """The layer backward on the same workload: dout N(0, 1) in bf16, every
+    gradient written each step; stage times from HIP events on the stream."""
+    import torch
+    g = torch.Generator(device=d["x"].device).manual_seed(0)
+    dout = torch.randn(d["x"].shape, generator=g, device=d["x"].device).to(torch.bfloat16)
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner,
+                         cfg.n_shared, cfg.shared_inner, n_groups=cfg.n_groups,
+                         topk_groups=cfg.topk_groups, score=cfg.score,
+                         norm_topk=cfg.norm_topk, routed_scale=cfg.routed_scale)
+    ws = torch.empty(moe.backward_workspace_size(desc), dtype=torch.uint8,
+                     device=d["x"].device)
+    names = moe.backward_stage_names()
+    nst = len(names)
+    events = [moe.HipEvents(nst + 1) for _ in range(steps)]
+    grads = None
+
+    def step(ev=None):
+        nonlocal grads
+        grads = moe.moe_layer_backward(
+            d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k, dout,
+            score=cfg.score, norm_topk=cfg.norm_topk, n_groups=cfg.n_groups,
+            topk_groups=cfg.topk_groups, select_bias=d["select_bias"],
+            logit_bias=d["logit_bias"], routed_scale=cfg.routed_scale, workspace=ws,
+            grads=grads, trace_events=None if ev is None else ev.handles)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {n: sum(ev.elapsed_ms(i, i + 1) for ev in events) / steps
+                for i, n in enumerate(names)}
+    for ev in events:
+        ev.close()
+    flops = backward_stage_flops(cfg)
+    total = sum(flops.values())
+    dom = max(flops, key=lambda n: stage_ms[n])
+    ach = flops[dom] / (stage_ms[dom] / 1e3) / 1e12
+    return {
+        "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+        "expert_tflop_per_step": round(total / 1e12, 3),
+        "tflops": round(total / (ms / 1e3) / 1e12, 1),
+        "frac_bf16_peak": round(total / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_tflops": {k: round(flops[k] / (stage_ms[k] / 1e3) / 1e12, 1)
+                         for k in flops if stage_ms[k] > 0},
+        "roofline": {"kernel": BWD_KERNEL[dom], "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,6 +319,8 @@ def main():
                          "each timed call so that no weights stay in L2 / MALL")
     ap.add_argument("--reps", type=int, default=50,
                     help="calls timed one by one for the per-call statistics")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the layer backward on the same workload")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3) variant of the same workload")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -393,6 +479,11 @@ def main():
         log(f"[bench] fp8 variant: {args.steps} steps")
         fp8 = time_fp8(moe, cfg, d, args.steps, args.warmup, fpt)
 
+    bwd = None
+    if not args.no_backward and cfg.dtype == "bf16" and not args.cold_cache:
+        log(f"[bench] backward: {args.steps} steps")
+        bwd = time_backward(moe, cfg, d, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         n = min(args.cpu_tokens or (min(cfg.T, 512) if streaming else cfg.T), cfg.T)
@@ -425,6 +516,7 @@ def main():
         "attainable_bf16_tflops": {"value": round(attain, 1),
                                    "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
         "fp8": fp8,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -232,6 +232,23 @@ moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, const void* x,
                                 moe_ffn_grads_t d_shared, int32_t* topk_idx, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Number of kernel stages moe_layer_backward_traced brackets with events,
+ * and the name of stage i (NULL if out of range). */
+int32_t moe_layer_backward_stage_count(void);
+const char* moe_layer_backward_stage_name(int32_t i);
+
+/* moe_layer_backward, with hipEvent_t events[i] recorded on `stream` before
+ * stage i and events[n] after the last (n = backward stage count); `events`
+ * holds n + 1 created events (MOE_ERR_INVALID_ARG if n_events is smaller).
+ * Otherwise identical. */
+moe_status_t moe_layer_backward_traced(
+    const moe_layer_desc_t* desc, const void* x, const float* w_gate,
+    const float* logit_bias, const float* select_bias, moe_ffn_weights_t routed,
+    moe_ffn_weights_t shared, const void* dout, void* dx, float* dw_gate,
+    float* dlogit_bias, moe_ffn_grads_t d_routed, moe_ffn_grads_t d_shared, int32_t* topk_idx,
+    void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+    int32_t n_events);
+
 /* Weights to the FP8 layer's format: `src` [batch][rows][cols] (src_dtype
  * MOE_F32 or MOE_BF16, device) to E4M3 `codes` (same shape, one byte each)
  * and `scales` [batch][rows / 128][cols / 128]: each 128 x 128 block gets the

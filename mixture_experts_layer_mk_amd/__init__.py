@@ -6,7 +6,7 @@ C ABI of ``include/moe_layer.h``); this package is its Python binding.
 from ._lib import (MOE_BF16, MOE_FP8, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_INVALID_ARG,
                    MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_F32, MOE_OK,
                    HipEvents, MoeError, MoeLayerDesc, header_functions,
-                   backward_workspace_size, load_library, make_desc, moe_bias_update,
+                   backward_stage_names, backward_workspace_size, load_library, make_desc, moe_bias_update,
                    moe_layer_backward, moe_layer_forward,
                    quantize_fp8_blocks, strerror,
                    trace_stage_names, validate, workspace_layout,
@@ -16,7 +16,7 @@ __all__ = [
     "MOE_BF16", "MOE_FP8", "MOE_ERR_ALIAS", "MOE_ERR_HIP", "MOE_ERR_INVALID_ARG",
     "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE", "MOE_F32", "MOE_OK",
     "HipEvents", "MoeError", "MoeLayerDesc", "header_functions",
-    "backward_workspace_size", "load_library", "make_desc", "moe_bias_update",
+    "backward_stage_names", "backward_workspace_size", "load_library", "make_desc", "moe_bias_update",
     "moe_layer_backward", "moe_layer_forward",
     "quantize_fp8_blocks", "strerror",
     "trace_stage_names", "validate", "workspace_layout", "workspace_size",

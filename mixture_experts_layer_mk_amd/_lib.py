@@ -94,6 +94,13 @@ def load_library():
     lib.moe_layer_backward.argtypes = [D, P, P, P, P, FfnWeights, FfnWeights, P, P, P, P,
                                        FfnGrads, FfnGrads, P, P, ctypes.c_size_t, P]
     lib.moe_layer_backward.restype = ctypes.c_int
+    lib.moe_layer_backward_traced.argtypes = lib.moe_layer_backward.argtypes + [
+        ctypes.POINTER(P), ctypes.c_int32]
+    lib.moe_layer_backward_traced.restype = ctypes.c_int
+    lib.moe_layer_backward_stage_count.argtypes = []
+    lib.moe_layer_backward_stage_count.restype = ctypes.c_int32
+    lib.moe_layer_backward_stage_name.argtypes = [ctypes.c_int32]
+    lib.moe_layer_backward_stage_name.restype = ctypes.c_char_p
     lib.moe_quantize_fp8_blocks.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                             ctypes.c_int32, P, P, P]
     lib.moe_quantize_fp8_blocks.restype = ctypes.c_int
@@ -181,17 +188,25 @@ def backward_workspace_size(desc: MoeLayerDesc) -> int:
     return n.value
 
 
+def backward_stage_names() -> list:
+    lib = load_library()
+    return [lib.moe_layer_backward_stage_name(i).decode()
+            for i in range(lib.moe_layer_backward_stage_count())]
+
+
 def moe_layer_backward(x, W_gate, experts: Sequence, shared: Optional[Sequence], K: int,
                        dout, *, score: str = "softmax", norm_topk: bool = False,
                        n_groups: int = 1, topk_groups: int = 1, select_bias=None,
                        logit_bias=None, routed_scale: float = 1.0, workspace=None,
-                       stream=None, grads=None):
+                       stream=None, grads=None, trace_events=None):
     """Backward pass of the bf16 layer (``moe_layer_backward`` in the C ABI):
     gradients of sum(dout * out) for the forward on the same inputs, the
     expert choice held fixed.  Returns a dict: dx [T, d] bf16, dw_gate [E, d],
     dlogit_bias [E] (or None without a logit bias), routed = (dw1, dw3, dw2),
     shared = same or None (fp32), topk_idx [T, K] int32.  ``grads`` (a dict of
-    that form) may be passed to write into existing tensors."""
+    that form) may be passed to write into existing tensors; ``trace_events``
+    (n + 1 raw hipEvent_t handles, n = ``backward_stage_names()``) records
+    every stage boundary."""
     import torch
     lib = load_library()
     dev = x.device
@@ -261,11 +276,15 @@ def moe_layer_backward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
         g_s = FfnGrads(gs[0].data_ptr(), gs[1].data_ptr(), gs[2].data_ptr())
     else:
         g_s = FfnGrads(None, None, None)
-    st = lib.moe_layer_backward(
-        ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias), _ptr(select_bias),
-        ffn_r, ffn_s, _ptr(dout), _ptr(grads["dx"]), _ptr(grads["dw_gate"]),
-        _ptr(grads["dlogit_bias"]), g_r, g_s, _ptr(grads.get("topk_idx")),
-        workspace.data_ptr(), workspace.numel(), stream)
+    args = [ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias), _ptr(select_bias),
+            ffn_r, ffn_s, _ptr(dout), _ptr(grads["dx"]), _ptr(grads["dw_gate"]),
+            _ptr(grads["dlogit_bias"]), g_r, g_s, _ptr(grads.get("topk_idx")),
+            workspace.data_ptr(), workspace.numel(), stream]
+    if trace_events is None:
+        st = lib.moe_layer_backward(*args)
+    else:
+        arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
+        st = lib.moe_layer_backward_traced(*args, arr, len(trace_events))
     if st != MOE_OK:
         raise MoeError(st, strerror(st))
     return grads

@@ -18,6 +18,14 @@ const char* const kStageNames[kStages] = {
     "gemm_gateup_routed", "gemm_gateup_shared", "gemm_down_routed",
     "gemm_down_shared",  "combine"};
 
+// Stages of the backward pass (moe_layer_backward_traced).
+constexpr int kBwdStages = 13;
+const char* const kBwdStageNames[kBwdStages] = {
+    "route",          "dh_routed",      "dh_shared",   "gateup_bwd_routed",
+    "gateup_bwd_shared", "router_bwd",  "dx_routed",   "dx_shared",
+    "dx_combine",     "dw2_routed",     "dw13_routed", "dw2_shared",
+    "dw13_shared"};
+
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 // Bytes per element of x / out (bf16 for bf16 and FP8 layers) and of the
@@ -388,7 +396,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
                            const void* dout, void* dx, float* dw_gate, float* dlogit_bias,
                            moe_ffn_grads_t d_routed, moe_ffn_grads_t d_shared,
                            int32_t* topk_idx, void* workspace, size_t workspace_bytes,
-                           void* stream_ptr) {
+                           void* stream_ptr, void* const* events) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_layer_desc_t& d = *desc;
@@ -400,8 +408,12 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     return MOE_ERR_INVALID_ARG;
   if (d.T > 0 && (!x || !dout || !dx)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
   const int64_t I = d.inner, Is = d.shared_inner, Ks = d.n_shared, E = d.n_routed;
   if (d.T == 0) {   // no tokens: every parameter gradient is zero
+    if (!mark(0)) return MOE_ERR_HIP;
     hipError_t e = launch_fill_zero(dw_gate, E * d.d, s);
     if (e == hipSuccess && dlogit_bias) e = launch_fill_zero(dlogit_bias, E, s);
     if (e == hipSuccess) e = launch_fill_zero(d_routed.dw1, E * I * d.d, s);
@@ -410,6 +422,8 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw1, Ks * Is * d.d, s);
     if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw3, Ks * Is * d.d, s);
     if (e == hipSuccess && Ks > 0) e = launch_fill_zero(d_shared.dw2, Ks * Is * d.d, s);
+    for (int i = 1; i <= kBwdStages && e == hipSuccess; ++i)
+      if (!mark(i)) return MOE_ERR_HIP;
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   }
   const BwdLayout B = bwd_layout_of(d);
@@ -424,6 +438,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
   int32_t* idx = topk_idx ? topk_idx : static_cast<int32_t*>(at(L.topk_idx));
   float* gw = static_cast<float*>(at(L.topk_w));
+  if (!mark(0)) return MOE_ERR_HIP;
   auto no_mark = [](int) { return true; };
   st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, nullptr, s,
                       no_mark);
@@ -485,9 +500,11 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
 
   // 1. G = dy W2 of every row (before the gate weight)
   {
+    if (!mark(1)) return MOE_ERR_HIP;
     BwdGemmArgs g = rb;
     g.kind = 0; g.c = static_cast<float*>(at(B.g_r)); g.ldc = d.inner;
     MOE_CHECK(launch_gemm_bwd(g, s));
+    if (!mark(2)) return MOE_ERR_HIP;
     if (Ks > 0) {
       g = sb;
       g.kind = 0; g.c = static_cast<float*>(at(B.g_s)); g.ldc = (int)(Ks * Is);
@@ -496,6 +513,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   }
   // 2. gate/up recomputed with the SwiGLU backward: dA, g h, dg row sums
   {
+    if (!mark(3)) return MOE_ERR_HIP;
     GemmArgs g{};
     g.mode = 3; g.d = d.d; g.tiles = static_cast<const MTile*>(at(L.tiles));
     g.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); g.max_mtiles = L.max_mtiles;
@@ -508,6 +526,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     g.da = static_cast<bf16_t*>(at(B.da_r)); g.ldda = 2 * d.inner;
     g.dg_part = static_cast<float*>(at(B.dg_part)); g.n_part = B.n_part;
     MOE_CHECK(launch_gemm_bf16(g, s));
+    if (!mark(4)) return MOE_ERR_HIP;
     if (Ks > 0) {
       g.shared = true; g.a_rows = nullptr;
       g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
@@ -522,6 +541,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   // 3. router: logits again (partial sums), scores, dg, dl, logit-bias and
   // gate gradients
   {
+    if (!mark(5)) return MOE_ERR_HIP;
     LogitsArgs la{};
     la.x = xb; la.planes = static_cast<const bf16_t*>(at(L.planes));
     la.T = d.T; la.d = d.d; la.E = d.n_routed; la.ep = L.ep; la.ds = L.ds;
@@ -532,31 +552,41 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   }
   // 4. input gradient of every row and of the shared experts, then dx
   {
+    if (!mark(6)) return MOE_ERR_HIP;
     BwdGemmArgs g = rb;
     g.kind = 1; g.c = static_cast<float*>(at(B.dx_rows)); g.ldc = d.d;
     MOE_CHECK(launch_gemm_bwd(g, s));
+    if (!mark(7)) return MOE_ERR_HIP;
     if (Ks > 0) {
       g = sb;
       g.kind = 1; g.c = static_cast<float*>(at(B.dx_s)); g.ldc = d.d;
       MOE_CHECK(launch_gemm_bwd(g, s));
     }
+    if (!mark(8)) return MOE_ERR_HIP;
     MOE_CHECK(launch_dx_combine(aux, s));
   }
   // 5. weight gradients
   {
+    if (!mark(9)) return MOE_ERR_HIP;
     BwdGemmArgs g = rb;
     g.kind = 2;
     MOE_CHECK(launch_gemm_bwd(g, s));
+    if (!mark(10)) return MOE_ERR_HIP;
     g.kind = 3;
     MOE_CHECK(launch_gemm_bwd(g, s));
+    g = sb;
+    if (!mark(11)) return MOE_ERR_HIP;
     if (Ks > 0) {
-      g = sb;
       g.kind = 2;
       MOE_CHECK(launch_gemm_bwd(g, s));
+    }
+    if (!mark(12)) return MOE_ERR_HIP;
+    if (Ks > 0) {
       g.kind = 3;
       MOE_CHECK(launch_gemm_bwd(g, s));
     }
   }
+  if (!mark(13)) return MOE_ERR_HIP;
 #undef MOE_CHECK
   return MOE_OK;
 }
@@ -650,7 +680,28 @@ moe_status_t moe_layer_backward(const moe_layer_desc_t* desc, const void* x,
                                 size_t workspace_bytes, void* stream) {
   return backward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, dout, dx,
                        dw_gate, dlogit_bias, d_routed, d_shared, topk_idx, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, nullptr);
+}
+
+int32_t moe_layer_backward_stage_count(void) { return kBwdStages; }
+
+const char* moe_layer_backward_stage_name(int32_t i) {
+  return (i >= 0 && i < kBwdStages) ? kBwdStageNames[i] : nullptr;
+}
+
+moe_status_t moe_layer_backward_traced(
+    const moe_layer_desc_t* desc, const void* x, const float* w_gate,
+    const float* logit_bias, const float* select_bias, moe_ffn_weights_t routed,
+    moe_ffn_weights_t shared, const void* dout, void* dx, float* dw_gate,
+    float* dlogit_bias, moe_ffn_grads_t d_routed, moe_ffn_grads_t d_shared, int32_t* topk_idx,
+    void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+    int32_t n_events) {
+  if (!events || n_events < kBwdStages + 1) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i <= kBwdStages; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return backward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, dout, dx,
+                       dw_gate, dlogit_bias, d_routed, d_shared, topk_idx, workspace,
+                       workspace_bytes, stream, events);
 }
 
 moe_status_t moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t batch,
