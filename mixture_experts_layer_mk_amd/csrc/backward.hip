@@ -223,12 +223,28 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
   }
 }
 
+// One workgroup per row, 16-byte chunks.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* src, const int32_t* idx,
+                                                          int cols, bf16_t* dst) {
+  const int64_t r = blockIdx.x;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (size_t)idx[r] * cols);
+  uint4* d = reinterpret_cast<uint4*>(dst + (size_t)r * cols);
+  for (int c = threadIdx.x; c < cols / 8; c += 256) d[c] = s[c];
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0.f;
 }
 
 }  // namespace
+
+hipError_t launch_gather_rows(const bf16_t* src, const int32_t* idx, int64_t n, int cols,
+                              bf16_t* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)n), dim3(256), 0, s, src, idx, cols, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

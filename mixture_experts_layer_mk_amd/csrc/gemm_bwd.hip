@@ -61,6 +61,7 @@ struct TileDesc {
   int grp;              // expert (routed) or shared expert / 0
   int row0;             // KIND 0/1: first row of the tile (expert-contiguous)
   int koff;             // KIND 2/3 routed: first row of the expert
+  int kbeg, split;      // KIND 2/3: first k-row of this split, split index
 };
 
 template <int KIND>
@@ -81,17 +82,26 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
     t.n0 = (nt % per) * BN;
     t.nval = (KIND == 0) ? a.inner : a.d;
     t.K = (KIND == 0) ? a.d : (a.shared ? 2 * a.inner * a.n_experts : 2 * a.inner);
-    t.koff = 0;
+    t.koff = 0; t.kbeg = 0; t.split = 0;
   } else {
     const int M = (KIND == 2) ? a.d : 2 * a.inner;
     const int N = (KIND == 2) ? a.inner : a.d;
     const int mdim = (M + TM - 1) / TM, ndim = (N + BN - 1) / BN;
-    t.grp = L / (mdim * ndim);
-    const int rem = L % (mdim * ndim);
+    const int per_split = a.n_experts * mdim * ndim;
+    t.split = L / per_split;
+    const int L2 = L % per_split;
+    t.grp = L2 / (mdim * ndim);
+    const int rem = L2 % (mdim * ndim);
     t.m0 = (rem / ndim) * TM; t.n0 = (rem % ndim) * BN;
     t.mval = M; t.nval = N;
-    if (a.shared) { t.koff = 0; t.K = a.T; }
-    else { t.koff = a.offsets[t.grp]; t.K = a.offsets[t.grp + 1] - t.koff; }
+    int k_all;
+    if (a.shared) { t.koff = 0; k_all = a.T; }
+    else { t.koff = a.offsets[t.grp]; k_all = a.offsets[t.grp + 1] - t.koff; }
+    // k-rows [kbeg, kbeg + K) of the group: split s of `splits` takes a
+    // range of whole k-blocks
+    const int kc = ((k_all + a.splits * TK - 1) / (a.splits * TK)) * TK;
+    t.kbeg = min(t.split * kc, k_all);
+    t.K = min(kc, k_all - t.kbeg);
     t.row0 = 0;
   }
   return true;
@@ -113,84 +123,85 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
 
   // ---- k-major A (KIND 0, 1): 256 rows x 8 chunks per stage ----
   // Lane slot: LDS row (wave * 8 + j) * 8 + lr, chunk (lane & 7) after the
-  // row swizzle, as in the forward kernels.
+  // row swizzle, as in the forward kernels.  Element offsets from the
+  // operand's base (32 bits: validation bounds every operand below 2^32
+  // elements); each stage adds k0.
   const int lr = lane >> 3;
   const int cg0 = (lane & 7) ^ lr, cg1 = cg0 ^ 1;
-  const bf16_t* arow[8];
+  const bf16_t* abase = nullptr;
+  uint32_t aoff[8];
   if constexpr (AK) {
+    int ld;
+    if (KIND == 0) { abase = a.shared ? a.dy : a.dyp; ld = a.d; }
+    else { abase = a.da; ld = a.ldda; }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = wave * 8 + j;
       const int r = min(blk * 8 + lr, t.mval - 1);
-      const int row = t.row0 + r;
-      const bf16_t* p;
-      if (KIND == 0) {
-        const int tok = a.shared ? row : a.row_src[row];
-        p = a.dy + (size_t)tok * a.d;
-      } else {
-        p = a.da + (size_t)row * a.ldda;
-      }
-      arow[j] = p + ((blk & 1) ? cg1 : cg0) * 8;
+      aoff[j] = (uint32_t)(t.row0 + r) * (uint32_t)ld + ((blk & 1) ? cg1 : cg0) * 8;
     }
   }
 
   // ---- mn-major operands: 64 k-rows x 32 chunks per stage ----
-  // Lane slot: k-row 2 (wave * 8 + j) + (lane >> 5), chunk (lane & 31).
+  // Lane slot: k-row kr_j = 2 (wave * 8 + j) + (lane >> 5), chunk (lane & 31),
+  // which holds global chunk (lane & 31) ^ swz_mn(kr_j) of that row (the
+  // tile's first chunk past the operand's last column: never stored).  The
+  // offset of the lane's chunk inside the stage's first k-row is fixed; a
+  // stage adds its uniform row base, and k-rows past the end read zeros.
   const int ks = lane >> 5, cs = lane & 31;
-  // global pointer of k-row k (absolute in [0, K)) of operand A / B, at this
-  // lane's chunk, or the zero row when k is past the end
-  auto a_row = [&](int k) -> const bf16_t* {
-    const int kr = k & (TK - 1);
+  auto mn_off = [&](int j, int col0, int extent, int ld) -> uint32_t {
+    const int kr = 2 * (wave * 8 + j) + ks;
     int c = cs ^ swz_mn(kr);
-    if (t.m0 + c * 8 >= t.mval) c = 0;
-    if (k >= t.K) return a.zero + cs * 8;
-    if (KIND == 2) {
-      const int tok = a.shared ? k : a.row_src[t.koff + k];
-      return a.dy + (size_t)tok * a.d + t.m0 + c * 8;
-    } else {   // KIND 3
-      const int row = t.koff + k;
-      const size_t off = a.shared ? (size_t)t.grp * 2 * a.inner : 0;
-      return a.da + (size_t)row * a.ldda + off + t.m0 + c * 8;
-    }
+    if (col0 + c * 8 >= extent) c = 0;
+    return (uint32_t)kr * (uint32_t)ld + (uint32_t)(col0 + c * 8);
   };
-  auto b_row = [&](int k) -> const bf16_t* {
-    const int kr = k & (TK - 1);
-    int c = cs ^ swz_mn(kr);
-    if (t.n0 + c * 8 >= t.nval) c = 0;
-    if (k >= t.K) return a.zero + cs * 8;
-    const int n = t.n0 + c * 8;
-    if (KIND == 0) {            // W2 of the group: [d][inner]
-      return a.w2 + ((size_t)t.grp * a.d + k) * a.inner + n;
-    } else if (KIND == 1) {     // W1 / W3 rows along k
+  uint32_t moff_a[8], moff_b[8];
+  int lda_mn = 0, ldb_mn;
+  if (KIND == 0) ldb_mn = a.inner;
+  else if (KIND == 1) ldb_mn = a.d;
+  else if (KIND == 2) { lda_mn = a.d; ldb_mn = a.ldhg; }
+  else { lda_mn = a.ldda; ldb_mn = a.d; }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (!AK) moff_a[j] = mn_off(j, t.m0, t.mval, lda_mn);
+    moff_b[j] = mn_off(j, t.n0, t.nval, ldb_mn);
+  }
+  // uniform base of the stage's first k-row (k0 relative to the tile's k range)
+  auto a_stage = [&](int k0) -> const bf16_t* {
+    const size_t row = (size_t)t.koff + t.kbeg + k0;
+    if (KIND == 2) return (a.shared ? a.dy : a.dyp) + row * a.d;
+    return a.da + row * a.ldda + (a.shared ? (size_t)t.grp * 2 * a.inner : 0);   // KIND 3
+  };
+  auto b_stage = [&](int k0) -> const bf16_t* {
+    if (KIND == 0) return a.w2 + ((size_t)t.grp * a.d + k0) * a.inner;
+    if (KIND == 1) {
       const int per = 2 * a.inner;
-      const int e = a.shared ? k / per : t.grp;
-      const int r = a.shared ? k % per : k;
+      const int e = a.shared ? k0 / per : t.grp;
+      const int r = a.shared ? k0 % per : k0;
       const bf16_t* w = (r < a.inner) ? a.w1 : a.w3;
-      return w + ((size_t)e * a.inner + (r % a.inner)) * a.d + n;
-    } else if (KIND == 2) {     // g h rows
-      const int row = t.koff + k;
-      const size_t off = a.shared ? (size_t)t.grp * a.inner : 0;
-      return a.hg + (size_t)row * a.ldhg + off + n;
-    } else {                    // token rows of x
-      const int tok = a.shared ? k : a.row_src[t.koff + k];
-      return a.x + (size_t)tok * a.d + n;
+      return w + ((size_t)e * a.inner + (r % a.inner)) * a.d;
     }
+    const size_t row = (size_t)t.koff + t.kbeg + k0;
+    if (KIND == 2) return a.hg + row * a.ldhg + (a.shared ? (size_t)t.grp * a.inner : 0);
+    return (a.shared ? a.x : a.xp) + row * a.d;                                   // KIND 3
   };
 
   auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
     const int k0 = kb * TK;
+    const bf16_t* zr = a.zero + cs * 8;
+    const bf16_t* as = nullptr;
+    if constexpr (!AK) as = a_stage(k0);
+    const bf16_t* bs = b_stage(k0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = wave * 8 + j;
-      if constexpr (AK) {
-        __builtin_amdgcn_global_load_lds((const glb_void*)(arow[j] + k0),
-                                         (lds_void*)&Ab[blk * 64], 16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds((const glb_void*)a_row(k0 + 2 * blk + ks),
-                                         (lds_void*)&Ab[blk * 64], 16, 0, 0);
-      }
-      __builtin_amdgcn_global_load_lds((const glb_void*)b_row(k0 + 2 * blk + ks),
-                                       (lds_void*)&Bb[blk * 64], 16, 0, 0);
+      const bool live = k0 + 2 * blk + ks < t.K;   // k-major A: K is whole stages
+      const bf16_t* ga;
+      if constexpr (AK) ga = abase + aoff[j] + k0;
+      else ga = live ? as + moff_a[j] : zr;
+      __builtin_amdgcn_global_load_lds((const glb_void*)ga, (lds_void*)&Ab[blk * 64], 16, 0, 0);
+      const bf16_t* gb = live ? bs + moff_b[j] : zr;
+      __builtin_amdgcn_global_load_lds((const glb_void*)gb, (lds_void*)&Bb[blk * 64], 16, 0, 0);
     }
   };
 
@@ -277,6 +288,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
       crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
     } else if (KIND == 1) {
       crow = a.c + (size_t)(t.row0 + m) * a.ldc;
+    } else if (a.splits > 1) {   // partial sums [split][group][M][N], reduced later
+      crow = a.part + (((size_t)t.split * a.n_experts + t.grp) * t.mval + m) * t.nval;
     } else if (KIND == 2) {
       crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
     } else {
@@ -299,6 +312,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   }
 }
 
+// Sum of the split-k partials of a weight gradient, splits in order, into
+// the gradient's own layout (4 consecutive elements per thread).
+template <int KIND>
+__global__ __launch_bounds__(256) void split_reduce_kernel(BwdGemmArgs a) {
+  const int M = (KIND == 2) ? a.d : 2 * a.inner;
+  const int N = (KIND == 2) ? a.inner : a.d;
+  const int64_t per = (int64_t)M * N;
+  const int64_t n = (int64_t)a.n_experts * per;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  float4 v = *reinterpret_cast<const float4*>(a.part + i);
+  for (int sp = 1; sp < a.splits; ++sp) {
+    const float4 w = *reinterpret_cast<const float4*>(a.part + (size_t)sp * n + i);
+    v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+  }
+  const int64_t g = i / per, r = i % per;
+  const int m = (int)(r / N), c = (int)(r % N);
+  float* dst;
+  if (KIND == 2) dst = a.dw2 + ((size_t)g * a.d + m) * a.inner + c;
+  else dst = (m < a.inner) ? a.dw1 + ((size_t)g * a.inner + m) * a.d + c
+                           : a.dw3 + ((size_t)g * a.inner + (m - a.inner)) * a.d + c;
+  *reinterpret_cast<float4*>(dst) = v;
+}
+
 template <int KIND>
 void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
   int grid;
@@ -310,10 +347,17 @@ void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
   } else {
     const int M = (KIND == 2) ? a.d : 2 * a.inner;
     const int N = (KIND == 2) ? a.inner : a.d;
-    grid = a.n_experts * ((M + TM - 1) / TM) * ((N + BN - 1) / BN);
+    grid = a.splits * a.n_experts * ((M + TM - 1) / TM) * ((N + BN - 1) / BN);
   }
   if (grid <= 0) return;
   hipLaunchKernelGGL(gemm_bwd_kernel<KIND>, dim3(grid), dim3(256), 0, s, a);
+  if ((KIND == 2 || KIND == 3) && a.splits > 1) {
+    const int M = (KIND == 2) ? a.d : 2 * a.inner;
+    const int N = (KIND == 2) ? a.inner : a.d;
+    const int64_t n = (int64_t)a.n_experts * M * N;
+    hipLaunchKernelGGL(split_reduce_kernel<KIND>, dim3((unsigned)((n / 4 + 255) / 256)),
+                       dim3(256), 0, s, a);
+  }
 }
 
 }  // namespace

@@ -353,9 +353,19 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
 struct BwdLayout {
   Layout f;
   int64_t plog, g_r, g_s, da_r, da_s, dx_rows, dx_s, row_g, dg_part, dg, dl, dwg_part, zero,
-      total;
+      dyp, xp, part, total;
   int32_t n_part, n_chunk;
+  int32_t splits2, splits3;   // k splits of the shared dW2 and dW1/dW3 GEMMs
 };
+
+// Split the shared experts' weight gradients (k = all T tokens) along k
+// until the grid holds about two tiles per CU, keeping >= 4 k-blocks per
+// split.
+int32_t shared_wgrad_splits(int64_t tiles, int64_t T) {
+  int64_t s = (512 + tiles - 1) / std::max<int64_t>(tiles, 1);
+  s = std::min<int64_t>(s, std::max<int64_t>(T / 256, 1));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, 16));
+}
 
 constexpr int kGateGradChunks = 16;
 
@@ -386,6 +396,19 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   const int64_t colsum = (int64_t)((d.T + 255) / 256) * d.n_routed;
   B.dwg_part = take(std::max<int64_t>((int64_t)B.n_chunk * d.n_routed * d.d, colsum) * 4);
   B.zero = take(1024);
+  B.dyp = take(TK * d.d * 2);
+  B.xp = take(TK * d.d * 2);
+  B.splits2 = B.splits3 = 1;
+  if (d.n_shared > 0) {
+    const int64_t Is = d.shared_inner, Ks = d.n_shared;
+    const int64_t t2 = Ks * ((d.d + 255) / 256) * ((Is + 255) / 256);
+    const int64_t t3 = Ks * ((2 * Is + 255) / 256) * ((d.d + 255) / 256);
+    B.splits2 = shared_wgrad_splits(t2, d.T);
+    B.splits3 = shared_wgrad_splits(t3, d.T);
+  }
+  const int64_t ps = std::max<int64_t>(B.splits2 > 1 ? B.splits2 : 0,
+                                       B.splits3 > 1 ? B.splits3 : 0);
+  B.part = ps > 0 ? take(ps * (int64_t)d.n_shared * 2 * d.shared_inner * d.d * 4) : -1;
   B.total = off;
   return B;
 }
@@ -473,6 +496,10 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   aux.dx = static_cast<bf16_t*>(dx);
   aux.zero = static_cast<bf16_t*>(at(B.zero)); aux.n_zero = 512;
   MOE_CHECK(launch_bwd_prep(aux, s));
+  // dy and x in the rows' order (expert-contiguous), read by the routed GEMMs
+  const int64_t TKr = (int64_t)d.T * d.top_k;
+  MOE_CHECK(launch_gather_rows(dyb, row_src, TKr, d.d, static_cast<bf16_t*>(at(B.dyp)), s));
+  MOE_CHECK(launch_gather_rows(xb, row_src, TKr, d.d, static_cast<bf16_t*>(at(B.xp)), s));
 
   BwdGemmArgs rb{};
   rb.T = d.T; rb.d = d.d; rb.inner = d.inner; rb.n_experts = d.n_routed; rb.shared = false;
@@ -480,6 +507,9 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   rb.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); rb.max_mtiles = L.max_mtiles;
   rb.offsets = static_cast<const int32_t*>(at(L.offsets)); rb.row_src = row_src;
   rb.dy = dyb; rb.x = xb;
+  rb.dyp = static_cast<const bf16_t*>(at(B.dyp));
+  rb.xp = static_cast<const bf16_t*>(at(B.xp));
+  rb.splits = 1; rb.part = nullptr;
   rb.w1 = static_cast<const bf16_t*>(routed.w1);
   rb.w3 = static_cast<const bf16_t*>(routed.w3);
   rb.w2 = static_cast<const bf16_t*>(routed.w2);
@@ -575,14 +605,15 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     g.kind = 3;
     MOE_CHECK(launch_gemm_bwd(g, s));
     g = sb;
+    g.part = static_cast<float*>(at(B.part));
     if (!mark(11)) return MOE_ERR_HIP;
     if (Ks > 0) {
-      g.kind = 2;
+      g.kind = 2; g.splits = B.splits2;
       MOE_CHECK(launch_gemm_bwd(g, s));
     }
     if (!mark(12)) return MOE_ERR_HIP;
     if (Ks > 0) {
-      g.kind = 3;
+      g.kind = 3; g.splits = B.splits3;
       MOE_CHECK(launch_gemm_bwd(g, s));
     }
   }
