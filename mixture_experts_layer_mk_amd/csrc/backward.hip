@@ -168,10 +168,15 @@ __global__ __launch_bounds__(256) void gate_grad_part_kernel(BwdAuxArgs a) {
     __syncthreads();
     if (j < a.d) {
       const int n = min(GG_T, t1 - tb);
-      for (int tt = 0; tt < n; ++tt) {
-        const float xv = bf16_to_f32(a.x[(size_t)(tb + tt) * a.d + j]);
+      for (int t8 = 0; t8 < n; t8 += 8) {
+        float xv[8];      // eight token loads in flight (zeros past the chunk)
 #pragma unroll
-        for (int i = 0; i < GG_E; ++i) acc[i] = fmaf(sdl[tt][i], xv, acc[i]);
+        for (int q = 0; q < 8; ++q)
+          xv[q] = (t8 + q < n) ? bf16_to_f32(a.x[(size_t)(tb + t8 + q) * a.d + j]) : 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int i = 0; i < GG_E; ++i) acc[i] = fmaf(sdl[t8 + q][i], xv[q], acc[i]);
       }
     }
   }
@@ -192,8 +197,10 @@ __global__ __launch_bounds__(256) void gate_grad_sum_kernel(BwdAuxArgs a) {
 }
 
 // dx = RNE(dy + dx_shared + sum_k dx_rows[slot_row[t][k]] + dl Wg): thread =
-// column j, DX_T tokens per workgroup, their dl rows staged in LDS.
-constexpr int DX_T = 8;
+// column j, DX_T tokens per workgroup.  The router term first (each Wg
+// element read once per workgroup, the tokens' dl rows staged in LDS), then
+// the row sums, four tokens' loads at a time.
+constexpr int DX_T = 16;
 __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
   __shared__ float sdl[DX_T][MAX_EXPERTS];
   const int t0 = blockIdx.x * DX_T;
@@ -213,23 +220,34 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
 #pragma unroll
     for (int tt = 0; tt < DX_T; ++tt) r[tt] = fmaf(sdl[tt][e], w, r[tt]);
   }
-  for (int tt = 0; tt < nt; ++tt) {
-    const int t = t0 + tt;
-    float v = bf16_to_f32(a.dy[(size_t)t * a.d + j]);
-    if (a.dx_shared) v += a.dx_shared[(size_t)t * a.d + j];
-    for (int k = 0; k < a.K; ++k) v += a.dx_rows[(size_t)a.slot_row[(size_t)t * a.K + k] * a.d + j];
-    v += r[tt];
-    a.dx[(size_t)t * a.d + j] = f32_to_bf16(v);
+#pragma unroll
+  for (int t4 = 0; t4 < DX_T; t4 += 4) {
+    float v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + t4 + q;
+      v[q] = 0.f;
+      if (t4 + q >= nt) continue;
+      v[q] = bf16_to_f32(a.dy[(size_t)t * a.d + j]);
+      if (a.dx_shared) v[q] += a.dx_shared[(size_t)t * a.d + j];
+    }
+    for (int k = 0; k < a.K; ++k) {
+      float w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + t4 + q;
+        w[q] = (t4 + q < nt)
+                   ? a.dx_rows[(size_t)a.slot_row[(size_t)t * a.K + k] * a.d + j] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] += w[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + t4 + q;
+      if (t4 + q < nt) a.dx[(size_t)t * a.d + j] = f32_to_bf16(v[q] + r[t4 + q]);
+    }
   }
-}
-
-// One workgroup per row, 16-byte chunks.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* src, const int32_t* idx,
-                                                          int cols, bf16_t* dst) {
-  const int64_t r = blockIdx.x;
-  const uint4* s = reinterpret_cast<const uint4*>(src + (size_t)idx[r] * cols);
-  uint4* d = reinterpret_cast<uint4*>(dst + (size_t)r * cols);
-  for (int c = threadIdx.x; c < cols / 8; c += 256) d[c] = s[c];
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
@@ -238,13 +256,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* p, int64_t n) {
 }
 
 }  // namespace
-
-hipError_t launch_gather_rows(const bf16_t* src, const int32_t* idx, int64_t n, int cols,
-                              bf16_t* dst, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)n), dim3(256), 0, s, src, idx, cols, dst);
-  return hipGetLastError();
-}
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

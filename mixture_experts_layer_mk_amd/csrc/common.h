@@ -173,7 +173,6 @@ struct BwdGemmArgs {
   const int32_t* row_src;           // routed: token of each row
   const bf16_t* dy;                 // [T][d]
   const bf16_t* x;                  // [T][d]
-  const bf16_t* dyp; const bf16_t* xp;   // routed: dy and x gathered to the rows [T K][d]
   const bf16_t* w1; const bf16_t* w3; const bf16_t* w2;   // the group's weights
   const bf16_t* da; int ldda;       // [rows][2 inner] (shared: per expert blocks)
   const bf16_t* hg; int ldhg;       // [rows][inner] g h (shared: per expert blocks)
@@ -211,9 +210,6 @@ hipError_t launch_router_bwd(const BwdAuxArgs& a, hipStream_t s);    // dg, dl, 
 hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s);     // dw_gate
 hipError_t launch_dx_combine(const BwdAuxArgs& a, hipStream_t s);    // dx
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-// dst[r] = src[idx[r]] for rows r < n (bf16 rows of `cols`, a multiple of 8).
-hipError_t launch_gather_rows(const bf16_t* src, const int32_t* idx, int64_t n, int cols,
-                              bf16_t* dst, hipStream_t s);
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s);
 
 // E4M3 quantisation with power-of-two scales: rows of `src` [R][C] (bf16 or

@@ -64,14 +64,14 @@ struct TileDesc {
   int kbeg, split;      // KIND 2/3: first k-row of this split, split index
 };
 
-template <int KIND>
+template <int KIND, bool SH>
 __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   if (KIND == 0 || KIND == 1) {
     const int per = (KIND == 0) ? (a.inner + BN - 1) / BN : (a.d + BN - 1) / BN;
-    const int ndim = (KIND == 0 && a.shared) ? per * a.n_experts : per;
+    const int ndim = (KIND == 0 && SH) ? per * a.n_experts : per;
     const int mt = L / ndim, nt = L % ndim;
-    if (!a.shared) {
+    if (!SH) {
       if (mt >= *a.n_tiles) return false;
       const MTile m = a.tiles[mt];
       t.row0 = m.row0; t.mval = m.rows; t.grp = m.expert;
@@ -81,7 +81,7 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
     t.m0 = 0;
     t.n0 = (nt % per) * BN;
     t.nval = (KIND == 0) ? a.inner : a.d;
-    t.K = (KIND == 0) ? a.d : (a.shared ? 2 * a.inner * a.n_experts : 2 * a.inner);
+    t.K = (KIND == 0) ? a.d : (SH ? 2 * a.inner * a.n_experts : 2 * a.inner);
     t.koff = 0; t.kbeg = 0; t.split = 0;
   } else {
     const int M = (KIND == 2) ? a.d : 2 * a.inner;
@@ -95,7 +95,7 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
     t.m0 = (rem / ndim) * TM; t.n0 = (rem % ndim) * BN;
     t.mval = M; t.nval = N;
     int k_all;
-    if (a.shared) { t.koff = 0; k_all = a.T; }
+    if (SH) { t.koff = 0; k_all = a.T; }
     else { t.koff = a.offsets[t.grp]; k_all = a.offsets[t.grp + 1] - t.koff; }
     // k-rows [kbeg, kbeg + K) of the group: split s of `splits` takes a
     // range of whole k-blocks
@@ -107,13 +107,13 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
   return true;
 }
 
-template <int KIND>
+template <int KIND, bool SH>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   __shared__ u32x4 As0[2048], As1[2048];   // 32 KB each: 256 x 8 or 64 x 32 chunks
   __shared__ u32x4 Bs0[2048], Bs1[2048];
 
   TileDesc t;
-  if (!decode<KIND>(a, t)) return;
+  if (!decode<KIND, SH>(a, t)) return;
 
   constexpr bool AK = (KIND == 0 || KIND == 1);   // A k-major; B is always mn-major
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,13 +132,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   uint32_t aoff[8];
   if constexpr (AK) {
     int ld;
-    if (KIND == 0) { abase = a.shared ? a.dy : a.dyp; ld = a.d; }
+    if (KIND == 0) { abase = a.dy; ld = a.d; }
     else { abase = a.da; ld = a.ldda; }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int blk = wave * 8 + j;
       const int r = min(blk * 8 + lr, t.mval - 1);
-      aoff[j] = (uint32_t)(t.row0 + r) * (uint32_t)ld + ((blk & 1) ? cg1 : cg0) * 8;
+      // routed dy rows: the row's token (a gather resolved once per tile)
+      const int row = (KIND == 0 && !SH) ? a.row_src[t.row0 + r] : t.row0 + r;
+      aoff[j] = (uint32_t)row * (uint32_t)ld + ((blk & 1) ? cg1 : cg0) * 8;
     }
   }
 
@@ -161,29 +163,45 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   else if (KIND == 1) ldb_mn = a.d;
   else if (KIND == 2) { lda_mn = a.d; ldb_mn = a.ldhg; }
   else { lda_mn = a.ldda; ldb_mn = a.d; }
+  // Routed weight gradients read one operand's k-rows from token rows (dy
+  // for KIND 2's A, x for KIND 3's B): that operand's offsets hold only the
+  // column part, and the tokens of the next stage's k-rows are loaded one
+  // stage ahead (the wait before each stage's barrier covers them).
+  constexpr bool gath = (KIND == 2 || KIND == 3) && !SH;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if constexpr (!AK) moff_a[j] = mn_off(j, t.m0, t.mval, lda_mn);
-    moff_b[j] = mn_off(j, t.n0, t.nval, ldb_mn);
+    if constexpr (!AK) moff_a[j] = mn_off(j, t.m0, t.mval, (KIND == 2 && gath) ? 0 : lda_mn);
+    moff_b[j] = mn_off(j, t.n0, t.nval, (KIND == 3 && gath) ? 0 : ldb_mn);
+  }
+  int tok[8];
+  auto load_tokens = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = kb * TK + 2 * (wave * 8 + j) + ks;
+      tok[j] = (k < t.K) ? a.row_src[t.koff + t.kbeg + k] : 0;
+    }
+  };
+  if constexpr (gath) {
+    if (nk > 0) load_tokens(0);
   }
   // uniform base of the stage's first k-row (k0 relative to the tile's k range)
   auto a_stage = [&](int k0) -> const bf16_t* {
     const size_t row = (size_t)t.koff + t.kbeg + k0;
-    if (KIND == 2) return (a.shared ? a.dy : a.dyp) + row * a.d;
-    return a.da + row * a.ldda + (a.shared ? (size_t)t.grp * 2 * a.inner : 0);   // KIND 3
+    if (KIND == 2) return SH ? a.dy + row * a.d : a.dy;     // routed: gathered
+    return a.da + row * a.ldda + (SH ? (size_t)t.grp * 2 * a.inner : 0);   // KIND 3
   };
   auto b_stage = [&](int k0) -> const bf16_t* {
     if (KIND == 0) return a.w2 + ((size_t)t.grp * a.d + k0) * a.inner;
     if (KIND == 1) {
       const int per = 2 * a.inner;
-      const int e = a.shared ? k0 / per : t.grp;
-      const int r = a.shared ? k0 % per : k0;
+      const int e = SH ? k0 / per : t.grp;
+      const int r = SH ? k0 % per : k0;
       const bf16_t* w = (r < a.inner) ? a.w1 : a.w3;
       return w + ((size_t)e * a.inner + (r % a.inner)) * a.d;
     }
     const size_t row = (size_t)t.koff + t.kbeg + k0;
-    if (KIND == 2) return a.hg + row * a.ldhg + (a.shared ? (size_t)t.grp * a.inner : 0);
-    return (a.shared ? a.x : a.xp) + row * a.d;                                   // KIND 3
+    if (KIND == 2) return a.hg + row * a.ldhg + (SH ? (size_t)t.grp * a.inner : 0);
+    return SH ? a.x + row * a.d : a.x;                      // KIND 3; routed: gathered
   };
 
   auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
@@ -196,13 +214,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
     for (int j = 0; j < 8; ++j) {
       const int blk = wave * 8 + j;
       const bool live = k0 + 2 * blk + ks < t.K;   // k-major A: K is whole stages
+      const uint32_t trow = (uint32_t)tok[j] * (uint32_t)a.d;
       const bf16_t* ga;
       if constexpr (AK) ga = abase + aoff[j] + k0;
-      else ga = live ? as + moff_a[j] : zr;
+      else ga = live ? as + moff_a[j] + ((KIND == 2 && gath) ? trow : 0u) : zr;
       __builtin_amdgcn_global_load_lds((const glb_void*)ga, (lds_void*)&Ab[blk * 64], 16, 0, 0);
-      const bf16_t* gb = live ? bs + moff_b[j] : zr;
+      const bf16_t* gb = live ? bs + moff_b[j] + ((KIND == 3 && gath) ? trow : 0u) : zr;
       __builtin_amdgcn_global_load_lds((const glb_void*)gb, (lds_void*)&Bb[blk * 64], 16, 0, 0);
     }
+    if constexpr (gath) load_tokens(min(kb + 1, nk - 1));    // the next stage issued
   };
 
   f32x16 acc[4][4];
@@ -284,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
     if (m >= t.mval) continue;
     float* crow;
     if (KIND == 0) {
-      const size_t col = a.shared ? (size_t)t.grp * a.inner : 0;
+      const size_t col = SH ? (size_t)t.grp * a.inner : 0;
       crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
     } else if (KIND == 1) {
       crow = a.c + (size_t)(t.row0 + m) * a.ldc;
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(BwdGemmArgs a) {
   *reinterpret_cast<float4*>(dst) = v;
 }
 
-template <int KIND>
+template <int KIND, bool SH>
 void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
   int grid;
   if (KIND == 0 || KIND == 1) {
@@ -350,7 +370,7 @@ void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
     grid = a.splits * a.n_experts * ((M + TM - 1) / TM) * ((N + BN - 1) / BN);
   }
   if (grid <= 0) return;
-  hipLaunchKernelGGL(gemm_bwd_kernel<KIND>, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_bwd_kernel<KIND, SH>), dim3(grid), dim3(256), 0, s, a);
   if ((KIND == 2 || KIND == 3) && a.splits > 1) {
     const int M = (KIND == 2) ? a.d : 2 * a.inner;
     const int N = (KIND == 2) ? a.inner : a.d;
@@ -363,11 +383,15 @@ void launch_kind(const BwdGemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bwd(const BwdGemmArgs& a, hipStream_t s) {
-  switch (a.kind) {
-    case 0: launch_kind<0>(a, s); break;
-    case 1: launch_kind<1>(a, s); break;
-    case 2: launch_kind<2>(a, s); break;
-    case 3: launch_kind<3>(a, s); break;
+  switch (a.kind * 2 + (a.shared ? 1 : 0)) {
+    case 0: launch_kind<0, false>(a, s); break;
+    case 1: launch_kind<0, true>(a, s); break;
+    case 2: launch_kind<1, false>(a, s); break;
+    case 3: launch_kind<1, true>(a, s); break;
+    case 4: launch_kind<2, false>(a, s); break;
+    case 5: launch_kind<2, true>(a, s); break;
+    case 6: launch_kind<3, false>(a, s); break;
+    case 7: launch_kind<3, true>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -353,7 +353,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
 struct BwdLayout {
   Layout f;
   int64_t plog, g_r, g_s, da_r, da_s, dx_rows, dx_s, row_g, dg_part, dg, dl, dwg_part, zero,
-      dyp, xp, part, total;
+      part, total;
   int32_t n_part, n_chunk;
   int32_t splits2, splits3;   // k splits of the shared dW2 and dW1/dW3 GEMMs
 };
@@ -367,7 +367,7 @@ int32_t shared_wgrad_splits(int64_t tiles, int64_t T) {
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, 16));
 }
 
-constexpr int kGateGradChunks = 16;
+constexpr int kGateGradChunks = 128;
 
 BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   BwdLayout B;
@@ -381,7 +381,7 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   const int64_t TK = (int64_t)d.T * d.top_k;
   const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
   B.n_part = (d.inner + 127) / 128;
-  B.n_chunk = kGateGradChunks;
+  B.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kGateGradChunks, d.T / 64));
   B.plog = take((int64_t)B.f.ds * d.T * B.f.ep * 4);
   B.g_r = take(TK * d.inner * 4);
   B.g_s = d.n_shared > 0 ? take((int64_t)d.T * ksi * 4) : -1;
@@ -396,8 +396,6 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   const int64_t colsum = (int64_t)((d.T + 255) / 256) * d.n_routed;
   B.dwg_part = take(std::max<int64_t>((int64_t)B.n_chunk * d.n_routed * d.d, colsum) * 4);
   B.zero = take(1024);
-  B.dyp = take(TK * d.d * 2);
-  B.xp = take(TK * d.d * 2);
   B.splits2 = B.splits3 = 1;
   if (d.n_shared > 0) {
     const int64_t Is = d.shared_inner, Ks = d.n_shared;
@@ -496,10 +494,6 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   aux.dx = static_cast<bf16_t*>(dx);
   aux.zero = static_cast<bf16_t*>(at(B.zero)); aux.n_zero = 512;
   MOE_CHECK(launch_bwd_prep(aux, s));
-  // dy and x in the rows' order (expert-contiguous), read by the routed GEMMs
-  const int64_t TKr = (int64_t)d.T * d.top_k;
-  MOE_CHECK(launch_gather_rows(dyb, row_src, TKr, d.d, static_cast<bf16_t*>(at(B.dyp)), s));
-  MOE_CHECK(launch_gather_rows(xb, row_src, TKr, d.d, static_cast<bf16_t*>(at(B.xp)), s));
 
   BwdGemmArgs rb{};
   rb.T = d.T; rb.d = d.d; rb.inner = d.inner; rb.n_experts = d.n_routed; rb.shared = false;
@@ -507,8 +501,6 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   rb.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); rb.max_mtiles = L.max_mtiles;
   rb.offsets = static_cast<const int32_t*>(at(L.offsets)); rb.row_src = row_src;
   rb.dy = dyb; rb.x = xb;
-  rb.dyp = static_cast<const bf16_t*>(at(B.dyp));
-  rb.xp = static_cast<const bf16_t*>(at(B.xp));
   rb.splits = 1; rb.part = nullptr;
   rb.w1 = static_cast<const bf16_t*>(routed.w1);
   rb.w3 = static_cast<const bf16_t*>(routed.w3);
