@@ -45,10 +45,10 @@ constexpr int BK = 64;    // k per stage (8 chunks of 16 B)
 // least BM x 128 B each) and Bs0/Bs1.  MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED,
 // 3 GATEUP_BWD; WAVES_M x (4 / WAVES_M) waves.  `red` (4 x BM floats of LDS)
 // carries GATEUP_BWD's row sums across the waves of a tile.
-template <int MODE, int BM, int WAVES_M>
+template <int MODE, int BM, int WAVES_M, int NS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows, int e,
-                                          int nt, u32x4* As0, u32x4* As1, u32x4* Bs0,
-                                          u32x4* Bs1, float* red) {
+                                          int nt, u32x4* As0, u32x4* As1, u32x4* As2,
+                                          u32x4* Bs0, u32x4* Bs1, u32x4* Bs2, float* red) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -179,9 +179,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   auto sched_ds_vm = [&]() { sched_groups<N_MMA, N_DS, N_VM>(); };
 
   // One k-block from buffers (Ac, Bc); block kb+1 is already streaming into
-  // (An, Bn).  Once every wave has its last fragments of this block in
-  // registers (barrier), (Ac, Bc) are free and block `next2` = kb+2 starts
-  // streaming into them -- two blocks of matrix work to cover the latency.
+  // (An, Bn) (and with three stages kb+2 into the third pair).  Once every
+  // wave has its last fragments of this block in registers (barrier), (Ac,
+  // Bc) are free and the block NS steps ahead starts streaming into them.
   // Blocks past the end re-load the last block (no branch; never read).
   auto block = [&](int next2, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
     load_frags(fa1, fb1, Ac, Bc, 1);
@@ -193,7 +193,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     load_frags(fa1, fb1, Ac, Bc, 3);
     mma(fa0, fb0);
     sched_ds();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb+1 landed
+    if constexpr (NS == 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());    // block kb+1 landed (kb+2 may fly)
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb+1 landed
     __syncthreads();
     issue(next2, Ac, Bc);
     load_frags(fa0, fb0, An, Bn, 0);
@@ -201,17 +204,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     sched_ds_vm();
   };
 
-  issue(0, As0, Bs0);
-  issue(min(1, nk - 1), As1, Bs1);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());       // block 0 landed
-  __syncthreads();
-  load_frags(fa0, fb0, As0, Bs0, 0);
-  int kb = 0;
-  for (; kb + 2 <= nk; kb += 2) {
-    block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
-    block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+  if constexpr (NS == 3) {
+    // Three-stage ring (tiles of at most 128 rows, which stream their
+    // weights: two blocks in flight while one is computed).
+    issue(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1);
+    issue(min(2, nk - 1), As2, Bs2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * N_VM>());   // block 0 landed
+    __syncthreads();
+    load_frags(fa0, fb0, As0, Bs0, 0);
+    int kb = 0;
+    for (; kb + 3 <= nk; kb += 3) {
+      block(min(kb + 3, nk - 1), As0, Bs0, As1, Bs1);
+      block(min(kb + 4, nk - 1), As1, Bs1, As2, Bs2);
+      block(min(kb + 5, nk - 1), As2, Bs2, As0, Bs0);
+    }
+    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
+    if (kb + 1 < nk) block(nk - 1, As1, Bs1, As2, Bs2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    issue(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());       // block 0 landed
+    __syncthreads();
+    load_frags(fa0, fb0, As0, Bs0, 0);
+    int kb = 0;
+    for (; kb + 2 <= nk; kb += 2) {
+      block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
+      block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+    }
+    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
   }
-  if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
 
   // ---- epilogue ----
   // acc[nb][mb][r] = D[n][m] with n = nb*32 + 8*(r/4) + 4*hi + (r%4) and
@@ -448,8 +471,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
   // Two LDS buffers per operand as distinct objects: accesses name their
   // buffer statically, so the compiler can tell the direct loads into one
   // buffer from the operand reads of the other and need not wait between.
-  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
-  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
+  // Tiles of at most 128 rows stream their weights and keep three stages
+  // in flight-or-compute (3 x (BM + 256) x 128 B <= 144 KB of LDS).
+  constexpr int NS = (BM <= 128) ? 3 : 2;
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
   // Row sums of GATEUP_BWD (the A buffers are free by the epilogue, but a
   // separate array keeps the buffers' accesses static).
   __shared__ float red[MODE == 3 ? 4 * BM : 1];
@@ -476,14 +502,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(GemmArgs a) {
     const MTile t = a.tiles[mt];
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
-        gemm_tile<MODE, BM / 2, 1>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, red);
+        gemm_tile<MODE, BM / 2, 1, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0,
+                                       Bs1, Bs2, red);
         return;
       }
     }
-    gemm_tile<MODE, BM, WAVES_M>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, red);
+    gemm_tile<MODE, BM, WAVES_M, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0, Bs1,
+                                     Bs2, red);
   } else {
     const int row0 = mt * BM;
-    gemm_tile<MODE, BM, WAVES_M>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, Bs0, Bs1, red);
+    gemm_tile<MODE, BM, WAVES_M, NS>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, As2, Bs0,
+                                     Bs1, Bs2, red);
   }
 }
 

@@ -31,9 +31,12 @@ constexpr int TK = 64;      // k per stage
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// Chunk swizzle of mn-major LDS rows (32 chunks of 16 B per k-row): the four
-// k-rows one transpose load touches fall on different chunk columns.
-__device__ __forceinline__ int swz_mn(int k) { return (k & 7) << 1; }
+// Chunk swizzle of mn-major LDS rows (32 chunks of 16 B per k-row).  Half a
+// wave's transpose load (32 lanes, 256 B) reads 4 consecutive k-rows
+// (k = 0..3 mod 4) times 4 consecutive chunks (a 4-aligned group); XOR-ing
+// the chunk with 4 (k mod 4) puts those 16 chunks on 16 different 16-byte
+// bank groups (one full pass over the banks, no conflict).
+__device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
 // A 32 (mn) x 16 (k) operand fragment for the matrix op from an mn-major
 // LDS tile (64 k-rows x 32 chunks): lanes 0-31 hold mn = base + lane % 32 at

@@ -124,14 +124,15 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   }
   const int nk = kdim / BK8;
 
-  // Scale bytes of the tile: token rows (sA[r][kb]) and the weight blocks
-  // (sB[h][kb]: GATEUP h = 0 / 1 for W1 / W3 of the tile's 128 inner rows;
-  // DOWN h = the 128-row halves of the 256 output columns).
+  // Scale bytes of the tile: token rows (sA[kb][r]: a wave's 32 rows of one
+  // k-block are 32 consecutive bytes, read without bank conflicts) and the
+  // weight blocks (sB[h][kb]: GATEUP h = 0 / 1 for W1 / W3 of the tile's 128
+  // inner rows; DOWN h = the 128-row halves of the 256 output columns).
   for (int i = tid; i < BM * nk; i += 256) {
-    const int r = i / nk, kb = i % nk;
+    const int r = i % BM, kb = i / BM;
     const int rr = min(r, rows - 1);
     const int src = a.a_rows ? a.a_rows[row0 + rr] : row0 + rr;
-    sA[r * MAX_NK + kb] = a.a_scale[(size_t)src * a.lda_s + kb];
+    sA[kb * BM + r] = a.a_scale[(size_t)src * a.lda_s + kb];
   }
   for (int i = tid; i < 2 * nk; i += 256) {
     const int h = i / nk, kb = i % nk;
@@ -203,7 +204,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   int sa[MB], sb[2];
   auto load_scales = [&](int kb) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) sa[mb] = sA[(wm * WM + mb * 32 + l32) * MAX_NK + kb];
+    for (int mb = 0; mb < MB; ++mb) sa[mb] = sA[kb * BM + wm * WM + mb * 32 + l32];
     if (MODE == 0) {
       sb[0] = sB[kb];
       sb[1] = sB[MAX_NK + kb];
