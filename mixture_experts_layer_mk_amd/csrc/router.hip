@@ -161,12 +161,16 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// Four waves stage the block's logits (the d-slice partials are the bulk
+// of the bytes; one wave alone keeps too few loads in flight); wave 0 then
+// selects for the block's 64 tokens, one token per lane.
 template <int KMAX>
-__global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   extern __shared__ float lg[];               // [64][E + 1]: logits, then p
   __shared__ uint64_t masks[MAX_EXPERTS];
   __shared__ float gsc[64][MAX_GROUPS + 1];
-  const int lane = threadIdx.x;
+  __shared__ float sbias[MAX_EXPERTS];        // selection bias (0 without one)
+  const int lane = threadIdx.x;               // token lane (wave 0)
   const int t0 = blockIdx.x * 64;
   const int t = t0 + lane;
   const bool live = t < a.T;
@@ -180,8 +184,9 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
   const int q4 = a.ep / 4;
   const float4* p4 = reinterpret_cast<const float4*>(a.plog);
   const size_t slice4 = (size_t)a.T * q4;
+  for (int e = threadIdx.x; e < E; e += 256) sbias[e] = a.select_bias ? a.select_bias[e] : 0.f;
 #pragma unroll 4
-  for (int i = lane; i < ntok * q4; i += 64) {
+  for (int i = threadIdx.x; i < ntok * q4; i += 256) {
     const int r = i / q4, c = i % q4;
     const size_t o = (size_t)(t0 + r) * q4 + c;
     float4 v = p4[o];
@@ -197,6 +202,11 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
+  if (threadIdx.x >= 64) {   // staging done: the other waves pass the two
+    __syncthreads();         // barriers of wave 0's selection and leave
+    __syncthreads();
+    return;
+  }
   float* my = lg + (live ? lane : 0) * ld;    // dead lanes shadow row 0
 
   // scores: softmax p_e = exp(l_e - max) / z (exponentials stored, divided
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a) {
   __syncthreads();
   auto score = [&](int e) -> float { return a.score == 0 ? my[e] / z : my[e]; };
   auto key_of = [&](int e, float s) -> float {
-    const float k = s + (a.select_bias ? a.select_bias[e] : 0.f);
+    const float k = s + sbias[e];
     return (k != k) ? -INFINITY : k;     // NaN never outranks a score
   };
 
@@ -603,8 +613,8 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
   sa.block_counts = r.block_counts;
   const dim3 grid((r.T + 63) / 64);
   const size_t lds = (size_t)64 * (r.E + 1) * sizeof(float);
-  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(64), lds, s, sa);
-  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(64), lds, s, sa);
+  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(256), lds, s, sa);
+  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(256), lds, s, sa);
   return hipGetLastError();
 }
 
