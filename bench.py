@@ -126,8 +126,19 @@ def cpu_baseline(cfg, host, n_tokens, reps):
         oracle.moe_forward(x, wg, tuple(w), tuple(ws) if ws else None, cfg.top_k,
                            n_shared=cfg.n_shared, score=cfg.score)
     dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    fpt = oracle.expert_flops_per_token(cfg.d, cfg.top_k, cfg.inner, cfg.n_shared,
+                                        cfg.shared_inner) + 2 * cfg.d * cfg.n_routed
     return {"value": n_tokens * reps / dt, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": model,
+            "gflops": round(fpt * n_tokens * reps / dt / 1e9, 1),
             "sample": f"{reps} x the first {n_tokens} of {cfg.T} tokens of the same workload "
                       f"(numpy fp64 oracle, BLAS threads={cores})"}
 
@@ -474,6 +485,24 @@ def main():
     attain = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 10 / 1e3) / 1e12
     del a8, b8
 
+    # Achieved rates of the stages around the GEMMs: the router's logits
+    # (fp32-accurate, 2 T d E FLOPs; x, the gate and the choice as bytes) and
+    # the permute's row maps (the choice read, two int32 maps written).
+    def rate(nbytes, ms_):
+        return round(nbytes / (ms_ / 1e3) / 1e9, 1) if ms_ > 0 else None
+    TKn = cfg.T * cfg.top_k
+    xb = 2 if cfg.dtype == "bf16" else 4
+    router_bytes = cfg.T * cfg.d * xb + cfg.n_routed * cfg.d * 4 + TKn * 8
+    stage_rates = {
+        "router": {"tflops_fp32_equiv": round(2.0 * cfg.T * cfg.d * cfg.n_routed /
+                                              (stage_ms["router"] / 1e3) / 1e12, 2),
+                   "gbs": rate(router_bytes, stage_ms["router"])},
+        "permute": {"gbs": rate(TKn * 4 * 3, stage_ms["permute"])},
+        "combine": ("fused into the shared down-projection" if cfg.n_shared > 0 and
+                    cfg.dtype == "bf16" else
+                    {"gbs": rate(TKn * cfg.d * 2 + cfg.T * cfg.d * 8, stage_ms["combine"])}),
+    }
+
     fp8 = None
     if not args.no_fp8 and cfg.dtype == "bf16" and not args.cold_cache:
         log(f"[bench] fp8 variant: {args.steps} steps")
@@ -508,6 +537,7 @@ def main():
         "frac_bf16_peak": round(act_tflops / PEAK_BF16_TFLOPS, 4),
         "router_gflop": round(router_gflop, 2),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_rates": stage_rates,
         "events_ms_per_step": round(total_ev, 4),
         "roofline": roofline,
         "per_call": per_call,
