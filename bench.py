@@ -38,6 +38,9 @@ GATEUP = {
              os.path.join(ROOT, "profiles", "traffic_gemm_gateup_routed.json")),
     "fp8": ("gemm_fp8_kernel<0", ("common.h", "gemm_common.h", "gemm_fp8.hip"),
             os.path.join(ROOT, "profiles", "traffic_gemm_fp8_gateup_routed.json")),
+    # the backward's slowest GEMM stage: routed dW1/dW3
+    "bwd": ("gemm_bwd_kernel<3, false>", ("common.h", "gemm_common.h", "gemm_bwd.hip"),
+            os.path.join(ROOT, "profiles", "traffic_gemm_bwd_dw13_routed.json")),
 }
 
 
@@ -87,7 +90,8 @@ def summarize_traffic(fetch_csv, write_csv, copy_mb):
     vals = {"fetch": per_kernel(fetch_csv, "FETCH_SIZE"),
             "write": per_kernel(write_csv, "WRITE_SIZE")}
     for kind, (prefix, _, path) in GATEUP.items():
-        out = {"source_hash": source_hash(kind), "kernel": prefix + ">, routed gate/up launch",
+        what = "routed dW1/dW3 launch" if kind == "bwd" else "routed gate/up launch"
+        out = {"source_hash": source_hash(kind), "kernel": prefix.rstrip(">") + ">, " + what,
                "copy_calibration_mib": copy_mb}
         for name in ("fetch", "write"):
             v_all = vals[name]
@@ -310,7 +314,8 @@ def time_backward(moe, cfg, d, steps, warmup):
                          for k in flops if stage_ms[k] > 0},
         "roofline": {"kernel": BWD_KERNEL[dom], "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("bwd") if dom == "dw13_routed" else None,
                      "flops_per_launch": flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)},
     }
 
