@@ -193,11 +193,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     load_frags(fa1, fb1, Ac, Bc, 3);
     mma(fa0, fb0);
     sched_ds();
-    if constexpr (NS == 3)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());    // block kb+1 landed (kb+2 may fly)
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb+1 landed
-    __syncthreads();
+    stage_sync<NS == 3 ? N_VM : 0>();   // block kb+1 landed (with NS = 3 kb+2 may fly)
     issue(next2, Ac, Bc);
     load_frags(fa0, fb0, An, Bn, 0);
     mma(fa1, fb1);
@@ -210,8 +206,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     issue(0, As0, Bs0);
     issue(min(1, nk - 1), As1, Bs1);
     issue(min(2, nk - 1), As2, Bs2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * N_VM>());   // block 0 landed
-    __syncthreads();
+    stage_sync<2 * N_VM>();   // block 0 landed
     load_frags(fa0, fb0, As0, Bs0, 0);
     int kb = 0;
     for (; kb + 3 <= nk; kb += 3) {
@@ -225,8 +220,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   } else {
     issue(0, As0, Bs0);
     issue(min(1, nk - 1), As1, Bs1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<N_VM>());       // block 0 landed
-    __syncthreads();
+    stage_sync<N_VM>();   // block 0 landed
     load_frags(fa0, fb0, As0, Bs0, 0);
     int kb = 0;
     for (; kb + 2 <= nk; kb += 2) {

@@ -88,6 +88,20 @@ constexpr int vmcnt_imm() {
   return (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
 }
 
+// Work-group barrier between pipeline stages: wait until at most N of this
+// wave's vector-memory loads are outstanding (the direct-to-LDS loads of the
+// stage about to be read have landed) and its LDS reads are done, then every
+// wave meets.  Wait and barrier sit in one asm statement with a memory
+// clobber, so the compiler can move no load across them and the count N
+// stays the one the caller derived.  Unlike __syncthreads(), whose
+// work-group fence makes the compiler drain every outstanding vector-memory
+// load here, this keeps the later stages' loads in flight.
+template <int N>
+__device__ __forceinline__ void stage_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Stages whose tiles are gate/up tiles (GATEUP and its backward).
 template <int MODE>
 constexpr bool is_gateup() { return MODE == 0 || MODE == 3; }
