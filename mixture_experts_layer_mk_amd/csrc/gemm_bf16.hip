@@ -115,7 +115,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   const int nk = kdim / BK;
 
   // Issue the direct loads of k-block kb into the LDS buffers (Ab, Bb).
-  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
+  // The direct loads of k-block kb into the LDS buffers (Ab, Bb): A_LD + B_LD
+  // per wave, numbered q (A first).  They are issued in NPART parts -- part p
+  // takes q in [p N / NPART, (p + 1) N / NPART) -- spread over successive
+  // k-steps rather than all beside the matrix ops of one step (measured: two
+  // parts for the two-stage 256-row tiles, four for the three-stage ring).
+  constexpr int N_VM = A_LD + B_LD;
+  constexpr int NPART = (NS == 3) ? 4 : 2;
+  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb, int part) {
+    const int lo = part * N_VM / NPART, hi_q = (part + 1) * N_VM / NPART;
     const size_t ka = (size_t)kb * BK;
     size_t kbo = ka;
     if (MODE == 2) {   // shared experts follow one another along k
@@ -124,10 +132,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     }
 #pragma unroll
     for (int j = 0; j < A_LD; ++j)
-      __builtin_amdgcn_global_load_lds((const glb_void*)(A + aoff[j] + ka),
-                                       (lds_void*)&Ab[(wave * A_LD + j) * 64], 16, 0, 0);
+      if (j >= lo && j < hi_q)
+        __builtin_amdgcn_global_load_lds((const glb_void*)(A + aoff[j] + ka),
+                                         (lds_void*)&Ab[(wave * A_LD + j) * 64], 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < B_LD; ++j) {
+      if (A_LD + j < lo || A_LD + j >= hi_q) continue;
       const bf16_t* base = B1;
       if (GU) {
         const int r = (wave * B_LD + j) * 8;        // uniform: W1 or W3 half
@@ -136,6 +146,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       __builtin_amdgcn_global_load_lds((const glb_void*)(base + boff[j] + kbo),
                                        (lds_void*)&Bb[(wave * B_LD + j) * 64], 16, 0, 0);
     }
+  };
+  auto issue_all = [&](int kb, u32x4* Ab, u32x4* Bb) {
+#pragma unroll
+    for (int p = 0; p < NPART; ++p) issue(kb, Ab, Bb, p);
   };
 
   f32x16 acc[NB][MB];
@@ -174,60 +188,68 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   };
   // Scheduling: spread the LDS reads (and the direct loads) of a k-step
   // between its matrix ops so the matrix pipe never waits on LDS latency.
-  constexpr int N_MMA = NB * MB, N_DS = NB + MB, N_VM = A_LD + B_LD;
-  auto sched_ds = [&]() { sched_groups<N_MMA, N_DS, 0>(); };
-  auto sched_ds_vm = [&]() { sched_groups<N_MMA, N_DS, N_VM>(); };
+  constexpr int N_MMA = NB * MB, N_DS = NB + MB;
+  constexpr int P0 = N_VM / NPART;                       // loads in part 0
+  constexpr int P1 = 2 * N_VM / NPART - P0, P2 = 3 * N_VM / NPART - 2 * N_VM / NPART;
+  constexpr int P3 = 4 * N_VM / NPART - 3 * N_VM / NPART;
 
-  // One k-block from buffers (Ac, Bc); block kb+1 is already streaming into
-  // (An, Bn) (and with three stages kb+2 into the third pair).  Once every
-  // wave has its last fragments of this block in registers (barrier), (Ac,
-  // Bc) are free and the block NS steps ahead starts streaming into them.
-  // Blocks past the end re-load the last block (no branch; never read).
-  auto block = [&](int next2, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
+  // One k-block from buffers (Ac, Bc); block kb+1 is already in (An, Bn)
+  // or streaming into them (and with three stages kb+2 into the third
+  // pair).  Parts 1.. of block `pend` (issued last) stream into (Ap, Bp)
+  // during the first k-steps.  Once every wave has its last fragments of
+  // this block in registers (barrier), (Ac, Bc) are free and part 0 of the
+  // block NS steps ahead starts streaming into them.  Blocks past the end
+  // re-load the last block (no branch; never read).
+  auto block = [&](int pend, u32x4* Ap, u32x4* Bp, int next, u32x4* Ac, u32x4* Bc,
+                   const u32x4* An, const u32x4* Bn) {
     load_frags(fa1, fb1, Ac, Bc, 1);
+    if (NPART > 1) issue(pend, Ap, Bp, 1);
     mma(fa0, fb0);
-    sched_ds();
+    sched_groups<N_MMA, N_DS, (NPART > 1 ? P1 : 0)>();
     load_frags(fa0, fb0, Ac, Bc, 2);
+    if (NPART > 2) issue(pend, Ap, Bp, 2);
     mma(fa1, fb1);
-    sched_ds();
+    sched_groups<N_MMA, N_DS, (NPART > 2 ? P2 : 0)>();
     load_frags(fa1, fb1, Ac, Bc, 3);
+    if (NPART > 3) issue(pend, Ap, Bp, 3);
     mma(fa0, fb0);
-    sched_ds();
+    sched_groups<N_MMA, N_DS, (NPART > 3 ? P3 : 0)>();
     stage_sync<NS == 3 ? N_VM : 0>();   // block kb+1 landed (with NS = 3 kb+2 may fly)
-    issue(next2, Ac, Bc);
+    issue(next, Ac, Bc, 0);
     load_frags(fa0, fb0, An, Bn, 0);
     mma(fa1, fb1);
-    sched_ds_vm();
+    sched_groups<N_MMA, N_DS, P0>();
   };
 
   if constexpr (NS == 3) {
     // Three-stage ring (tiles of at most 128 rows, which stream their
     // weights: two blocks in flight while one is computed).
-    issue(0, As0, Bs0);
-    issue(min(1, nk - 1), As1, Bs1);
-    issue(min(2, nk - 1), As2, Bs2);
-    stage_sync<2 * N_VM>();   // block 0 landed
+    issue_all(0, As0, Bs0);
+    issue_all(min(1, nk - 1), As1, Bs1);
+    issue(min(2, nk - 1), As2, Bs2, 0);
+    stage_sync<N_VM + P0>();   // block 0 landed
     load_frags(fa0, fb0, As0, Bs0, 0);
     int kb = 0;
     for (; kb + 3 <= nk; kb += 3) {
-      block(min(kb + 3, nk - 1), As0, Bs0, As1, Bs1);
-      block(min(kb + 4, nk - 1), As1, Bs1, As2, Bs2);
-      block(min(kb + 5, nk - 1), As2, Bs2, As0, Bs0);
+      block(min(kb + 2, nk - 1), As2, Bs2, min(kb + 3, nk - 1), As0, Bs0, As1, Bs1);
+      block(min(kb + 3, nk - 1), As0, Bs0, min(kb + 4, nk - 1), As1, Bs1, As2, Bs2);
+      block(min(kb + 4, nk - 1), As1, Bs1, min(kb + 5, nk - 1), As2, Bs2, As0, Bs0);
     }
-    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
-    if (kb + 1 < nk) block(nk - 1, As1, Bs1, As2, Bs2);
+    if (kb < nk) block(nk - 1, As2, Bs2, nk - 1, As0, Bs0, As1, Bs1);
+    if (kb + 1 < nk) block(nk - 1, As0, Bs0, nk - 1, As1, Bs1, As2, Bs2);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
-    issue(0, As0, Bs0);
-    issue(min(1, nk - 1), As1, Bs1);
-    stage_sync<N_VM>();   // block 0 landed
+    issue_all(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1, 0);
+    stage_sync<P0>();   // block 0 landed
     load_frags(fa0, fb0, As0, Bs0, 0);
     int kb = 0;
     for (; kb + 2 <= nk; kb += 2) {
-      block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
-      block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+      block(min(kb + 1, nk - 1), As1, Bs1, min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
+      block(min(kb + 2, nk - 1), As0, Bs0, min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
     }
-    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
+    if (kb < nk) block(nk - 1, As1, Bs1, nk - 1, As0, Bs0, As1, Bs1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---- epilogue ----

@@ -91,15 +91,16 @@ constexpr int vmcnt_imm() {
 // Work-group barrier between pipeline stages: wait until at most N of this
 // wave's vector-memory loads are outstanding (the direct-to-LDS loads of the
 // stage about to be read have landed) and its LDS reads are done, then every
-// wave meets.  Wait and barrier sit in one asm statement with a memory
-// clobber, so the compiler can move no load across them and the count N
-// stays the one the caller derived.  Unlike __syncthreads(), whose
-// work-group fence makes the compiler drain every outstanding vector-memory
-// load here, this keeps the later stages' loads in flight.
+// wave meets.  Unlike __syncthreads(), whose work-group fence makes the
+// compiler drain every outstanding vector-memory load here, this keeps the
+// later stages' loads in flight.  The count wait is the builtin, which the
+// compiler's wait insertion sees (so it adds no wait of its own for these
+// loads after the barrier) and which no memory access is moved across; the
+// barrier's memory clobber keeps LDS reads and loads on their side of it.
 template <int N>
 __device__ __forceinline__ void stage_sync() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<N>());
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Stages whose tiles are gate/up tiles (GATEUP and its backward).
