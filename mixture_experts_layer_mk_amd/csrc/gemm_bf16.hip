@@ -57,7 +57,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the waves");
   static_assert(MB >= 1 && NB >= 2 && (NB % 2) == 0, "tile shape");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: kept in a scalar register, so the per-wave
+  // LDS bases of the direct loads (M0) and the fragment rows need no
+  // per-load vector-to-scalar moves.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   constexpr bool GU = is_gateup<MODE>();
   const bool routed = !(MODE == 2 || (GU && a.shared));

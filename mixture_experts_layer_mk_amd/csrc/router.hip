@@ -16,10 +16,11 @@
 //     The hidden dimension may be split over DS waves (more waves in flight);
 //     the DS partial sums are added in a fixed order by the select kernel.
 //     (fp32 x: a plain fp32 FMA GEMM instead.)
-//  3. select: one lane per token, 64 tokens per wave (= one histogram
-//     block): scores in fp32, group limit, top-K kept in registers ordered
-//     by (key descending, index ascending), gate weights; then per expert a
-//     wave ballot gives the block's count and each slot's in-block rank.
+//  3. select: eight lanes per token, 64 tokens (= one histogram block) per
+//     workgroup: scores in fp32, group limit, top-K ordered by (key
+//     descending, index ascending) in K merge rounds, gate weights; per
+//     expert a 64-bit mask of the block's tokens gives the block's count and
+//     each slot's in-block rank.
 // bf16 layers with at most 64 experts, K <= 8 and no group limit run 2 and 3
 // fused in one kernel per 64-token block (4 below).
 #include "common.h"
@@ -52,66 +53,84 @@ __global__ __launch_bounds__(256) void split_gate_kernel(const float* __restrict
 // ---------------------------------------------------------------------------
 // 2a. logits on the matrix cores (bf16 x)
 // ---------------------------------------------------------------------------
-// One wave per (token block, expert block, d-slice) tile; 4 waves per
-// workgroup.  plog[ds][t][e] (row stride ep) receives the partial sum of the
-// ds-th slice of the hidden dimension.
+// One wave per (group of LG_TB token blocks, expert block, d-slice) tile; 4
+// waves per workgroup, which take consecutive expert blocks of the same
+// tokens (their x loads meet in the L1 cache).  Each weight fragment is read
+// once per k-step and used for all LG_TB token blocks.  plog[ds][t][e] (row
+// stride ep) receives the partial sum of the ds-th slice of the hidden
+// dimension.
+constexpr int LG_TB = 4;   // 32-token blocks per wave
+
 __global__ __launch_bounds__(256) void logits_mfma_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
   const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n_eb = (a.E + 31) / 32, n_tb = (a.T + 31) / 32;
-  if (tile >= n_eb * n_tb * a.ds) return;
+  const int n_eb = (a.E + 31) / 32, n_tg = (a.T + 32 * LG_TB - 1) / (32 * LG_TB);
+  if (tile >= n_eb * n_tg * a.ds) return;
   const int eb = tile % n_eb;
-  const int tb = (tile / n_eb) % n_tb;
-  const int ds = tile / (n_eb * n_tb);
+  const int tg = (tile / n_eb) % n_tg;
+  const int ds = tile / (n_eb * n_tg);
   const int l32 = lane & 31, hi = lane >> 5;
   const int er = min(eb * 32 + l32, a.E - 1);
-  const int tr = min(tb * 32 + l32, a.T - 1);
   const int kspan = a.d / a.ds;                      // multiple of 16
   const int k0 = ds * kspan;
   const size_t pn = (size_t)a.E * a.d;
-  const bf16_t* xp = a.x + (size_t)tr * a.d + k0 + 8 * hi;
+  const bf16_t* xp[LG_TB];
+#pragma unroll
+  for (int b = 0; b < LG_TB; ++b) {
+    const int tr = min((tg * LG_TB + b) * 32 + l32, a.T - 1);
+    xp[b] = a.x + (size_t)tr * a.d + k0 + 8 * hi;
+  }
   const bf16_t* wp = a.planes + (size_t)er * a.d + k0 + 8 * hi;
 
-  f32x16 acc;
+  f32x16 acc[LG_TB];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  constexpr int U = 4;   // k-steps of 16 per batch (loads of a batch in flight)
+  for (int b = 0; b < LG_TB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+  constexpr int U = 2;   // k-steps of 16 per batch (loads of a batch in flight)
+  auto step = [&](const bf16x8 (&xf)[LG_TB], bf16x8 wl, bf16x8 wm, bf16x8 wh) {
+#pragma unroll
+    for (int b = 0; b < LG_TB; ++b) {
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl, xf[b], acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wm, xf[b], acc[b], 0, 0, 0);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh, xf[b], acc[b], 0, 0, 0);
+    }
+  };
   int k = 0;
   for (; k + 16 * U <= kspan; k += 16 * U) {
-    bf16x8 xf[U], wh[U], wm[U], wl[U];
+    bf16x8 xf[U][LG_TB], wh[U], wm[U], wl[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      xf[u] = *reinterpret_cast<const bf16x8*>(xp + k + 16 * u);
       wh[u] = *reinterpret_cast<const bf16x8*>(wp + k + 16 * u);
       wm[u] = *reinterpret_cast<const bf16x8*>(wp + pn + k + 16 * u);
       wl[u] = *reinterpret_cast<const bf16x8*>(wp + 2 * pn + k + 16 * u);
+#pragma unroll
+      for (int b = 0; b < LG_TB; ++b)
+        xf[u][b] = *reinterpret_cast<const bf16x8*>(xp[b] + k + 16 * u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wl[u], xf[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wm[u], xf[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wh[u], xf[u], acc, 0, 0, 0);
-    }
+    for (int u = 0; u < U; ++u) step(xf[u], wl[u], wm[u], wh[u]);
   }
   for (; k < kspan; k += 16) {
-    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xp + k);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(wp + 2 * pn + k), xf, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(wp + pn + k), xf, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        *reinterpret_cast<const bf16x8*>(wp + k), xf, acc, 0, 0, 0);
+    bf16x8 xf[LG_TB];
+#pragma unroll
+    for (int b = 0; b < LG_TB; ++b) xf[b] = *reinterpret_cast<const bf16x8*>(xp[b] + k);
+    step(xf, *reinterpret_cast<const bf16x8*>(wp + 2 * pn + k),
+         *reinterpret_cast<const bf16x8*>(wp + pn + k), *reinterpret_cast<const bf16x8*>(wp + k));
   }
-  // acc[r] = D[e][t]: e = eb*32 + 8*(r/4) + 4*hi + r%4, t = tb*32 + l32
-  const int t = tb * 32 + l32;
-  if (t >= a.T) return;
-  float* row = a.plog + ((size_t)ds * a.T + t) * a.ep;
+  // acc[b][r] = D[e][t]: e = eb*32 + 8*(r/4) + 4*hi + r%4, t = token block b's row l32
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int e0 = eb * 32 + 8 * g + 4 * hi;
+  for (int b = 0; b < LG_TB; ++b) {
+    const int t = (tg * LG_TB + b) * 32 + l32;
+    if (t >= a.T) continue;
+    float* row = a.plog + ((size_t)ds * a.T + t) * a.ep;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (e0 + q < a.E) row[e0 + q] = acc[4 * g + q];
+    for (int g = 0; g < 4; ++g) {
+      const int e0 = eb * 32 + 8 * g + 4 * hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e0 + q < a.E) row[e0 + q] = acc[b][4 * g + q];
+    }
   }
 }
 
@@ -161,37 +180,48 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// Four waves stage the block's logits (the d-slice partials are the bulk
-// of the bytes; one wave alone keeps too few loads in flight); wave 0 then
-// selects for the block's 64 tokens, one token per lane.
+// Eight waves per block of 64 tokens (one histogram block): all of them stage
+// the block's logits (sum of the d-slice partials in slice order, plus the
+// logit bias), then each token takes eight adjacent lanes, lane j over the
+// j-th contiguous eighth of the experts:
+//  a. scores in fp32: softmax (max and sum over the eight lanes; the
+//     exponentials are stored and divided on use) or sigmoid;
+//  b. group limit: each group's score is the sum of its two best keys (its
+//     best key for groups of one expert), merged over the lanes, and the
+//     topk_groups best groups are kept (ties to the lower group index);
+//  c. top-K by K rounds: each lane offers its best untaken kept expert, the
+//     eight offers are merged, and the round's winner (key descending, index
+//     ascending) is the next kept expert -- the same total order as a sorted
+//     scan over all experts;
+//  d. gate weights from the kept scores in selection order;
+//  e. block histogram and in-block ranks: every kept (token, expert) ORs the
+//     token's bit into the expert's 64-bit LDS mask (order-free, so
+//     deterministic); counts and ranks are popcounts.
 template <int KMAX>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  extern __shared__ float lg[];               // [64][E + 1]: logits, then p
-  __shared__ uint64_t masks[MAX_EXPERTS];
+__global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
+  extern __shared__ float lg[];               // [64][E + 1]: logits, then scores
+  __shared__ unsigned long long masks[MAX_EXPERTS];
   __shared__ float gsc[64][MAX_GROUPS + 1];
   __shared__ float sbias[MAX_EXPERTS];        // selection bias (0 without one)
-  const int lane = threadIdx.x;               // token lane (wave 0)
+  const int tid = threadIdx.x;
   const int t0 = blockIdx.x * 64;
-  const int t = t0 + lane;
-  const bool live = t < a.T;
   const int E = a.E, K = a.K, ld = E + 1;
   const int ntok = min(64, a.T - t0);
 
-  // Stage this block's logits: sum of the d-slice partials in slice order,
-  // plus the logit bias (coalesced: the block's rows are contiguous).
-  // (rows of ep floats, ep a multiple of 4: float4 loads; the slices are
-  // independent loads, batched so several are in flight.)
   const int q4 = a.ep / 4;
   const float4* p4 = reinterpret_cast<const float4*>(a.plog);
   const size_t slice4 = (size_t)a.T * q4;
-  for (int e = threadIdx.x; e < E; e += 256) sbias[e] = a.select_bias ? a.select_bias[e] : 0.f;
+  for (int e = tid; e < E; e += 512) {
+    sbias[e] = a.select_bias ? a.select_bias[e] : 0.f;
+    masks[e] = 0ull;
+  }
 #pragma unroll 4
-  for (int i = threadIdx.x; i < ntok * q4; i += 256) {
+  for (int i = tid; i < ntok * q4; i += 512) {
     const int r = i / q4, c = i % q4;
     const size_t o = (size_t)(t0 + r) * q4 + c;
     float4 v = p4[o];
-    for (int s = 1; s < a.ds; ++s) {
-      const float4 w = p4[o + s * slice4];
+    for (int sl = 1; sl < a.ds; ++sl) {
+      const float4 w = p4[o + sl * slice4];
       v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
     }
     const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -202,122 +232,140 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  if (threadIdx.x >= 64) {   // staging done: the other waves pass the two
-    __syncthreads();         // barriers of wave 0's selection and leave
-    __syncthreads();
-    return;
-  }
-  float* my = lg + (live ? lane : 0) * ld;    // dead lanes shadow row 0
 
-  // scores: softmax p_e = exp(l_e - max) / z (exponentials stored, divided
-  // on use) or sigmoid p_e = 1 / (1 + exp(-l_e)); always in fp32.
+  const int j = tid & 7;                      // lane of the token's eight
+  const int tl = tid >> 3;                    // token in the block
+  const int t = t0 + tl;
+  const bool live = tl < ntok;
+  float* my = lg + (live ? tl : 0) * ld;      // dead tokens shadow row 0 (read only)
+  const int C = (E + 7) / 8;                  // experts per lane (at most 32)
+  const int e0 = min(E, j * C), e1 = min(E, e0 + C);
+  auto xor8 = [](float v, int m) { return __shfl_xor(v, m, 8); };
+
+  // a. scores
   float z = 1.f;
   if (a.score == 0) {
     float mx = -INFINITY;
-    for (int e = 0; e < E; ++e) mx = fmaxf(mx, my[e]);
-    z = 0.f;
-    for (int e = 0; e < E; ++e) {
+    for (int e = e0; e < e1; ++e) mx = fmaxf(mx, my[e]);
+    mx = fmaxf(mx, xor8(mx, 1));
+    mx = fmaxf(mx, xor8(mx, 2));
+    mx = fmaxf(mx, xor8(mx, 4));
+    float zs = 0.f;
+    for (int e = e0; e < e1; ++e) {
       const float v = expf(my[e] - mx);
-      z += v;
+      zs += v;
       if (live) my[e] = v;
     }
+    zs += xor8(zs, 1);
+    zs += xor8(zs, 2);
+    zs += xor8(zs, 4);
+    z = zs;
   } else {
-    for (int e = 0; e < E; ++e) {
+    for (int e = e0; e < e1; ++e) {
       const float v = 1.f / (1.f + expf(-my[e]));
       if (live) my[e] = v;
     }
   }
-  __syncthreads();
   auto score = [&](int e) -> float { return a.score == 0 ? my[e] / z : my[e]; };
-  auto key_of = [&](int e, float s) -> float {
-    const float k = s + sbias[e];
+  auto key_of = [&](int e, float sc) -> float {
+    const float k = sc + sbias[e];
     return (k != k) ? -INFINITY : k;     // NaN never outranks a score
   };
 
-  // group limit: bitmask of the kept groups
+  // b. group limit: bitmask of the kept groups
   uint64_t keep = ~0ull;
   int gsz = E;
   if (a.n_groups > 1) {
     gsz = E / a.n_groups;
     for (int g = 0; g < a.n_groups; ++g) {
       float b1 = -INFINITY, b2 = -INFINITY;
-      for (int q = 0; q < gsz; ++q) {
-        const int e = g * gsz + q;
+      const int lo = max(e0, g * gsz), hi_e = min(e1, (g + 1) * gsz);
+      for (int e = lo; e < hi_e; ++e) {
         const float kv = key_of(e, score(e));
         if (kv > b1) { b2 = b1; b1 = kv; } else if (kv > b2) { b2 = kv; }
       }
-      gsc[lane][g] = (gsz > 1) ? b1 + b2 : b1;
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {   // top two of both lanes' top two
+        const float c1 = xor8(b1, m), c2 = xor8(b2, m);
+        const float n2 = fmaxf(fminf(b1, c1), fmaxf(b2, c2));
+        b1 = fmaxf(b1, c1);
+        b2 = n2;
+      }
+      if (j == 0) gsc[tl][g] = (gsz > 1) ? b1 + b2 : b1;
     }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     keep = 0;
     for (int r = 0; r < a.topk_groups; ++r) {
       float bk = -INFINITY;
       int bi = 0x7fffffff;
       for (int g = 0; g < a.n_groups; ++g) {
         if ((keep >> g) & 1) continue;
-        const float v = gsc[lane][g];
+        const float v = gsc[tl][g];
         if (better(v, g, bk, bi)) { bk = v; bi = g; }
       }
       keep |= 1ull << bi;
     }
   }
 
-  // top-K in registers, sorted by (key desc, index asc)
-  float tk[KMAX], ts[KMAX];
+  // c. top-K: K rounds of the best untaken kept expert over the eight lanes
+  float ts[KMAX];
   int ti[KMAX];
+  uint32_t taken = 0;                         // bit e - e0: kept already
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
-  const int ngr = E / gsz;
-  for (int g = 0; g < ngr; ++g) {
-    if (!((keep >> g) & 1)) continue;
-    for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
-      const float s = score(e);
-      float ck = key_of(e, s), cs = s;
-      int ci = e;
-#pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
-          const float k2 = tk[j], s2 = ts[j];
-          const int i2 = ti[j];
-          tk[j] = ck; ts[j] = cs; ti[j] = ci;
-          ck = k2; cs = s2; ci = i2;
-        }
-      }
+  for (int r = 0; r < KMAX; ++r) {
+    ts[r] = 0.f;
+    ti[r] = 0x7fffffff;
+    if (r >= K) continue;
+    float bk = -INFINITY, bs = 0.f;
+    int bi = 0x7fffffff;
+    for (int e = e0; e < e1; ++e) {
+      if ((taken >> (e - e0)) & 1) continue;
+      if (!((keep >> (e / gsz)) & 1)) continue;
+      const float sc = score(e);
+      const float kv = key_of(e, sc);
+      if (better(kv, e, bk, bi)) { bk = kv; bi = e; bs = sc; }
     }
-  }
-  float gsum = 0.f;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (j < K) gsum += ts[j];
-  if (live) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j >= K) break;
-      float g = ts[j];
-      if (a.norm_topk) g = g / gsum;
-      g *= a.routed_scale;
-      a.topk_idx[(size_t)t * K + j] = ti[j];
-      a.topk_w[(size_t)t * K + j] = g;
+    for (int m = 1; m < 8; m <<= 1) {
+      const float ok = xor8(bk, m), os = xor8(bs, m);
+      const int oi = __shfl_xor(bi, m, 8);
+      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bs = os; }
     }
+    ts[r] = bs;
+    ti[r] = bi;
+    if (bi >= e0 && bi < e1) taken |= 1u << (bi - e0);
   }
 
-  // block histogram and in-block ranks (token order = lane order)
-  for (int e = 0; e < E; ++e) {
-    bool has = false;
+  // d. gate weights; lane j writes the slots r = j mod 8
+  float gsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < K) has |= (ti[j] == e);
-    const uint64_t m = __ballot(live && has);
-    if (lane == 0) masks[e] = m;
+  for (int r = 0; r < KMAX; ++r)
+    if (r < K) gsum += ts[r];
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      if (r >= K || (r & 7) != j) continue;
+      float g = ts[r];
+      if (a.norm_topk) g = g / gsum;
+      g *= a.routed_scale;
+      a.topk_idx[(size_t)t * K + r] = ti[r];
+      a.topk_w[(size_t)t * K + r] = g;
+      atomicOr(&masks[ti[r]], 1ull << tl);
+    }
   }
   __syncthreads();
-  for (int e = lane; e < E; e += 64)   // layout [E][blocks]
+
+  // e. block histogram and in-block ranks (token order)
+  for (int e = tid; e < E; e += 512)   // layout [E][blocks]
     a.block_counts[(size_t)e * gridDim.x + blockIdx.x] = __popcll(masks[e]);
   if (live) {
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j >= K) break;
-      a.rank[(size_t)t * K + j] = __popcll(masks[ti[j]] & below);
+    for (int r = 0; r < KMAX; ++r) {
+      if (r >= K || (r & 7) != j) continue;
+      a.rank[(size_t)t * K + r] = __popcll(masks[ti[r]] & below);
     }
   }
 }
@@ -554,12 +602,17 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
 
 int router_tokens_per_block(int) { return 64; }
 
+// Waves of the logits kernel for one d-slice.
+static int logits_tiles(int T, int E) {
+  return ((T + 32 * LG_TB - 1) / (32 * LG_TB)) * ((E + 31) / 32);
+}
+
 int router_dsplit(int T, int E, int d, int dtype) {
   if (dtype != 1) return 1;
-  const int tiles = ((T + 31) / 32) * ((E + 31) / 32);
+  const int tiles = logits_tiles(T, E);
   int ds = 1;
-  // aim for ~4096 waves; every slice a multiple of 64 columns
-  while (tiles * ds * 2 <= 4096 && (d % (ds * 2 * 64)) == 0 && ds < 16) ds *= 2;
+  // aim for ~1024 waves (one per SIMD); every slice a multiple of 64 columns
+  while (tiles * ds * 2 <= 1024 && (d % (ds * 2 * 64)) == 0 && ds < 16) ds *= 2;
   return ds;
 }
 
@@ -569,7 +622,7 @@ bool router_fused(int E, int K, int n_groups, int dtype) {
 
 hipError_t launch_logits(const LogitsArgs& la, hipStream_t s) {
   if (la.T == 0) return hipSuccess;
-  const int tiles = ((la.T + 31) / 32) * ((la.E + 31) / 32) * la.ds;
+  const int tiles = logits_tiles(la.T, la.E) * la.ds;
   hipLaunchKernelGGL(logits_mfma_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s, la);
   return hipGetLastError();
 }
@@ -593,7 +646,7 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
                        r.w_gate, r.planes, n);
     la.x = static_cast<const bf16_t*>(r.x);
     la.planes = r.planes;
-    const int tiles = ((r.T + 31) / 32) * ((r.E + 31) / 32) * r.ds;
+    const int tiles = logits_tiles(r.T, r.E) * r.ds;
     hipLaunchKernelGGL(logits_mfma_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s, la);
   } else {
     la.xf = static_cast<const float*>(r.x);
@@ -613,8 +666,8 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
   sa.block_counts = r.block_counts;
   const dim3 grid((r.T + 63) / 64);
   const size_t lds = (size_t)64 * (r.E + 1) * sizeof(float);
-  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(256), lds, s, sa);
-  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(256), lds, s, sa);
+  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(512), lds, s, sa);
+  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(512), lds, s, sa);
   return hipGetLastError();
 }
 
