@@ -184,15 +184,16 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 // the block's logits (sum of the d-slice partials in slice order, plus the
 // logit bias), then each token takes eight adjacent lanes, lane j over the
 // j-th contiguous eighth of the experts:
-//  a. scores in fp32: softmax (max and sum over the eight lanes; the
-//     exponentials are stored and divided on use) or sigmoid;
+//  a. scores in fp32, softmax (max and sum over the eight lanes) or
+//     sigmoid, and the selection keys (score + selection bias), kept in the
+//     lane's registers (at most 32 experts per lane);
 //  b. group limit: each group's score is the sum of its two best keys (its
 //     best key for groups of one expert), merged over the lanes, and the
 //     topk_groups best groups are kept (ties to the lower group index);
-//  c. top-K by K rounds: each lane offers its best untaken kept expert, the
-//     eight offers are merged, and the round's winner (key descending, index
-//     ascending) is the next kept expert -- the same total order as a sorted
-//     scan over all experts;
+//  c. top-K by K rounds: each lane offers its best expert still available
+//     (in a kept group, not yet taken), the eight offers are merged, and the
+//     round's winner (key descending, index ascending) is the next kept
+//     expert -- the same total order as a sorted scan over all experts;
 //  d. gate weights from the kept scores in selection order;
 //  e. block histogram and in-block ranks: every kept (token, expert) ORs the
 //     token's bit into the expert's 64-bit LDS mask (order-free, so
@@ -237,52 +238,63 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
   const int tl = tid >> 3;                    // token in the block
   const int t = t0 + tl;
   const bool live = tl < ntok;
-  float* my = lg + (live ? tl : 0) * ld;      // dead tokens shadow row 0 (read only)
-  const int C = (E + 7) / 8;                  // experts per lane (at most 32)
+  const float* my = lg + (live ? tl : 0) * ld;   // dead tokens shadow row 0
+  constexpr int CM = MAX_EXPERTS / 8;         // experts per lane, at most
+  const int C = (E + 7) / 8;
   const int e0 = min(E, j * C), e1 = min(E, e0 + C);
   auto xor8 = [](float v, int m) { return __shfl_xor(v, m, 8); };
 
-  // a. scores
-  float z = 1.f;
+  // a. scores and keys of the lane's experts, in registers
+  float sv[CM], kv[CM];
+#pragma unroll
+  for (int i = 0; i < CM; ++i) sv[i] = (e0 + i < e1) ? my[e0 + i] : 0.f;
   if (a.score == 0) {
     float mx = -INFINITY;
-    for (int e = e0; e < e1; ++e) mx = fmaxf(mx, my[e]);
+#pragma unroll
+    for (int i = 0; i < CM; ++i)
+      if (e0 + i < e1) mx = fmaxf(mx, sv[i]);
     mx = fmaxf(mx, xor8(mx, 1));
     mx = fmaxf(mx, xor8(mx, 2));
     mx = fmaxf(mx, xor8(mx, 4));
-    float zs = 0.f;
-    for (int e = e0; e < e1; ++e) {
-      const float v = expf(my[e] - mx);
-      zs += v;
-      if (live) my[e] = v;
-    }
-    zs += xor8(zs, 1);
-    zs += xor8(zs, 2);
-    zs += xor8(zs, 4);
-    z = zs;
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < CM; ++i)
+      if (e0 + i < e1) {
+        sv[i] = expf(sv[i] - mx);
+        z += sv[i];
+      }
+    z += xor8(z, 1);
+    z += xor8(z, 2);
+    z += xor8(z, 4);
+#pragma unroll
+    for (int i = 0; i < CM; ++i) sv[i] = sv[i] / z;
   } else {
-    for (int e = e0; e < e1; ++e) {
-      const float v = 1.f / (1.f + expf(-my[e]));
-      if (live) my[e] = v;
-    }
+#pragma unroll
+    for (int i = 0; i < CM; ++i) sv[i] = 1.f / (1.f + expf(-sv[i]));
   }
-  auto score = [&](int e) -> float { return a.score == 0 ? my[e] / z : my[e]; };
-  auto key_of = [&](int e, float sc) -> float {
-    const float k = sc + sbias[e];
-    return (k != k) ? -INFINITY : k;     // NaN never outranks a score
-  };
+#pragma unroll
+  for (int i = 0; i < CM; ++i) {
+    const float k = sv[i] + ((e0 + i < e1) ? sbias[e0 + i] : 0.f);
+    kv[i] = (k != k) ? -INFINITY : k;     // NaN never outranks a score
+  }
 
-  // b. group limit: bitmask of the kept groups
+  // b. group limit: bitmask of the kept groups, then the lane's kept experts
   uint64_t keep = ~0ull;
   int gsz = E;
+  uint32_t avail = 0;                         // bit i: expert e0 + i may be kept
   if (a.n_groups > 1) {
     gsz = E / a.n_groups;
+    const int g_lo = e0 / gsz, g_hi = (e1 > e0) ? (e1 - 1) / gsz : g_lo - 1;
     for (int g = 0; g < a.n_groups; ++g) {
       float b1 = -INFINITY, b2 = -INFINITY;
-      const int lo = max(e0, g * gsz), hi_e = min(e1, (g + 1) * gsz);
-      for (int e = lo; e < hi_e; ++e) {
-        const float kv = key_of(e, score(e));
-        if (kv > b1) { b2 = b1; b1 = kv; } else if (kv > b2) { b2 = kv; }
+      if (g >= g_lo && g <= g_hi) {
+        const int lo = g * gsz - e0, hi_i = (g + 1) * gsz - e0;
+#pragma unroll
+        for (int i = 0; i < CM; ++i) {
+          if (i < lo || i >= hi_i || e0 + i >= e1) continue;
+          const float k = kv[i];
+          if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+        }
       }
 #pragma unroll
       for (int m = 1; m < 8; m <<= 1) {   // top two of both lanes' top two
@@ -294,8 +306,6 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
       if (j == 0) gsc[tl][g] = (gsz > 1) ? b1 + b2 : b1;
     }
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     keep = 0;
     for (int r = 0; r < a.topk_groups; ++r) {
       float bk = -INFINITY;
@@ -307,25 +317,31 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
       }
       keep |= 1ull << bi;
     }
+    for (int g = g_lo; g <= g_hi; ++g) {
+      if (!((keep >> g) & 1)) continue;
+      const int lo = max(0, g * gsz - e0), hi_i = min(e1 - e0, (g + 1) * gsz - e0);
+      avail |= (uint32_t)((hi_i >= 32 ? ~0ull : ((1ull << hi_i) - 1)) & ~((1ull << lo) - 1));
+    }
+  } else {
+    const int n = e1 - e0;
+    avail = (n >= 32) ? ~0u : ((1u << n) - 1);
   }
 
-  // c. top-K: K rounds of the best untaken kept expert over the eight lanes
+  // c. top-K: K rounds of the best available expert over the eight lanes
   float ts[KMAX];
   int ti[KMAX];
-  uint32_t taken = 0;                         // bit e - e0: kept already
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
     ts[r] = 0.f;
     ti[r] = 0x7fffffff;
     if (r >= K) continue;
+    // the lane's best: increasing index, so a tie keeps the lower index
     float bk = -INFINITY, bs = 0.f;
     int bi = 0x7fffffff;
-    for (int e = e0; e < e1; ++e) {
-      if ((taken >> (e - e0)) & 1) continue;
-      if (!((keep >> (e / gsz)) & 1)) continue;
-      const float sc = score(e);
-      const float kv = key_of(e, sc);
-      if (better(kv, e, bk, bi)) { bk = kv; bi = e; bs = sc; }
+#pragma unroll
+    for (int i = 0; i < CM; ++i) {
+      if (!((avail >> i) & 1)) continue;
+      if (bi == 0x7fffffff || kv[i] > bk) { bk = kv[i]; bs = sv[i]; bi = e0 + i; }
     }
 #pragma unroll
     for (int m = 1; m < 8; m <<= 1) {
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
     }
     ts[r] = bs;
     ti[r] = bi;
-    if (bi >= e0 && bi < e1) taken |= 1u << (bi - e0);
+    if (bi >= e0 && bi < e1) avail &= ~(1u << (bi - e0));
   }
 
   // d. gate weights; lane j writes the slots r = j mod 8
