@@ -16,12 +16,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
 }
 
 // Round-to-nearest-even fp32 -> bf16 (NaN stays a quiet NaN).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the hardware
+// conversion (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
-    return static_cast<bf16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 // Load one element as fp32 / store fp32 as the element type.
