@@ -87,7 +87,7 @@ hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
 int router_tokens_per_block(int T);   // tokens per histogram block
 int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 // True when logits and selection run fused (no partial-logit buffer).
-bool router_fused(int E, int K, int n_groups, int dtype);
+bool router_fused(int T, int E, int K, int n_groups, int dtype);
 
 struct ScanArgs {
   const int32_t* block_counts; int32_t* block_base; int32_t* counts;

@@ -121,7 +121,7 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
   L.planes = bf16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
-  L.plog = router_fused(d.n_routed, d.top_k, d.n_groups, bf16 ? 1 : 0)
+  L.plog = router_fused(d.T, d.n_routed, d.top_k, d.n_groups, bf16 ? 1 : 0)
                ? -1 : take((int64_t)L.ds * d.T * L.ep * 4);
   L.total = off;
   return L;
