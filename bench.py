@@ -392,9 +392,16 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Stage breakdown from a traced pass of as many steps: a traced call runs
+    # the stages one after the other on the layer's stream (an untraced call
+    # of a weight-streaming bf16 layer runs the shared experts concurrently).
+    log(f"[bench] traced pass {args.steps} steps")
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
     stage_ms = {n: 0.0 for n in names}
     total_ev = 0.0
     for ev in events:

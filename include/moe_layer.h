@@ -24,10 +24,17 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP), row-major, densely packed,
  *    unless stated otherwise.  The caller owns all memory; the library never
- *    allocates or frees device memory and keeps no global state, so calls on
+ *    allocates or frees device memory.  Its only state is one side stream and
+ *    two events per host thread and device, created on first use (see
+ *    moe_layer_forward) and kept until the process ends, so calls on
  *    different streams may run concurrently (with distinct workspaces).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
+ *    For bf16 layers with shared experts whose routed experts average fewer
+ *    than 192 rows (weight-streaming tiles of at most 128 rows), the untraced
+ *    forward runs the shared experts on the side stream, forked from `stream`
+ *    at the start of the call and joined back before the final combine; the
+ *    call as a whole stays ordered on `stream`, under stream capture too.
  *  - Validation errors are returned before anything is enqueued.  A failed
  *    kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise reproducible for identical inputs and shapes (no
@@ -190,7 +197,9 @@ const char* moe_layer_trace_stage_name(int32_t i);
 /* moe_layer_forward, with hipEvent_t events[i] recorded on `stream` before
  * stage i and events[n] after the last stage (n = stage count), so the
  * caller can time every stage.  `events` holds n + 1 created events
- * (MOE_ERR_INVALID_ARG if n_events is smaller).  Otherwise identical. */
+ * (MOE_ERR_INVALID_ARG if n_events is smaller).  Every stage runs in order
+ * on `stream` (no side stream); the results are bitwise equal to the
+ * untraced call's.  Otherwise identical. */
 moe_status_t moe_layer_forward_traced(
     const moe_layer_desc_t* desc, const void* x, const float* w_gate,
     const float* logit_bias, const float* select_bias,

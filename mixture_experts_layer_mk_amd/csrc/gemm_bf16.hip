@@ -399,6 +399,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
     // shared experts first, then the kept experts in slot order, each Y
     // element decoded as fp16 times its group's inverse scale).  The kept
     // experts' rows are fetched one slot ahead, their row indices two ahead.
+    // Without out2 the tile writes S = x + shared experts (fp32) to out
+    // instead, for the separate combine.
     bf16_t* out = static_cast<bf16_t*>(a.out2);
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
     const uint16_t* ybuf = static_cast<const uint16_t*>(a.ybuf);
@@ -427,6 +429,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
           o[nb][g][2] = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
           o[nb][g][3] = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
         }
+      if (!out) {   // combine not fused: S = x + shared experts in fp32 to a.out
+        float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+            if (n >= a.d) continue;
+            *reinterpret_cast<float4*>(srow + n) =
+                make_float4(o[nb][g][0], o[nb][g][1], o[nb][g][2], o[nb][g][3]);
+          }
+        continue;
+      }
       // Scale group of column block nb: columns nb*32 .. nb*32+31 of the
       // wave's range lie in one 64-column group.
       int sgrp[NB];

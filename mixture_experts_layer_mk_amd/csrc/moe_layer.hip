@@ -1,10 +1,14 @@
 // Host side of the C ABI (include/moe_layer.h): validation, workspace
 // layout, and the kernel sequence of one layer forward pass, enqueued on the
 // caller's stream with no host synchronisation and no device allocation.
+// Layers whose routed experts stream their weights run the shared experts on
+// a side stream (one per host thread and device, created on first use),
+// forked from and joined back into the caller's stream.
 #include "moe_layer.h"
 
 #include <cmath>
 #include <cstring>
+#include <unordered_map>
 
 #include "common.h"
 
@@ -43,6 +47,39 @@ int choose_bm(const moe_layer_desc_t& d) {
   if (avg >= 192) return 256;
   if (avg >= 96) return 128;
   return 64;
+}
+
+// The shared experts run concurrently with the router, the dispatch and the
+// routed experts (their combine then separate, on S = x + shared experts in
+// fp32) for bf16 layers whose routed tiles are at most 128 rows: there the
+// routed GEMMs stream weights and the shared GEMMs alone fill few CUs.
+bool concurrent_shared(const moe_layer_desc_t& d, int bm) {
+  return d.dtype == MOE_BF16 && d.n_shared > 0 && bm < 256;
+}
+
+// Side stream and the fork / join events, per host thread and device (so
+// concurrent host threads never share them); never destroyed.  Default
+// priority, non-blocking with respect to the legacy default stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+SideStream* side_stream() {
+  thread_local std::unordered_map<int, SideStream> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  auto it = cache.find(dev);
+  if (it != cache.end()) return &it->second;
+  SideStream ss;
+  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    (void)hipStreamDestroy(ss.s);
+    return nullptr;
+  }
+  return &cache.emplace(dev, ss).first->second;
 }
 
 moe_status_t validate(const moe_layer_desc_t* d) {
@@ -117,7 +154,8 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.y_scale = bf16 ? take(TK * (d.d / Y_GROUP) * 4) : -1;
   // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
   // layers fuse the combine into the shared down-projection.
-  L.s = (d.n_shared > 0 && d.dtype == MOE_F32) ? take((int64_t)d.T * d.d * 4) : -1;
+  L.s = (d.n_shared > 0 && (d.dtype == MOE_F32 || concurrent_shared(d, L.bm)))
+            ? take((int64_t)d.T * d.d * 4) : -1;
   L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
   L.planes = bf16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
@@ -252,18 +290,42 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     if (err != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
-  st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
-                      s, mark);
-  if (st != MOE_OK) return st;
   MTile* tiles = static_cast<MTile*>(at(L.tiles));
   int32_t* n_tiles = static_cast<int32_t*>(at(L.n_tiles));
-  auto gemm = [&](const GemmArgs& g) {
-    return fp8 ? launch_gemm_fp8(g, s) : bf16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+  auto gemm_on = [&](const GemmArgs& g, hipStream_t st_) {
+    return fp8 ? launch_gemm_fp8(g, st_) : bf16 ? launch_gemm_bf16(g, st_)
+                                                : launch_gemm_f32(g, st_);
   };
+  auto gemm = [&](const GemmArgs& g) { return gemm_on(g, s); };
   const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
   GemmArgs base{};
   base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
   base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
+
+  // Shared experts on the side stream (untraced calls of weight-streaming
+  // bf16 layers): fork, shared gate/up and shared down -> S, join before the
+  // combine.  The shared stages touch only x, the shared weights, h_shared
+  // and S, which nothing on the caller's stream touches before the join.
+  SideStream* side = (!events && concurrent_shared(d, L.bm)) ? side_stream() : nullptr;
+  if (side) {
+    MOE_CHECK(hipEventRecord(side->fork, s));
+    MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
+    GemmArgs g = base;
+    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
+    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.h_shared); g.ldo = (int)ksi;
+    MOE_CHECK(gemm_on(g, side->s));
+    GemmArgs h = base;
+    h.mode = 2; h.a = at(L.h_shared); h.lda = (int)ksi;
+    h.w2 = shared.w2; h.inner = d.shared_inner; h.n_experts = d.n_shared;
+    h.out = at(L.s); h.ldo = d.d;   // S; no out2: the combine runs separately
+    MOE_CHECK(gemm_on(h, side->s));
+    MOE_CHECK(hipEventRecord(side->join, side->s));
+  }
+
+  st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
+                      s, mark);
+  if (st != MOE_OK) return st;
   // 4. routed gate/up
   if (!mark(3)) return MOE_ERR_HIP;
   {
@@ -282,7 +344,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   }
   // 5. shared gate/up
   if (!mark(4)) return MOE_ERR_HIP;
-  if (d.n_shared > 0) {
+  if (d.n_shared > 0 && !side) {
     GemmArgs g = base;
     g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
     g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
@@ -310,9 +372,11 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     MOE_CHECK(gemm(g));
   }
   // 7. shared down (+ residual); for bf16 layers the combine is fused here
+  // (not with the side stream: there the join comes first)
   if (!mark(6)) return MOE_ERR_HIP;
-  const bool fused = bf16 && d.n_shared > 0;
-  if (d.n_shared > 0) {
+  const bool fused = bf16 && d.n_shared > 0 && !side;
+  if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
+  if (d.n_shared > 0 && !side) {
     GemmArgs g = base;
     g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;
     g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;

@@ -83,6 +83,29 @@ def test_deterministic_bitwise():
         assert torch.equal(r1[k], r2[k])
 
 
+@pytest.mark.parametrize("name", ["skewed-16b-small", "v3-d512-T700"])
+def test_side_stream_matches_in_order(name):
+    """Weight-streaming bf16 layers with shared experts run the shared experts
+    on a side stream when the call is not traced (S = x + shared experts in
+    fp32, then the separate combine); a traced call runs every stage in order
+    with the combine fused into the shared down-projection.  Both add the
+    same fp32 terms in the same order, so the outputs are bitwise equal, on
+    repeated calls too (the side stream's writes of one call never overtake
+    the previous call's combine)."""
+    from mixture_experts_layer_mk_amd import HipEvents, trace_stage_names
+    case = Case(REDUCED[name])
+    ev = HipEvents(len(trace_stage_names()) + 1)
+    try:
+        traced, _ = case.run_gpu(trace_events=ev.handles)
+        traced = traced.clone()
+        outs = [case.run_gpu()[0].clone() for _ in range(3)]
+        torch.cuda.synchronize()
+    finally:
+        ev.close()
+    for o in outs:
+        assert torch.equal(o, traced)
+
+
 def test_intermediates_dispatch_exact():
     """Counts, offsets and the expert-contiguous permutation are integers and
     copies: exact against the oracle's dispatch of the GPU's own choices."""
