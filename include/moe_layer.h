@@ -30,11 +30,13 @@
  *    different streams may run concurrently (with distinct workspaces).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
- *    For bf16 layers with shared experts whose routed experts average fewer
- *    than 192 rows (weight-streaming tiles of at most 128 rows), the untraced
- *    forward runs the shared experts on the side stream, forked from `stream`
- *    at the start of the call and joined back before the final combine; the
- *    call as a whole stays ordered on `stream`, under stream capture too.
+ *    For bf16 layers with shared experts the untraced forward runs the
+ *    shared experts on the side stream, forked from `stream` at the start of
+ *    the call and joined back before the combine: all of them when the routed
+ *    experts average fewer than 192 rows (weight-streaming tiles of at most
+ *    128 rows; the combine then runs separately), otherwise their gate/up
+ *    projection only.  The call as a whole stays ordered on `stream`, under
+ *    stream capture too.
  *  - Validation errors are returned before anything is enqueued.  A failed
  *    kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise reproducible for identical inputs and shapes (no

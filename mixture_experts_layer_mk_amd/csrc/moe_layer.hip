@@ -1,9 +1,10 @@
 // Host side of the C ABI (include/moe_layer.h): validation, workspace
 // layout, and the kernel sequence of one layer forward pass, enqueued on the
 // caller's stream with no host synchronisation and no device allocation.
-// Layers whose routed experts stream their weights run the shared experts on
-// a side stream (one per host thread and device, created on first use),
-// forked from and joined back into the caller's stream.
+// bf16 layers run the shared experts (weight-streaming layers) or their
+// gate/up (the others) on a side stream (one per host thread and device,
+// created on first use), forked from and joined back into the caller's
+// stream.
 #include "moe_layer.h"
 
 #include <cmath>
@@ -307,6 +308,22 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   // combine.  The shared stages touch only x, the shared weights, h_shared
   // and S, which nothing on the caller's stream touches before the join.
   SideStream* side = (!events && concurrent_shared(d, L.bm)) ? side_stream() : nullptr;
+  // Other bf16 layers with shared experts: only the shared gate/up on the
+  // side stream (it fills the router's and the routed GEMMs' idle CUs), the
+  // fused combine stays in the shared down-projection after the join
+  // (16B-shaped layer -1%, 2B-shaped -1 to -5%).
+  SideStream* side_gu = (!events && !side && d.dtype == MOE_BF16 && d.n_shared > 0)
+                            ? side_stream() : nullptr;
+  if (side_gu) {
+    MOE_CHECK(hipEventRecord(side_gu->fork, s));
+    MOE_CHECK(hipStreamWaitEvent(side_gu->s, side_gu->fork, 0));
+    GemmArgs g = base;
+    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
+    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.h_shared); g.ldo = (int)ksi;
+    MOE_CHECK(gemm_on(g, side_gu->s));
+    MOE_CHECK(hipEventRecord(side_gu->join, side_gu->s));
+  }
   if (side) {
     MOE_CHECK(hipEventRecord(side->fork, s));
     MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
@@ -344,7 +361,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   }
   // 5. shared gate/up
   if (!mark(4)) return MOE_ERR_HIP;
-  if (d.n_shared > 0 && !side) {
+  if (d.n_shared > 0 && !side && !side_gu) {
     GemmArgs g = base;
     g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
     g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
@@ -376,6 +393,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   if (!mark(6)) return MOE_ERR_HIP;
   const bool fused = bf16 && d.n_shared > 0 && !side;
   if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
+  if (side_gu) MOE_CHECK(hipStreamWaitEvent(s, side_gu->join, 0));
   if (d.n_shared > 0 && !side) {
     GemmArgs g = base;
     g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;

@@ -83,15 +83,16 @@ def test_deterministic_bitwise():
         assert torch.equal(r1[k], r2[k])
 
 
-@pytest.mark.parametrize("name", ["skewed-16b-small", "v3-d512-T700"])
+@pytest.mark.parametrize("name", ["skewed-16b-small", "v3-d512-T700", "16b-T2600"])
 def test_side_stream_matches_in_order(name):
-    """Weight-streaming bf16 layers with shared experts run the shared experts
-    on a side stream when the call is not traced (S = x + shared experts in
-    fp32, then the separate combine); a traced call runs every stage in order
-    with the combine fused into the shared down-projection.  Both add the
-    same fp32 terms in the same order, so the outputs are bitwise equal, on
-    repeated calls too (the side stream's writes of one call never overtake
-    the previous call's combine)."""
+    """bf16 layers with shared experts run them on a side stream when the
+    call is not traced: weight-streaming layers all of the shared experts
+    (S = x + shared experts in fp32, then the separate combine), the others
+    (16b-T2600: 256-row tiles) the shared gate/up only.  A traced call runs
+    every stage in order with the combine fused into the shared
+    down-projection.  Both add the same fp32 terms in the same order, so the
+    outputs are bitwise equal, on repeated calls too (the side stream's
+    writes of one call never overtake the previous call's reads)."""
     from mixture_experts_layer_mk_amd import HipEvents, trace_stage_names
     case = Case(REDUCED[name])
     ev = HipEvents(len(trace_stage_names()) + 1)
