@@ -25,18 +25,16 @@
  *  - All tensor pointers are DEVICE pointers (HIP), row-major, densely packed,
  *    unless stated otherwise.  The caller owns all memory; the library never
  *    allocates or frees device memory.  Its only state is one side stream and
- *    two events per host thread and device, created on first use (see
- *    moe_layer_forward) and kept until the process ends, so calls on
+ *    two events per host thread and device, created on first use by a bf16
+ *    forward with shared experts and kept until the process ends, so calls on
  *    different streams may run concurrently (with distinct workspaces).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
  *    For bf16 layers with shared experts the untraced forward runs the
  *    shared experts on the side stream, forked from `stream` at the start of
- *    the call and joined back before the combine: all of them when the routed
- *    experts average fewer than 192 rows (weight-streaming tiles of at most
- *    128 rows; the combine then runs separately), otherwise their gate/up
- *    projection only.  The call as a whole stays ordered on `stream`, under
- *    stream capture too.
+ *    the call and joined back before the combine (which then runs as its own
+ *    kernel).  The call as a whole stays ordered on `stream`, under stream
+ *    capture too.
  *  - Validation errors are returned before anything is enqueued.  A failed
  *    kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise reproducible for identical inputs and shapes (no

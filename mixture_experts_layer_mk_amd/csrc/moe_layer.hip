@@ -1,10 +1,9 @@
 // Host side of the C ABI (include/moe_layer.h): validation, workspace
 // layout, and the kernel sequence of one layer forward pass, enqueued on the
 // caller's stream with no host synchronisation and no device allocation.
-// bf16 layers run the shared experts (weight-streaming layers) or their
-// gate/up (the others) on a side stream (one per host thread and device,
-// created on first use), forked from and joined back into the caller's
-// stream.
+// bf16 layers run the shared experts on a side stream (one per host thread
+// and device, created on first use), forked from and joined back into the
+// caller's stream.
 #include "moe_layer.h"
 
 #include <cmath>
@@ -50,12 +49,13 @@ int choose_bm(const moe_layer_desc_t& d) {
   return 64;
 }
 
-// The shared experts run concurrently with the router, the dispatch and the
-// routed experts (their combine then separate, on S = x + shared experts in
-// fp32) for bf16 layers whose routed tiles are at most 128 rows: there the
-// routed GEMMs stream weights and the shared GEMMs alone fill few CUs.
-bool concurrent_shared(const moe_layer_desc_t& d, int bm) {
-  return d.dtype == MOE_BF16 && d.n_shared > 0 && bm < 256;
+// The shared experts of bf16 layers run concurrently with the router, the
+// dispatch and the routed experts (their combine then separate, on S = x +
+// shared experts in fp32).  Measured against the in-order sequence with the
+// combine fused into the shared down-projection: skewed 128-token batch
+// -16%, V3-shaped -3.6%, 2B-shaped -5%, 16B-shaped even.
+bool concurrent_shared(const moe_layer_desc_t& d) {
+  return d.dtype == MOE_BF16 && d.n_shared > 0;
 }
 
 // Side stream and the fork / join events, per host thread and device (so
@@ -155,7 +155,7 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.y_scale = bf16 ? take(TK * (d.d / Y_GROUP) * 4) : -1;
   // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
   // layers fuse the combine into the shared down-projection.
-  L.s = (d.n_shared > 0 && (d.dtype == MOE_F32 || concurrent_shared(d, L.bm)))
+  L.s = (d.n_shared > 0 && (d.dtype == MOE_F32 || concurrent_shared(d)))
             ? take((int64_t)d.T * d.d * 4) : -1;
   L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
@@ -303,27 +303,10 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
   base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
 
-  // Shared experts on the side stream (untraced calls of weight-streaming
-  // bf16 layers): fork, shared gate/up and shared down -> S, join before the
-  // combine.  The shared stages touch only x, the shared weights, h_shared
+  // Shared experts on the side stream (untraced calls of bf16 layers):
+  // fork, shared gate/up and shared down -> S, join before the combine.  The shared stages touch only x, the shared weights, h_shared
   // and S, which nothing on the caller's stream touches before the join.
-  SideStream* side = (!events && concurrent_shared(d, L.bm)) ? side_stream() : nullptr;
-  // Other bf16 layers with shared experts: only the shared gate/up on the
-  // side stream (it fills the router's and the routed GEMMs' idle CUs), the
-  // fused combine stays in the shared down-projection after the join
-  // (16B-shaped layer -1%, 2B-shaped -1 to -5%).
-  SideStream* side_gu = (!events && !side && d.dtype == MOE_BF16 && d.n_shared > 0)
-                            ? side_stream() : nullptr;
-  if (side_gu) {
-    MOE_CHECK(hipEventRecord(side_gu->fork, s));
-    MOE_CHECK(hipStreamWaitEvent(side_gu->s, side_gu->fork, 0));
-    GemmArgs g = base;
-    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
-    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-    g.out = at(L.h_shared); g.ldo = (int)ksi;
-    MOE_CHECK(gemm_on(g, side_gu->s));
-    MOE_CHECK(hipEventRecord(side_gu->join, side_gu->s));
-  }
+  SideStream* side = (!events && concurrent_shared(d)) ? side_stream() : nullptr;
   if (side) {
     MOE_CHECK(hipEventRecord(side->fork, s));
     MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
@@ -361,7 +344,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   }
   // 5. shared gate/up
   if (!mark(4)) return MOE_ERR_HIP;
-  if (d.n_shared > 0 && !side && !side_gu) {
+  if (d.n_shared > 0 && !side) {
     GemmArgs g = base;
     g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
     g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
@@ -393,7 +376,6 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   if (!mark(6)) return MOE_ERR_HIP;
   const bool fused = bf16 && d.n_shared > 0 && !side;
   if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
-  if (side_gu) MOE_CHECK(hipStreamWaitEvent(s, side_gu->join, 0));
   if (d.n_shared > 0 && !side) {
     GemmArgs g = base;
     g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;

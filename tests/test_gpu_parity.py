@@ -86,11 +86,10 @@ def test_deterministic_bitwise():
 @pytest.mark.parametrize("name", ["skewed-16b-small", "v3-d512-T700", "16b-T2600"])
 def test_side_stream_matches_in_order(name):
     """bf16 layers with shared experts run them on a side stream when the
-    call is not traced: weight-streaming layers all of the shared experts
-    (S = x + shared experts in fp32, then the separate combine), the others
-    (16b-T2600: 256-row tiles) the shared gate/up only.  A traced call runs
-    every stage in order with the combine fused into the shared
-    down-projection.  Both add the same fp32 terms in the same order, so the
+    call is not traced (S = x + shared experts in fp32, then the separate
+    combine), for weight-streaming tiles and 256-row tiles (16b-T2600)
+    alike.  A traced call runs every stage in order with the combine fused
+    into the shared down-projection.  Both add the same fp32 terms in the same order, so the
     outputs are bitwise equal, on repeated calls too (the side stream's
     writes of one call never overtake the previous call's reads)."""
     from mixture_experts_layer_mk_amd import HipEvents, trace_stage_names
