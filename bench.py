@@ -210,9 +210,12 @@ def time_fp8(moe, cfg, d, steps, warmup, fpt):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    for i in range(steps):   # stage breakdown: a traced pass (stages in order)
+        step(events[i])
+    torch.cuda.synchronize()
     stage_ms = {n: sum(ev.elapsed_ms(i, i + 1) for ev in events) / steps
                 for i, n in enumerate(names)}
     for ev in events:
@@ -293,9 +296,12 @@ def time_backward(moe, cfg, d, steps, warmup):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    for i in range(steps):   # stage breakdown: a traced pass (stages in order)
+        step(events[i])
+    torch.cuda.synchronize()
     stage_ms = {n: sum(ev.elapsed_ms(i, i + 1) for ev in events) / steps
                 for i, n in enumerate(names)}
     for ev in events:

@@ -348,7 +348,8 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   } else {
     // Combine fused, exactly as in the bf16 layer: out = RNE(x + shared +
     // sum_k g_k Y_k), residual and shared first, then the kept experts in
-    // slot order; kept experts' rows fetched one slot ahead.
+    // slot order; kept experts' rows fetched one slot ahead.  Without out2
+    // the tile writes S = x + shared experts (fp32) to out instead.
     bf16_t* out = static_cast<bf16_t*>(a.out2);
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
     const uint16_t* ybuf = static_cast<const uint16_t*>(a.ybuf);
@@ -377,6 +378,19 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
           o[nb][g][2] = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
           o[nb][g][3] = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
         }
+      if (!out) {   // combine not fused: S = x + shared experts in fp32 to a.out
+        float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+            if (n >= a.d) continue;
+            *reinterpret_cast<float4*>(srow + n) =
+                make_float4(o[nb][g][0], o[nb][g][1], o[nb][g][2], o[nb][g][3]);
+          }
+        continue;
+      }
       int sgrp[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) sgrp[nb] = min(n0 + wn * WN + nb * 32, a.d - 1) / Y_GROUP;

@@ -49,13 +49,13 @@ int choose_bm(const moe_layer_desc_t& d) {
   return 64;
 }
 
-// The shared experts of bf16 layers run concurrently with the router, the
+// The shared experts of bf16 and FP8 layers run concurrently with the router, the
 // dispatch and the routed experts (their combine then separate, on S = x +
 // shared experts in fp32).  Measured against the in-order sequence with the
 // combine fused into the shared down-projection: skewed 128-token batch
 // -16%, V3-shaped -3.6%, 2B-shaped -5%, 16B-shaped even.
 bool concurrent_shared(const moe_layer_desc_t& d) {
-  return d.dtype == MOE_BF16 && d.n_shared > 0;
+  return d.dtype != MOE_F32 && d.n_shared > 0;
 }
 
 // Side stream and the fork / join events, per host thread and device (so
@@ -172,14 +172,27 @@ bool overlaps(const void* a, const void* b, size_t n) {
   return pa < pb + n && pb < pa + n;
 }
 
+// The token rows in E4M3, per 1 x 128 of the hidden dimension (FP8 layers).
+hipError_t quant_x_rows(const moe_layer_desc_t& d, const Layout& L, char* ws, const void* x,
+                        hipStream_t s) {
+  QuantArgs q{};
+  q.src = x; q.src_f32 = 0; q.batch = 1; q.rows = d.T; q.cols = d.d;
+  q.codes = reinterpret_cast<uint8_t*>(ws + L.x_q);
+  q.scales = reinterpret_cast<uint8_t*>(ws + L.x_scale);
+  return launch_quant_rows(q, s);
+}
+
 // Router, per-expert scan and tile schedule, and the row maps (steps 1-3
 // of the forward; the backward re-runs them to recover the same expert
 // choice).  mark(i) records trace event i before step i.
+// (FP8 layers: also the token rows in E4M3 unless quant_x is false, when the
+// caller has quantised them already.)
 template <class Mark>
 moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws,
                             const void* x, const float* w_gate, const float* logit_bias,
                             const float* select_bias, int32_t* idx, float* gw,
-                            int32_t* expert_counts, hipStream_t s, Mark mark) {
+                            int32_t* expert_counts, hipStream_t s, Mark mark,
+                            bool quant_x = true) {
   auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
   const bool bf16 = d.dtype != MOE_F32;
   const bool fp8 = d.dtype == MOE_FP8;
@@ -205,13 +218,7 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
     r.rank = static_cast<int32_t*>(at(L.rank));
     r.block_counts = static_cast<int32_t*>(at(L.block_counts));
     MOE_CHECK(launch_router(r, s));
-    if (fp8) {   // the token rows in E4M3, per 1 x 128 of the hidden dimension
-      QuantArgs q{};
-      q.src = x; q.src_f32 = 0; q.batch = 1; q.rows = d.T; q.cols = d.d;
-      q.codes = static_cast<uint8_t*>(at(L.x_q));
-      q.scales = static_cast<uint8_t*>(at(L.x_scale));
-      MOE_CHECK(launch_quant_rows(q, s));
-    }
+    if (fp8 && quant_x) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
   }
   // 2. scan + tile schedule
   if (!mark(1)) return MOE_ERR_HIP;
@@ -303,28 +310,49 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
   base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
 
-  // Shared experts on the side stream (untraced calls of bf16 layers):
-  // fork, shared gate/up and shared down -> S, join before the combine.  The shared stages touch only x, the shared weights, h_shared
-  // and S, which nothing on the caller's stream touches before the join.
-  SideStream* side = (!events && concurrent_shared(d)) ? side_stream() : nullptr;
-  if (side) {
-    MOE_CHECK(hipEventRecord(side->fork, s));
-    MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
+  // The shared experts' two GEMMs (both paths below).
+  auto shared_gateup = [&]() {
     GemmArgs g = base;
     g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
     g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
     g.out = at(L.h_shared); g.ldo = (int)ksi;
-    MOE_CHECK(gemm_on(g, side->s));
-    GemmArgs h = base;
-    h.mode = 2; h.a = at(L.h_shared); h.lda = (int)ksi;
-    h.w2 = shared.w2; h.inner = d.shared_inner; h.n_experts = d.n_shared;
-    h.out = at(L.s); h.ldo = d.d;   // S; no out2: the combine runs separately
-    MOE_CHECK(gemm_on(h, side->s));
+    if (fp8) {
+      g.a = at(L.x_q);
+      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
+      g.s1 = shared.s1; g.s3 = shared.s3;
+      g.out_scale = static_cast<uint8_t*>(at(L.h_shared_scale)); g.ldo_s = (int)(ksi / 128);
+    }
+    return g;
+  };
+  auto shared_down = [&]() {   // S (fp32) for fp32 layers and the side stream
+    GemmArgs g = base;
+    g.mode = 2; g.a = at(L.h_shared); g.lda = (int)ksi;
+    g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.s); g.ldo = d.d;
+    if (fp8) {
+      g.a_scale = static_cast<const uint8_t*>(at(L.h_shared_scale)); g.lda_s = (int)(ksi / 128);
+      g.s2 = shared.s2;
+    }
+    return g;
+  };
+
+  // Shared experts on the side stream (untraced calls of bf16 and FP8
+  // layers): fork, shared gate/up and shared down -> S, join before the
+  // combine.  The shared stages touch only x (its E4M3 rows for FP8 layers,
+  // quantised before the fork), the shared weights, h_shared and S, which
+  // nothing on the caller's stream touches before the join.
+  SideStream* side = (!events && concurrent_shared(d)) ? side_stream() : nullptr;
+  if (side) {
+    if (fp8) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
+    MOE_CHECK(hipEventRecord(side->fork, s));
+    MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
+    MOE_CHECK(gemm_on(shared_gateup(), side->s));
+    MOE_CHECK(gemm_on(shared_down(), side->s));   // no out2: S; the combine runs separately
     MOE_CHECK(hipEventRecord(side->join, side->s));
   }
 
   st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
-                      s, mark);
+                      s, mark, /*quant_x=*/side == nullptr);
   if (st != MOE_OK) return st;
   // 4. routed gate/up
   if (!mark(3)) return MOE_ERR_HIP;
@@ -344,19 +372,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   }
   // 5. shared gate/up
   if (!mark(4)) return MOE_ERR_HIP;
-  if (d.n_shared > 0 && !side) {
-    GemmArgs g = base;
-    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
-    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-    g.out = at(L.h_shared); g.ldo = d.n_shared * d.shared_inner;
-    if (fp8) {
-      g.a = at(L.x_q);
-      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
-      g.s1 = shared.s1; g.s3 = shared.s3;
-      g.out_scale = static_cast<uint8_t*>(at(L.h_shared_scale)); g.ldo_s = (int)(ksi / 128);
-    }
-    MOE_CHECK(gemm(g));
-  }
+  if (d.n_shared > 0 && !side) MOE_CHECK(gemm(shared_gateup()));
   // 6. routed down
   if (!mark(5)) return MOE_ERR_HIP;
   {
@@ -377,14 +393,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   const bool fused = bf16 && d.n_shared > 0 && !side;
   if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
   if (d.n_shared > 0 && !side) {
-    GemmArgs g = base;
-    g.mode = 2; g.a = at(L.h_shared); g.lda = d.n_shared * d.shared_inner;
-    g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-    g.out = at(L.s); g.ldo = d.d;
-    if (fp8) {
-      g.a_scale = static_cast<const uint8_t*>(at(L.h_shared_scale)); g.lda_s = (int)(ksi / 128);
-      g.s2 = shared.s2;
-    }
+    GemmArgs g = shared_down();
     if (fused) {
       g.ybuf = at(L.y);
       g.yscale = static_cast<float*>(at(L.y_scale));

@@ -83,17 +83,21 @@ def test_deterministic_bitwise():
         assert torch.equal(r1[k], r2[k])
 
 
-@pytest.mark.parametrize("name", ["skewed-16b-small", "v3-d512-T700", "16b-T2600"])
-def test_side_stream_matches_in_order(name):
+@pytest.mark.parametrize("name,dtype", [("skewed-16b-small", None), ("v3-d512-T700", None),
+                                        ("16b-T2600", None), ("16b-T2600", "fp8"),
+                                        ("skewed-16b-small", "fp8")])
+def test_side_stream_matches_in_order(name, dtype):
     """bf16 layers with shared experts run them on a side stream when the
     call is not traced (S = x + shared experts in fp32, then the separate
     combine), for weight-streaming tiles and 256-row tiles (16b-T2600)
-    alike.  A traced call runs every stage in order with the combine fused
+    alike, and for FP8 layers (the E4M3 token rows are quantised before the
+    fork).  A traced call runs every stage in order with the combine fused
     into the shared down-projection.  Both add the same fp32 terms in the same order, so the
     outputs are bitwise equal, on repeated calls too (the side stream's
     writes of one call never overtake the previous call's reads)."""
     from mixture_experts_layer_mk_amd import HipEvents, trace_stage_names
-    case = Case(REDUCED[name])
+    cfg = REDUCED[name] if dtype is None else REDUCED[name].replace(dtype=dtype)
+    case = Case(cfg)
     ev = HipEvents(len(trace_stage_names()) + 1)
     try:
         traced, _ = case.run_gpu(trace_events=ev.handles)
