@@ -63,7 +63,7 @@ bool concurrent_shared(const moe_layer_desc_t& d) {
 // priority, non-blocking with respect to the legacy default stream.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr;
 };
 
 SideStream* side_stream() {
@@ -75,8 +75,10 @@ SideStream* side_stream() {
   SideStream ss;
   if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
   if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming) != hipSuccess) {
     if (ss.fork) (void)hipEventDestroy(ss.fork);
+    if (ss.join) (void)hipEventDestroy(ss.join);
     (void)hipStreamDestroy(ss.s);
     return nullptr;
   }
@@ -593,6 +595,56 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     sb.dw1 = d_shared.dw1; sb.dw3 = d_shared.dw3; sb.dw2 = d_shared.dw2;
   }
 
+  // The shared experts' branch: G_s = dy W2_s; gate/up recomputed with the
+  // SwiGLU backward (dA_s, g h); dx_s; dW2_s and dW1/dW3_s (split k, ordered
+  // reductions).  It needs no routing.  Untraced calls run it on the side
+  // stream (forked here, after the zero row is written): `join` after dx_s
+  // (before the dx combine), `join2` at the end.  It writes only g_s,
+  // h_shared, da_s, dx_s, the split partials and the shared gradients.
+  SideStream* side = (!events && Ks > 0) ? side_stream() : nullptr;
+  auto shared_dh = [&](hipStream_t st_) {
+    BwdGemmArgs g = sb;
+    g.kind = 0; g.c = static_cast<float*>(at(B.g_s)); g.ldc = (int)(Ks * Is);
+    return launch_gemm_bwd(g, st_);
+  };
+  auto shared_gateup = [&](hipStream_t st_) {
+    GemmArgs g{};
+    g.mode = 3; g.d = d.d; g.tiles = static_cast<const MTile*>(at(L.tiles));
+    g.n_tiles = static_cast<const int32_t*>(at(L.n_tiles)); g.max_mtiles = L.max_mtiles;
+    g.T = d.T; g.bm = L.bm; g.x = x;
+    g.shared = true; g.a = x; g.lda = d.d; g.a_rows = nullptr;
+    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
+    g.out = at(L.h_shared); g.ldo = (int)(Ks * Is);
+    g.gin = static_cast<const float*>(at(B.g_s)); g.ldgin = (int)(Ks * Is);
+    g.row_g = nullptr;
+    g.da = static_cast<bf16_t*>(at(B.da_s)); g.ldda = (int)(2 * Ks * Is);
+    g.dg_part = nullptr; g.n_part = 0;
+    return launch_gemm_bf16(g, st_);
+  };
+  auto shared_dx = [&](hipStream_t st_) {
+    BwdGemmArgs g = sb;
+    g.kind = 1; g.c = static_cast<float*>(at(B.dx_s)); g.ldc = d.d;
+    return launch_gemm_bwd(g, st_);
+  };
+  auto shared_dw = [&](int kind, hipStream_t st_) {
+    BwdGemmArgs g = sb;
+    g.part = static_cast<float*>(at(B.part));
+    g.kind = kind; g.splits = kind == 2 ? B.splits2 : B.splits3;
+    return launch_gemm_bwd(g, st_);
+  };
+  if (side) {
+    MOE_CHECK(hipEventRecord(side->fork, s));
+    MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
+    MOE_CHECK(shared_dh(side->s));
+    MOE_CHECK(shared_gateup(side->s));
+    MOE_CHECK(shared_dx(side->s));
+    MOE_CHECK(hipEventRecord(side->join, side->s));
+    MOE_CHECK(shared_dw(2, side->s));
+    MOE_CHECK(shared_dw(3, side->s));
+    MOE_CHECK(hipEventRecord(side->join2, side->s));
+  }
+  const bool in_order = Ks > 0 && !side;
+
   // 1. G = dy W2 of every row (before the gate weight)
   {
     if (!mark(1)) return MOE_ERR_HIP;
@@ -600,11 +652,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     g.kind = 0; g.c = static_cast<float*>(at(B.g_r)); g.ldc = d.inner;
     MOE_CHECK(launch_gemm_bwd(g, s));
     if (!mark(2)) return MOE_ERR_HIP;
-    if (Ks > 0) {
-      g = sb;
-      g.kind = 0; g.c = static_cast<float*>(at(B.g_s)); g.ldc = (int)(Ks * Is);
-      MOE_CHECK(launch_gemm_bwd(g, s));
-    }
+    if (in_order) MOE_CHECK(shared_dh(s));
   }
   // 2. gate/up recomputed with the SwiGLU backward: dA, g h, dg row sums
   {
@@ -622,16 +670,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     g.dg_part = static_cast<float*>(at(B.dg_part)); g.n_part = B.n_part;
     MOE_CHECK(launch_gemm_bf16(g, s));
     if (!mark(4)) return MOE_ERR_HIP;
-    if (Ks > 0) {
-      g.shared = true; g.a_rows = nullptr;
-      g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-      g.out = at(L.h_shared); g.ldo = (int)(Ks * Is);
-      g.gin = static_cast<const float*>(at(B.g_s)); g.ldgin = (int)(Ks * Is);
-      g.row_g = nullptr;
-      g.da = static_cast<bf16_t*>(at(B.da_s)); g.ldda = (int)(2 * Ks * Is);
-      g.dg_part = nullptr; g.n_part = 0;
-      MOE_CHECK(launch_gemm_bf16(g, s));
-    }
+    if (in_order) MOE_CHECK(shared_gateup(s));
   }
   // 3. router: logits again (partial sums), scores, dg, dl, logit-bias and
   // gate gradients
@@ -652,11 +691,8 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     g.kind = 1; g.c = static_cast<float*>(at(B.dx_rows)); g.ldc = d.d;
     MOE_CHECK(launch_gemm_bwd(g, s));
     if (!mark(7)) return MOE_ERR_HIP;
-    if (Ks > 0) {
-      g = sb;
-      g.kind = 1; g.c = static_cast<float*>(at(B.dx_s)); g.ldc = d.d;
-      MOE_CHECK(launch_gemm_bwd(g, s));
-    }
+    if (in_order) MOE_CHECK(shared_dx(s));
+    if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
     if (!mark(8)) return MOE_ERR_HIP;
     MOE_CHECK(launch_dx_combine(aux, s));
   }
@@ -669,18 +705,11 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     if (!mark(10)) return MOE_ERR_HIP;
     g.kind = 3;
     MOE_CHECK(launch_gemm_bwd(g, s));
-    g = sb;
-    g.part = static_cast<float*>(at(B.part));
     if (!mark(11)) return MOE_ERR_HIP;
-    if (Ks > 0) {
-      g.kind = 2; g.splits = B.splits2;
-      MOE_CHECK(launch_gemm_bwd(g, s));
-    }
+    if (in_order) MOE_CHECK(shared_dw(2, s));
     if (!mark(12)) return MOE_ERR_HIP;
-    if (Ks > 0) {
-      g.kind = 3; g.splits = B.splits3;
-      MOE_CHECK(launch_gemm_bwd(g, s));
-    }
+    if (in_order) MOE_CHECK(shared_dw(3, s));
+    if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join2, 0));
   }
   if (!mark(13)) return MOE_ERR_HIP;
 #undef MOE_CHECK

@@ -216,15 +216,18 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
     sbias[e] = a.select_bias ? a.select_bias[e] : 0.f;
     masks[e] = 0ull;
   }
-#pragma unroll 4
   for (int i = tid; i < ntok * q4; i += 512) {
     const int r = i / q4, c = i % q4;
     const size_t o = (size_t)(t0 + r) * q4 + c;
-    float4 v = p4[o];
-    for (int sl = 1; sl < a.ds; ++sl) {
-      const float4 w = p4[o + sl * slice4];
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
+    // all slices' loads in flight first, then the sum in slice order
+    float4 w[16];
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl)
+      if (sl < a.ds) w[sl] = p4[o + sl * slice4];
+    float4 v = w[0];
+#pragma unroll
+    for (int sl = 1; sl < 16; ++sl)
+      if (sl < a.ds) { v.x += w[sl].x; v.y += w[sl].y; v.z += w[sl].z; v.w += w[sl].w; }
     const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -153,6 +153,35 @@ def test_backward_bitwise_reproducible():
         assert torch.equal(a["shared"][j], b["shared"][j])
 
 
+def test_backward_side_stream_matches_in_order():
+    """Untraced backward calls run the shared experts' branch on a side stream
+    (joined before the dx combine and at the end); a traced call runs every
+    stage in order.  Every gradient is bitwise equal, on a repeated call too."""
+    import mixture_experts_layer_mk_amd as moe
+    case = Case(B16.replace(T=600, seed=8))
+    c, d = case.cfg, case.dev
+    dout = torch.from_numpy(workloads.make_inputs(c).dout()).to(torch.bfloat16).cuda()
+    ev = moe.HipEvents(len(moe.backward_stage_names()) + 1)
+
+    def run(events=None):
+        return moe.moe_layer_backward(
+            d["x"], d["w_gate"], d["routed"], d["shared"], c.top_k, dout,
+            score=c.score, norm_topk=c.norm_topk, n_groups=c.n_groups,
+            topk_groups=c.topk_groups, select_bias=d["select_bias"],
+            logit_bias=d["logit_bias"], routed_scale=c.routed_scale, trace_events=events)
+    try:
+        ref = run(ev.handles)
+        outs = [run(), run()]
+        torch.cuda.synchronize()
+    finally:
+        ev.close()
+    for o in outs:
+        assert torch.equal(o["dx"], ref["dx"]) and torch.equal(o["dw_gate"], ref["dw_gate"])
+        for j in range(3):
+            assert torch.equal(o["routed"][j], ref["routed"][j])
+            assert torch.equal(o["shared"][j], ref["shared"][j])
+
+
 def test_backward_no_tokens_gives_zero_weight_gradients():
     import mixture_experts_layer_mk_amd as moe
     case = Case(B16.replace(T=64, d=256, inner=128, shared_inner=128, seed=7))
