@@ -14,6 +14,8 @@ namespace moe {
 
 namespace {
 
+constexpr int CB_K = 8;   // slots whose loads are all issued up front
+
 template <typename T, int VEC, bool BASE_F32, bool Y16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   static_assert(!Y16 || VEC == 8, "fp16 rows are read 8 columns at a time");
@@ -31,6 +33,38 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = ld_f32<T>(b + v);
   }
+  if (Y16 && a.K <= CB_K) {
+    // All slots' row indices and weights, then all their rows and scales in
+    // flight together, then the sums in slot order (as below).
+    int rows[CB_K];
+    float gk[CB_K], inv[CB_K];
+    uint4 hv[CB_K];
+#pragma unroll
+    for (int k = 0; k < CB_K; ++k)
+      if (k < a.K) {
+        rows[k] = a.slot_row[t * a.K + k];
+        gk[k] = a.topk_w[t * a.K + k];
+      }
+#pragma unroll
+    for (int k = 0; k < CB_K; ++k)
+      if (k < a.K) {
+        hv[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.y) +
+                                                (size_t)rows[k] * a.d + n0);
+        inv[k] = a.yscale[(size_t)rows[k] * (a.d / Y_GROUP) + n0 / Y_GROUP];
+      }
+#pragma unroll
+    for (int k = 0; k < CB_K; ++k) {
+      if (k >= a.K) break;
+      const uint32_t w[4] = {hv[k].x, hv[k].y, hv[k].z, hv[k].w};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[v] & 0xffffu));
+        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[v] >> 16));
+        acc[2 * v + 0] = fmaf(gk[k], lo * inv[k], acc[2 * v + 0]);
+        acc[2 * v + 1] = fmaf(gk[k], hi * inv[k], acc[2 * v + 1]);
+      }
+    }
+  } else
   for (int k = 0; k < a.K; ++k) {
     const int q = t * a.K + k;
     const float g = a.topk_w[q];
