@@ -1,0 +1,120 @@
+"""GPU tests of the forward's stream behaviour: bf16 layers with shared
+experts run the shared experts on a side stream (one per host thread and
+device), forked from the caller's stream and joined back into it.
+
+* Stream capture: the call captured into a graph on a side stream of torch's
+  own, replayed several times with eager work and synchronisations in
+  between, gives the eager result bitwise on every replay (the library
+  enqueues no memset or copy, only kernels and event waits).
+* Host threads: two threads, each with its own stream and workspace, calling
+  the layer repeatedly at the same time, give the single-threaded result
+  bitwise (each thread has its own side stream and events).
+"""
+import sys
+import threading
+
+import pytest
+import torch
+
+import workloads
+from parity import Case
+
+pytestmark = pytest.mark.gpu
+C = workloads.CONFIGS
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _forward(case, out, ws):
+    import mixture_experts_layer_mk_amd as moe
+    c, d = case.cfg, case.dev
+    moe.moe_layer_forward(d["x"], d["w_gate"], d["routed"], d["shared"], c.top_k,
+                          score=c.score, norm_topk=c.norm_topk, n_groups=c.n_groups,
+                          topk_groups=c.topk_groups, select_bias=d["select_bias"],
+                          logit_bias=d["logit_bias"], routed_scale=c.routed_scale,
+                          out=out, workspace=ws)
+
+
+def _workspace(case):
+    import mixture_experts_layer_mk_amd as moe
+    c = case.cfg
+    desc = moe.make_desc(c.T, c.d, c.n_routed, c.top_k, c.inner, c.n_shared, c.shared_inner,
+                         n_groups=c.n_groups, topk_groups=c.topk_groups, score=c.score,
+                         norm_topk=c.norm_topk, routed_scale=c.routed_scale, dtype=c.dtype)
+    return torch.empty(moe.workspace_size(desc), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("skewed-16b-small", C["skewed-16b-small"]),
+    ("16b-T2600", C["deepseekmoe-16b"].replace(T=2600, seed=9)),
+])
+def test_forward_graph_capture_replays_match_eager(name, cfg):
+    case = Case(cfg)
+    say(f"[graph] {name}")
+    ws = _workspace(case)
+    ref = torch.empty_like(case.dev["x"])
+    _forward(case, ref, ws)                      # eager; creates the side stream
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _forward(case, out, ws)                  # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _forward(case, out, ws)
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager call"
+        scratch = torch.empty_like(ref)          # eager work between the replays
+        _forward(case, scratch, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, ref)
+    say(f"[graph] {name}: 3 replays equal")
+
+
+def test_forward_concurrent_host_threads():
+    case = Case(C["deepseekmoe-16b"].replace(T=1500, seed=10))
+    ws0 = _workspace(case)
+    ref = torch.empty_like(case.dev["x"])
+    _forward(case, ref, ws0)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            ws = _workspace(case)
+            outs = [torch.empty_like(ref) for _ in range(4)]
+            with torch.cuda.stream(s):
+                for o in outs:
+                    _forward(case, o, ws)
+            s.synchronize()
+            results[k] = outs
+        except Exception as e:   # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == [0, 1]
+    for k in results:
+        for o in results[k]:
+            assert torch.equal(o, ref)
+    say("[threads] 2 threads x 4 calls equal")
