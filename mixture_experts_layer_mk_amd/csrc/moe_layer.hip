@@ -66,22 +66,31 @@ struct SideStream {
   hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr;
 };
 
-SideStream* side_stream() {
+// The side stream of the caller's stream's device (the null stream: the
+// current device); created with that device current.  nullptr on any
+// failure, and the call then runs every stage in order on `s`.
+SideStream* side_stream(hipStream_t s) {
   thread_local std::unordered_map<int, SideStream> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return nullptr;
   auto it = cache.find(dev);
   if (it != cache.end()) return &it->second;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
   SideStream ss;
-  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming) != hipSuccess) {
-    if (ss.fork) (void)hipEventDestroy(ss.fork);
+  bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
     if (ss.join) (void)hipEventDestroy(ss.join);
-    (void)hipStreamDestroy(ss.s);
-    return nullptr;
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    if (ss.s) (void)hipStreamDestroy(ss.s);
   }
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (!ok) return nullptr;
   return &cache.emplace(dev, ss).first->second;
 }
 
@@ -343,7 +352,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   // combine.  The shared stages touch only x (its E4M3 rows for FP8 layers,
   // quantised before the fork), the shared weights, h_shared and S, which
   // nothing on the caller's stream touches before the join.
-  SideStream* side = (!events && concurrent_shared(d)) ? side_stream() : nullptr;
+  SideStream* side = (!events && concurrent_shared(d)) ? side_stream(s) : nullptr;
   if (side) {
     if (fp8) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
     MOE_CHECK(hipEventRecord(side->fork, s));
@@ -601,7 +610,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   // stream (forked here, after the zero row is written): `join` after dx_s
   // (before the dx combine), `join2` at the end.  It writes only g_s,
   // h_shared, da_s, dx_s, the split partials and the shared gradients.
-  SideStream* side = (!events && Ks > 0) ? side_stream() : nullptr;
+  SideStream* side = (!events && Ks > 0) ? side_stream(s) : nullptr;
   auto shared_dh = [&](hipStream_t st_) {
     BwdGemmArgs g = sb;
     g.kind = 0; g.c = static_cast<float*>(at(B.g_s)); g.ldc = (int)(Ks * Is);
