@@ -446,7 +446,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    constexpr int U = 4;   // k-steps of 16 per batch (32 loads in flight)
+    constexpr int U = 2;   // k-steps of 16 per batch; two batches in flight
     int k = 0;
     auto step = [&](const bf16x8 (&xf)[2], const bf16x8 (&w)[2][3]) {
 #pragma unroll
@@ -458,19 +458,37 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
           acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][0], xf[tb], acc[eb][tb], 0, 0, 0);
         }
     };
-    for (; k + 16 * U <= kq; k += 16 * U) {
-      bf16x8 xf[U][2], w[U][2][3];
+    // software pipeline: the loads of batch i+1 are issued before the matrix
+    // ops of batch i (each wave is alone on its SIMD: nothing else hides them)
+    auto load_batch = [&](bf16x8 (&xf)[U][2], bf16x8 (&w)[U][2][3], int kb) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          xf[u][b] = *reinterpret_cast<const bf16x8*>(xp[b] + k + 16 * u);
+          xf[u][b] = *reinterpret_cast<const bf16x8*>(xp[b] + kb + 16 * u);
 #pragma unroll
           for (int p = 0; p < 3; ++p)
-            w[u][b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + k + 16 * u);
+            w[u][b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + kb + 16 * u);
         }
+    };
+    const int nb = kq / (16 * U);                // whole batches
+    if (nb > 0) {
+      bf16x8 xa[U][2], wa[U][2][3], xb[U][2], wb[U][2][3];
+      load_batch(xa, wa, 0);
+      int i = 0;
+      for (; i + 2 <= nb; i += 2) {
+        load_batch(xb, wb, (i + 1) * 16 * U);
 #pragma unroll
-      for (int u = 0; u < U; ++u) step(xf[u], w[u]);
+        for (int u = 0; u < U; ++u) step(xa[u], wa[u]);
+        if (i + 2 < nb) load_batch(xa, wa, (i + 2) * 16 * U);
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(xb[u], wb[u]);
+      }
+      if (i < nb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(xa[u], wa[u]);
+      }
+      k = nb * 16 * U;
     }
     for (; k < kq; k += 16) {
       bf16x8 xf[2], w[2][3];
