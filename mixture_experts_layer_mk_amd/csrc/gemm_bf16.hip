@@ -525,6 +525,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
   // both its token-row tiles and its weight tiles in L2.
   const int ndim = n_tiles_of<MODE, BM>(a);
   int mt, nt;
+  constexpr int NGRP = ngrp_for<BM>();
   {
     const int full = ndim / NGRP;
     const int ntg = L / (mdim * NGRP);

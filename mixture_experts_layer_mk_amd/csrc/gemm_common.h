@@ -80,7 +80,11 @@ __device__ __forceinline__ void sched_groups() {
   }
 }
 
-constexpr int NGRP = 4;   // N-tiles per tile-order group
+// N-tiles per tile-order group, by tile height: BM / 64.  Measured on the
+// layers each height is chosen for: 256-row tiles (16B-shaped) 4, with 2 and 8
+// slower; 128-row tiles (V3-shaped) 2 against 4 -5.6% bf16 and -8% FP8, with 1
+// slower; 64-row tiles (a skewed 128-token batch) 1 against 4 -6%.
+template <int BM> constexpr int ngrp_for() { return BM >= 128 ? BM / 64 : 1; }
 
 // s_waitcnt immediate that waits until at most N vector-memory operations
 // are outstanding (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8],

@@ -461,6 +461,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int ndim = n_tiles_of<MODE, BM>(a);
   int mt, nt;
+  constexpr int NGRP = ngrp_for<BM>();
   {
     const int full = ndim / NGRP;
     const int ntg = L / (mdim * NGRP);
