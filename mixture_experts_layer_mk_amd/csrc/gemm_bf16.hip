@@ -271,20 +271,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       if (m >= rows) continue;
       bf16_t* orow = out + (size_t)(row0 + m) * a.ldo + col_off;
 #pragma unroll
-      for (int nb = 0; nb < HALF_NB; ++nb)
+      for (int nb = 0; nb < HALF_NB; ++nb) {
+        // inner is a multiple of 64: a 32-column block is all in or all out.
+        const int inner = inner0 + wn * (WN / 2) + nb * 32;
+        if (inner >= a.inner) continue;
+        uint32_t p[4][2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int inner = inner0 + wn * (WN / 2) + nb * 32 + 8 * g + 4 * hi;
-          if (inner >= a.inner) continue;
           float h[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             h[q] = silu_f(acc[nb][mb][4 * g + q]) * acc[nb + HALF_NB][mb][4 * g + q];
-          uint2 v;
-          v.x = pack2(h[0], h[1]);
-          v.y = pack2(h[2], h[3]);
-          *reinterpret_cast<uint2*>(orow + inner) = v;
+          p[g][0] = pack2(h[0], h[1]);
+          p[g][1] = pack2(h[2], h[3]);
         }
+        swap_halves(p);
+        store_block(orow + inner + 8 * hi, p);
+      }
     }
   } else if (MODE == 3) {
     // SwiGLU backward on the recomputed pre-activations a1 (W1 half) and a3:
@@ -379,16 +382,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
         if (m >= rows) continue;
         uint16_t* orow = out + (size_t)(row0 + m) * a.ldo;
 #pragma unroll
-        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+          // d is a multiple of 64: a 32-column block is all in or all out.
+          const int n = n0 + wn * WN + nb * 32;
+          if (n >= a.d) continue;
+          uint32_t p[4][2];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-            if (n >= a.d) continue;
-            uint2 v;
-            v.x = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
-            v.y = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
-            *reinterpret_cast<uint2*>(orow + n) = v;
+            p[g][0] = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
+            p[g][1] = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
           }
+          swap_halves(p);
+          store_block(orow + n + 8 * hi, p);
+        }
         const int ng = n0 + wn * WN + gi * Y_GROUP;
         if (hi == 0 && ng < a.d) a.yscale[(size_t)(row0 + m) * gpr + ng / Y_GROUP] = inv;
       }

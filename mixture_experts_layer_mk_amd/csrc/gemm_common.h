@@ -46,6 +46,29 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
+// Lanes l and l + 32 of a wave hold the same output row of a 32-column block:
+// lane half h (0 or 1) has columns 8 g + 4 h + {0, 1} in p[g][0] and {2, 3} in
+// p[g][1], g = 0..3.  Two swaps between the halves (the low half's g = 1 and 3
+// words for the high half's g = 0 and 2 words) leave each lane 8 consecutive
+// columns per pair of g: the low half 0-7 and 16-23, the high half 8-15 and
+// 24-31, as {p[0], p[1]} and {p[2], p[3]}, so the row is written with 16-byte
+// stores.
+__device__ __forceinline__ void swap_halves(uint32_t (&p)[4][2]) {
+#pragma unroll
+  for (int g = 0; g < 4; g += 2)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto r = __builtin_amdgcn_permlane32_swap(p[g][j], p[g + 1][j], false, false);
+      p[g][j] = r[0];
+      p[g + 1][j] = r[1];
+    }
+}
+__device__ __forceinline__ void store_block(void* row_at_8h, const uint32_t (&p)[4][2]) {
+  uint4* q = static_cast<uint4*>(row_at_8h);
+  q[0] = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);   // columns 8 h .. 8 h + 7
+  q[2] = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);   // 16 + 8 h .. 16 + 8 h + 7
+}
+
 __device__ __forceinline__ float h_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
