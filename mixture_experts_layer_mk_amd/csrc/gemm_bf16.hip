@@ -312,11 +312,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       bf16_t* darow = a.da + (size_t)row * a.ldda + da_off;
       float part = 0.f;
 #pragma unroll
-      for (int nb = 0; nb < HALF_NB; ++nb)
+      for (int nb = 0; nb < HALF_NB; ++nb) {
+        // inner is a multiple of 64: a 32-column block is all in or all out.
+        const int ib = inner0 + wn * (WN / 2) + nb * 32;
+        if (ib >= a.inner) continue;
+        uint32_t ph[4][2], p1[4][2], p3[4][2];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int inner = inner0 + wn * (WN / 2) + nb * 32 + 8 * q4 + 4 * hi;
-          if (inner >= a.inner) continue;
+          const int inner = ib + 8 * q4 + 4 * hi;
           const float4 gv = *reinterpret_cast<const float4*>(grow + inner);
           const float gi[4] = {gv.x, gv.y, gv.z, gv.w};
           float hv[4], d1[4], d3[4];
@@ -333,18 +336,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
             d1[q] = dh * a3 * (sg * (1.f + a1 * (1.f - sg)));
             d3[q] = dh * sl;
           }
-          if (!live) continue;
-          uint2 v;
-          v.x = pack2(g * hv[0], g * hv[1]);
-          v.y = pack2(g * hv[2], g * hv[3]);
-          *reinterpret_cast<uint2*>(orow + inner) = v;
-          v.x = pack2(d1[0], d1[1]);
-          v.y = pack2(d1[2], d1[3]);
-          *reinterpret_cast<uint2*>(darow + inner) = v;
-          v.x = pack2(d3[0], d3[1]);
-          v.y = pack2(d3[2], d3[3]);
-          *reinterpret_cast<uint2*>(darow + a.inner + inner) = v;
+          ph[q4][0] = pack2(g * hv[0], g * hv[1]);
+          ph[q4][1] = pack2(g * hv[2], g * hv[3]);
+          p1[q4][0] = pack2(d1[0], d1[1]);
+          p1[q4][1] = pack2(d1[2], d1[3]);
+          p3[q4][0] = pack2(d3[0], d3[1]);
+          p3[q4][1] = pack2(d3[2], d3[3]);
         }
+        swap_halves(ph);
+        swap_halves(p1);
+        swap_halves(p3);
+        if (!live) continue;
+        store_block(orow + ib + 8 * hi, ph);
+        store_block(darow + ib + 8 * hi, p1);
+        store_block(darow + a.inner + ib + 8 * hi, p3);
+      }
       if (routed && a.dg_part) {
         part += __shfl_xor(part, 32);
         if (hi == 0) red[wn * BM + m] = part;
@@ -491,16 +497,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       }
       bf16_t* orow = out + (size_t)t * a.d;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        // d is a multiple of 64: a 32-column block is all in or all out.
+        const int n = n0 + wn * WN + nb * 32;
+        if (n >= a.d) continue;
+        uint32_t p[4][2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-          if (n >= a.d) continue;
-          uint2 v;
-          v.x = pack2(o[nb][g][0], o[nb][g][1]);
-          v.y = pack2(o[nb][g][2], o[nb][g][3]);
-          *reinterpret_cast<uint2*>(orow + n) = v;
+          p[g][0] = pack2(o[nb][g][0], o[nb][g][1]);
+          p[g][1] = pack2(o[nb][g][2], o[nb][g][3]);
         }
+        swap_halves(p);
+        store_block(orow + n + 8 * hi, p);
+      }
     }
   }
 }

@@ -63,6 +63,25 @@ __device__ __forceinline__ void swap_halves(uint32_t (&p)[4][2]) {
       p[g + 1][j] = r[1];
     }
 }
+// The same for one-byte elements: p[g] holds columns 8 g + 4 h .. + 3.  The
+// first round leaves the low half 0-7 and 16-23 (p[0], p[1] and p[2], p[3]),
+// the high half 8-15 and 24-31; the second swaps the low half's 16-23 with the
+// high half's 8-15, so the low half holds columns 0-15 and the high half
+// 16-31, in p[0..3] order.
+__device__ __forceinline__ void swap_halves_bytes(uint32_t (&p)[4]) {
+#pragma unroll
+  for (int g = 0; g < 4; g += 2) {
+    const auto r = __builtin_amdgcn_permlane32_swap(p[g], p[g + 1], false, false);
+    p[g] = r[0];
+    p[g + 1] = r[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(p[j], p[j + 2], false, false);
+    p[j] = r[0];
+    p[j + 2] = r[1];
+  }
+}
 __device__ __forceinline__ void store_block(void* row_at_8h, const uint32_t (&p)[4][2]) {
   uint4* q = static_cast<uint4*>(row_at_8h);
   q[0] = make_uint4(p[0][0], p[0][1], p[1][0], p[1][1]);   // columns 8 h .. 8 h + 7

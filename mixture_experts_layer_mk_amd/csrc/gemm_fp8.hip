@@ -297,15 +297,18 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
       if (m >= rows) continue;
       uint8_t* orow = out + (size_t)(row0 + m) * a.ldo + col_off;
 #pragma unroll
-      for (int nb = 0; nb < HALF_NB; ++nb)
+      for (int nb = 0; nb < HALF_NB; ++nb) {
+        // inner is a multiple of 128: a 32-column block is all in or all out.
+        const int ib = inner0 + wn * (WN / 2) + nb * 32;
+        if (ib >= a.inner) continue;
+        uint32_t p[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int inner = inner0 + wn * (WN / 2) + nb * 32 + 8 * g + 4 * hi;
-          if (inner >= a.inner) continue;
-          *reinterpret_cast<uint32_t*>(orow + inner) =
-              e4m3_pack4(h[mb][nb][g][0] * s, h[mb][nb][g][1] * s, h[mb][nb][g][2] * s,
-                         h[mb][nb][g][3] * s);
-        }
+        for (int g = 0; g < 4; ++g)
+          p[g] = e4m3_pack4(h[mb][nb][g][0] * s, h[mb][nb][g][1] * s, h[mb][nb][g][2] * s,
+                            h[mb][nb][g][3] * s);
+        swap_halves_bytes(p);
+        *reinterpret_cast<uint4*>(orow + ib + 16 * hi) = make_uint4(p[0], p[1], p[2], p[3]);
+      }
       if (wn == 0 && hi == 0)
         a.out_scale[(size_t)(row0 + m) * a.ldo_s + (col_off + inner0) / 128] = (uint8_t)(E + 127);
     }
@@ -331,16 +334,19 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
         if (m >= rows) continue;
         uint16_t* orow = out + (size_t)(row0 + m) * a.ldo;
 #pragma unroll
-        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+          // d is a multiple of 128: a 32-column block is all in or all out.
+          const int n = n0 + wn * WN + nb * 32;
+          if (n >= a.d) continue;
+          uint32_t p[4][2];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-            if (n >= a.d) continue;
-            uint2 v;
-            v.x = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
-            v.y = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
-            *reinterpret_cast<uint2*>(orow + n) = v;
+            p[g][0] = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
+            p[g][1] = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
           }
+          swap_halves(p);
+          store_block(orow + n + 8 * hi, p);
+        }
         const int ng = n0 + wn * WN + gi * Y_GROUP;
         if (hi == 0 && ng < a.d) a.yscale[(size_t)(row0 + m) * gpr + ng / Y_GROUP] = inv;
       }
@@ -432,16 +438,19 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
       }
       bf16_t* orow = out + (size_t)t * a.d;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        // d is a multiple of 128: a 32-column block is all in or all out.
+        const int n = n0 + wn * WN + nb * 32;
+        if (n >= a.d) continue;
+        uint32_t p[4][2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-          if (n >= a.d) continue;
-          uint2 v;
-          v.x = pack2(o[nb][g][0], o[nb][g][1]);
-          v.y = pack2(o[nb][g][2], o[nb][g][3]);
-          *reinterpret_cast<uint2*>(orow + n) = v;
+          p[g][0] = pack2(o[nb][g][0], o[nb][g][1]);
+          p[g][1] = pack2(o[nb][g][2], o[nb][g][3]);
         }
+        swap_halves(p);
+        store_block(orow + n + 8 * hi, p);
+      }
     }
   }
 }
