@@ -428,19 +428,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       const bf16_t* xrow = x + (size_t)t * a.d;
       const int32_t* srt = a.slot_row + (size_t)t * K;
       const float* gwt = a.gw + (size_t)t * K;
-      int ncol[NB][4];
+      // The rows of x are read in 16-byte chunks, 8 consecutive columns per
+      // lane, then swapped into the accumulator layout (a block past d reads
+      // the row's last block; its values are never stored).  The Y rows below
+      // keep 8-byte reads: the swapped form needs more registers than the
+      // four-wave tile has left.
+      int cblk[NB];
       float o[NB][4][4];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        cblk[nb] = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
+        uint32_t p[4][2];
+        load_block(xrow + cblk[nb], p);
+        swap_halves(p);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          ncol[nb][g] = min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4);
-          const uint2 xv = *reinterpret_cast<const uint2*>(xrow + ncol[nb][g]);
-          o[nb][g][0] = bf16_to_f32((bf16_t)(xv.x & 0xffff)) + acc[nb][mb][4 * g + 0];
-          o[nb][g][1] = bf16_to_f32((bf16_t)(xv.x >> 16)) + acc[nb][mb][4 * g + 1];
-          o[nb][g][2] = bf16_to_f32((bf16_t)(xv.y & 0xffff)) + acc[nb][mb][4 * g + 2];
-          o[nb][g][3] = bf16_to_f32((bf16_t)(xv.y >> 16)) + acc[nb][mb][4 * g + 3];
+          o[nb][g][0] = bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0];
+          o[nb][g][1] = bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1];
+          o[nb][g][2] = bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2];
+          o[nb][g][3] = bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3];
         }
+      }
       if (!out) {   // combine not fused: S = x + shared experts in fp32 to a.out
         float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
 #pragma unroll
@@ -466,8 +474,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           sc[nb] = ysc[(size_t)row * gpr + sgrp[nb]];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) y[nb][g] = *reinterpret_cast<const uint2*>(yr + ncol[nb][g]);
+          for (int g = 0; g < 4; ++g) y[nb][g] = *reinterpret_cast<const uint2*>(yr + min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4));
         }
       };
       fetch(ycur, scur, srt[0]);
@@ -479,7 +486,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
         const float g2 = gwt[min(k + 2, K - 1)];
         if (k + 1 < K) fetch(ynxt, snxt, s1);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             o[nb][g][0] = fmaf(gcur, h_lo(ycur[nb][g].x) * scur[nb], o[nb][g][0]);
@@ -487,6 +494,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
             o[nb][g][2] = fmaf(gcur, h_lo(ycur[nb][g].y) * scur[nb], o[nb][g][2]);
             o[nb][g][3] = fmaf(gcur, h_hi(ycur[nb][g].y) * scur[nb], o[nb][g][3]);
           }
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           scur[nb] = snxt[nb];

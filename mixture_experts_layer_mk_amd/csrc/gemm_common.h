@@ -88,6 +88,16 @@ __device__ __forceinline__ void store_block(void* row_at_8h, const uint32_t (&p)
   q[2] = make_uint4(p[2][0], p[2][1], p[3][0], p[3][1]);   // 16 + 8 h .. 16 + 8 h + 7
 }
 
+// The inverse: a lane's two 16-byte chunks of a row (at columns 8 h and
+// 16 + 8 h of a 32-column block) as p[0..3], before swap_halves puts them in
+// the accumulator layout.
+__device__ __forceinline__ void load_block(const void* row_at_8h, uint32_t (&p)[4][2]) {
+  const uint4* q = static_cast<const uint4*>(row_at_8h);
+  const uint4 u = q[0], v = q[2];
+  p[0][0] = u.x; p[0][1] = u.y; p[1][0] = u.z; p[1][1] = u.w;
+  p[2][0] = v.x; p[2][1] = v.y; p[3][0] = v.z; p[3][1] = v.w;
+}
+
 __device__ __forceinline__ float h_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
