@@ -352,7 +352,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
         store_block(darow + a.inner + ib + 8 * hi, p3);
       }
       if (routed && a.dg_part) {
-        part += __shfl_xor(part, 32);
+        part = sum_halves(part);
         if (hi == 0) red[wn * BM + m] = part;
       }
     }
@@ -382,7 +382,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
         for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[nb][mb][r]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        amax = max_halves(amax);
         float sc, inv;
         y_scale_of(amax, sc, inv);
         if (m >= rows) continue;

@@ -46,6 +46,20 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
 }
+// Max and sum over lanes l and l ^ 32, with one swap of the wave's halves (a
+// VALU op) instead of a cross-lane read through LDS.  Both lanes combine the
+// same two values, and max and + are commutative, so both get the same bits.
+__device__ __forceinline__ float max_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Lanes l and l + 32 of a wave hold the same output row of a 32-column block:
 // lane half h (0 or 1) has columns 8 g + 4 h + {0, 1} in p[g][0] and {2, 3} in
 // p[g][1], g = 0..3.  Two swaps between the halves (the low half's g = 1 and 3

@@ -280,7 +280,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
             h[mb][nb][g][q] = v;
             amax = fmaxf(amax, fabsf(v));
           }
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      amax = max_halves(amax);
       if (hi == 0) gmax[wn * BM + wm * WM + mb * 32 + l32] = amax;
     }
     __syncthreads();
@@ -328,7 +328,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
         for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[nb][mb][r]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        amax = max_halves(amax);
         float sc, inv;
         y_scale_of(amax, sc, inv);
         if (m >= rows) continue;
