@@ -54,6 +54,7 @@ int choose_bm(const moe_layer_desc_t& d) {
 // shared experts in fp32).  Measured against the in-order sequence with the
 // combine fused into the shared down-projection: skewed 128-token batch
 // -16%, V3-shaped -3.6%, 2B-shaped -5%, 16B-shaped even.
+constexpr int kLateForkTokens = 1024;
 bool concurrent_shared(const moe_layer_desc_t& d) {
   return d.dtype != MOE_F32 && d.n_shared > 0;
 }
@@ -352,19 +353,30 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   // combine.  The shared stages touch only x (its E4M3 rows for FP8 layers,
   // quantised before the fork), the shared weights, h_shared and S, which
   // nothing on the caller's stream touches before the join.
+  //
+  // Batches of fewer than kLateForkTokens tokens fork after the router and
+  // the dispatch instead, which then run alone on the GPU (measured on the
+  // skewed 128-token batch: -9.5%; on the 16B shape the early fork is 1.2%
+  // faster, on the V3 shape 2.2%).
   SideStream* side = (!events && concurrent_shared(d)) ? side_stream(s) : nullptr;
-  if (side) {
+  const bool late_fork = side && d.T < kLateForkTokens;
+  auto fork_shared = [&]() -> hipError_t {
+    hipError_t e = hipEventRecord(side->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e == hipSuccess) e = gemm_on(shared_gateup(), side->s);
+    if (e == hipSuccess) e = gemm_on(shared_down(), side->s);   // no out2: S, combined separately
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
+    return e;
+  };
+  if (side && !late_fork) {
     if (fp8) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
-    MOE_CHECK(hipEventRecord(side->fork, s));
-    MOE_CHECK(hipStreamWaitEvent(side->s, side->fork, 0));
-    MOE_CHECK(gemm_on(shared_gateup(), side->s));
-    MOE_CHECK(gemm_on(shared_down(), side->s));   // no out2: S; the combine runs separately
-    MOE_CHECK(hipEventRecord(side->join, side->s));
+    MOE_CHECK(fork_shared());
   }
 
   st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
-                      s, mark, /*quant_x=*/side == nullptr);
+                      s, mark, /*quant_x=*/side == nullptr || late_fork);
   if (st != MOE_OK) return st;
+  if (late_fork) MOE_CHECK(fork_shared());   // the E4M3 rows of FP8 layers are ready
   // 4. routed gate/up
   if (!mark(3)) return MOE_ERR_HIP;
   {
