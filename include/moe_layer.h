@@ -26,13 +26,14 @@
  *    unless stated otherwise.  The caller owns all memory; the library never
  *    allocates or frees device memory.  Its only state is one side stream and
  *    two events per host thread and device, created on first use by a bf16
- *    forward with shared experts and kept until the process ends, so calls on
+ *    or FP8 forward with shared experts and kept until the process ends, so calls on
  *    different streams may run concurrently (with distinct workspaces).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
- *    For bf16 layers with shared experts the untraced forward runs the
- *    shared experts on the side stream, forked from `stream` at the start of
- *    the call and joined back before the combine (which then runs as its own
+ *    For bf16 and FP8 layers with shared experts the untraced forward runs
+ *    the shared experts on the side stream, forked from `stream` at the start
+ *    of the call (batches of fewer than 1024 tokens: after the router and the
+ *    dispatch) and joined back before the combine (which then runs as its own
  *    kernel).  The call as a whole stays ordered on `stream`, under stream
  *    capture too.
  *  - Validation errors are returned before anything is enqueued.  A failed
