@@ -36,6 +36,10 @@ REDUCED = {
     "2b-T2000": C["deepseekmoe-2b"].replace(T=2000),
     "16b-T2600": C["deepseekmoe-16b"].replace(T=2600),
     "16b-T1000": C["deepseekmoe-16b"].replace(T=1000, seed=1),
+    # 1024 tokens: the fused router and the side stream's fork at the start of
+    # the call; 1023: the split router and the fork after the dispatch.
+    "16b-T1023": C["deepseekmoe-16b"].replace(T=1023, seed=6),
+    "16b-T1024": C["deepseekmoe-16b"].replace(T=1024, seed=7),
     "v3-d512-T4096": C["deepseek-v3"].replace(d=512, inner=256, shared_inner=256),
     "v3-d512-T700": C["deepseek-v3"].replace(T=700, d=512, inner=256,
                                              shared_inner=256, seed=2),
@@ -85,13 +89,15 @@ def test_deterministic_bitwise():
 
 @pytest.mark.parametrize("name,dtype", [("skewed-16b-small", None), ("v3-d512-T700", None),
                                         ("16b-T2600", None), ("16b-T2600", "fp8"),
-                                        ("skewed-16b-small", "fp8")])
+                                        ("skewed-16b-small", "fp8"), ("16b-T1023", None),
+                                        ("16b-T1024", None)])
 def test_side_stream_matches_in_order(name, dtype):
     """bf16 layers with shared experts run them on a side stream when the
     call is not traced (S = x + shared experts in fp32, then the separate
     combine), for weight-streaming tiles and 256-row tiles (16b-T2600)
     alike, and for FP8 layers (the E4M3 token rows are quantised before the
-    fork).  A traced call runs every stage in order with the combine fused
+    fork).  Batches of fewer than 1024 tokens fork after the router and the
+    dispatch, larger ones at the start of the call (16b-T1023 / 16b-T1024).  A traced call runs every stage in order with the combine fused
     into the shared down-projection.  Both add the same fp32 terms in the same order, so the
     outputs are bitwise equal, on repeated calls too (the side stream's
     writes of one call never overtake the previous call's reads)."""
