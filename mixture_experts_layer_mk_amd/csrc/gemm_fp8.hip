@@ -236,8 +236,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
     load_frags(fa1, fb1, Ac, Bc, 1);
     mma(fa0, fb0);
     sched_ds();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // block kb+1 landed
-    __syncthreads();
+    // Block kb+1 landed: the count wait the compiler sees, then the barrier
+    // (with the wait hidden in asm, or a fence, the compiler also waited for
+    // the loads issued just after it before the next fragment reads;
+    // measured: V3-shaped FP8 layer -8.5%, 16B-shaped -1.8%).
+    stage_sync<0>();
     issue(next2, Ac, Bc);
     load_frags(fa0, fb0, An, Bn, 0);
     mma(fa1, fb1);
