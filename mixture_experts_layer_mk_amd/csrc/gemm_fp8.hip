@@ -54,11 +54,11 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 // e for routed tiles) times N-tile nt.  LDS: operand buffers As0/As1 (at least
 // BM x 128 B) and Bs0/Bs1, the tile's scale bytes sA [BM][MAX_NK] and
 // sB [2][MAX_NK], and gmax [4][BM] for the GATEUP epilogue.
-template <int MODE, int BM, int WAVES_M>
+template <int MODE, int BM, int WAVES_M, int NS>
 __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows, int e,
-                                           int nt, u32x4* As0, u32x4* As1, u32x4* Bs0,
-                                           u32x4* Bs1, uint8_t* sA, uint8_t* sB,
-                                           float* gmax) {
+                                           int nt, u32x4* As0, u32x4* As1, u32x4* As2,
+                                           u32x4* Bs0, u32x4* Bs1, u32x4* Bs2, uint8_t* sA,
+                                           uint8_t* sB, float* gmax) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int MB = WM / 32, NB = WN / 32;
@@ -230,6 +230,8 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   // fragments of this block (barrier): (Ac, Bc) are free and block `next2`
   // starts streaming into them.  Blocks past the end re-load the last block
   // (never read).
+  // With three stages the block after next may still be in flight at the
+  // barrier: the wait leaves the most recent stage's N_VM loads outstanding.
   auto block = [&](int kb, int next2, u32x4* Ac, u32x4* Bc, const u32x4* An,
                    const u32x4* Bn) {
     load_scales(kb);
@@ -240,24 +242,43 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
     // (with the wait hidden in asm, or a fence, the compiler also waited for
     // the loads issued just after it before the next fragment reads;
     // measured: V3-shaped FP8 layer -8.5%, 16B-shaped -1.8%).
-    stage_sync<0>();
+    stage_sync<NS == 3 ? N_VM : 0>();
     issue(next2, Ac, Bc);
     load_frags(fa0, fb0, An, Bn, 0);
     mma(fa1, fb1);
     sched_ds_vm();
   };
 
-  issue(0, As0, Bs0);
-  issue(min(1, nk - 1), As1, Bs1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // block 0 and the scales
-  __syncthreads();
-  load_frags(fa0, fb0, As0, Bs0, 0);
-  int kb = 0;
-  for (; kb + 2 <= nk; kb += 2) {
-    block(kb, min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
-    block(kb + 1, min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+  if constexpr (NS == 3) {
+    // Three-stage ring (tiles of at most 128 rows, which stream their
+    // weights): two blocks in flight while one is computed.
+    issue(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1);
+    issue(min(2, nk - 1), As2, Bs2);
+    stage_sync<2 * N_VM>();                              // block 0 and the scales
+    load_frags(fa0, fb0, As0, Bs0, 0);
+    int kb = 0;
+    for (; kb + 3 <= nk; kb += 3) {
+      block(kb, min(kb + 3, nk - 1), As0, Bs0, As1, Bs1);
+      block(kb + 1, min(kb + 4, nk - 1), As1, Bs1, As2, Bs2);
+      block(kb + 2, min(kb + 5, nk - 1), As2, Bs2, As0, Bs0);
+    }
+    if (kb < nk) block(kb, nk - 1, As0, Bs0, As1, Bs1);
+    if (kb + 1 < nk) block(kb + 1, nk - 1, As1, Bs1, As2, Bs2);
+  } else {
+    issue(0, As0, Bs0);
+    issue(min(1, nk - 1), As1, Bs1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // block 0 and the scales
+    __syncthreads();
+    load_frags(fa0, fb0, As0, Bs0, 0);
+    int kb = 0;
+    for (; kb + 2 <= nk; kb += 2) {
+      block(kb, min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
+      block(kb + 1, min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+    }
+    if (kb < nk) block(kb, nk - 1, As0, Bs0, As1, Bs1);
   }
-  if (kb < nk) block(kb, nk - 1, As0, Bs0, As1, Bs1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");       // no load left in flight
 
   // ---- epilogue ----
   // acc[nb][mb][r] = D[n][m] with n = nb*32 + 8*(r/4) + 4*hi + (r%4) and
@@ -470,8 +491,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
 // BM / 2 rows run the half-height layout.
 template <int MODE, int BM, int WAVES_M>
 __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
-  __shared__ u32x4 As0[BM * 8], As1[BM * 8];
-  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8];
+  // Tiles of at most 128 rows keep a third stage (3 x (BM + 256) x 128 B
+  // <= 144 KB of LDS).
+  constexpr int NS = (BM <= 128) ? 3 : 2;
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
   __shared__ uint8_t sA[BM * MAX_NK];
   __shared__ uint8_t sB[2 * MAX_NK];
   __shared__ float gmax[4 * BM];
@@ -495,17 +519,17 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
     const MTile t = a.tiles[mt];
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
-        gemm8_tile<MODE, BM / 2, 1>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, sA,
-                                    sB, gmax);
+        gemm8_tile<MODE, BM / 2, 1, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0,
+                                        Bs1, Bs2, sA, sB, gmax);
         return;
       }
     }
-    gemm8_tile<MODE, BM, WAVES_M>(a, t.row0, t.rows, t.expert, nt, As0, As1, Bs0, Bs1, sA, sB,
-                                  gmax);
+    gemm8_tile<MODE, BM, WAVES_M, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0, Bs1,
+                                      Bs2, sA, sB, gmax);
   } else {
     const int row0 = mt * BM;
-    gemm8_tile<MODE, BM, WAVES_M>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, Bs0, Bs1, sA,
-                                  sB, gmax);
+    gemm8_tile<MODE, BM, WAVES_M, NS>(a, row0, min(BM, a.T - row0), 0, nt, As0, As1, As2, Bs0,
+                                      Bs1, Bs2, sA, sB, gmax);
   }
 }
 
