@@ -276,8 +276,7 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   } else {
     issue(0, As0, Bs0);
     issue(min(1, nk - 1), As1, Bs1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // block 0 and the scales
-    __syncthreads();
+    stage_sync<N_VM>();   // block 0 and the scales (block 1 may still fly)
     load_frags(fa0, fb0, As0, Bs0, 0);
     int kb = 0;
     for (; kb + 2 <= nk; kb += 2) {
