@@ -61,6 +61,10 @@ REDUCED = {
     "v3-fp8-d512-T700": C["deepseek-v3"].replace(T=700, d=512, inner=256, shared_inner=256,
                                                   seed=2, dtype="fp8"),
     "skewed-fp8": C["skewed-16b-small"].replace(dtype="fp8"),
+    # group-limited routing with 2048 tokens: the split router and the token
+    # rows quantised on the side stream
+    "v3-fp8-d512-T2048": C["deepseek-v3"].replace(T=2048, d=512, inner=256, shared_inner=256,
+                                                  dtype="fp8", seed=11),
 }
 
 

@@ -90,13 +90,13 @@ def test_deterministic_bitwise():
 @pytest.mark.parametrize("name,dtype", [("skewed-16b-small", None), ("v3-d512-T700", None),
                                         ("16b-T2600", None), ("16b-T2600", "fp8"),
                                         ("skewed-16b-small", "fp8"), ("16b-T1023", None),
-                                        ("16b-T1024", None)])
+                                        ("16b-T1024", None), ("v3-d512-T4096", "fp8")])
 def test_side_stream_matches_in_order(name, dtype):
     """bf16 layers with shared experts run them on a side stream when the
     call is not traced (S = x + shared experts in fp32, then the separate
     combine), for weight-streaming tiles and 256-row tiles (16b-T2600)
     alike, and for FP8 layers (the E4M3 token rows are quantised before the
-    fork).  Batches of fewer than 1024 tokens fork after the router and the
+    fork, or on the side stream behind the split router: v3-d512-T4096).  Batches of fewer than 1024 tokens fork after the router and the
     dispatch, larger ones at the start of the call (16b-T1023 / 16b-T1024).  A traced call runs every stage in order with the combine fused
     into the shared down-projection.  Both add the same fp32 terms in the same order, so the
     outputs are bitwise equal, on repeated calls too (the side stream's
