@@ -25,9 +25,13 @@
  *  - All tensor pointers are DEVICE pointers (HIP), row-major, densely packed,
  *    unless stated otherwise.  The caller owns all memory; the library never
  *    allocates or frees device memory.  Its only state is one side stream and
- *    two events per host thread and device, created on first use by a bf16
- *    or FP8 forward with shared experts and kept until the process ends, so calls on
- *    different streams may run concurrently (with distinct workspaces).
+ *    four events per host thread and device, created on first use by an
+ *    untraced bf16 or FP8 forward (or backward) with shared experts, and
+ *    destroyed when that host thread exits (moe_side_stream_count reports how
+ *    many exist).  Calls on different streams may run concurrently (with
+ *    distinct workspaces); calls made from one host thread on different
+ *    streams share that thread's side stream, so their shared-expert branches
+ *    run one after the other (each call's result is unaffected).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
  *    For bf16 and FP8 layers with shared experts the untraced forward runs
@@ -180,7 +184,8 @@ moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* desc,
  *   workspace    device scratch of >= moe_layer_workspace_size bytes,
  *                256-byte aligned; contents on entry are ignored
  *   stream       hipStream_t (NULL = null stream)
- * T == 0 is valid and enqueues nothing. */
+ * T == 0 is valid: it enqueues only a kernel that writes zeros to
+ * expert_counts (nothing at all when expert_counts is NULL). */
 moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
                                const float* w_gate, const float* logit_bias,
                                const float* select_bias,
@@ -189,6 +194,11 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
                                int32_t* topk_idx, float* topk_w,
                                int32_t* expert_counts, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Side streams the library currently holds, over all host threads and
+ * devices (each is destroyed when the host thread that created it exits).
+ * Host-only; for leak checks. */
+int32_t moe_side_stream_count(void);
 
 /* Number of kernel stages moe_layer_forward_traced brackets with events,
  * and the name of stage i (NULL if out of range). */

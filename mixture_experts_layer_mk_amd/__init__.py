@@ -8,7 +8,7 @@ from ._lib import (MOE_BF16, MOE_FP8, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_INVALI
                    HipEvents, MoeError, MoeLayerDesc, header_functions,
                    backward_stage_names, backward_workspace_size, load_library, make_desc, moe_bias_update,
                    moe_layer_backward, moe_layer_forward,
-                   quantize_fp8_blocks, strerror,
+                   quantize_fp8_blocks, side_stream_count, strerror,
                    trace_stage_names, validate, workspace_layout,
                    workspace_size)
 
@@ -18,6 +18,6 @@ __all__ = [
     "HipEvents", "MoeError", "MoeLayerDesc", "header_functions",
     "backward_stage_names", "backward_workspace_size", "load_library", "make_desc", "moe_bias_update",
     "moe_layer_backward", "moe_layer_forward",
-    "quantize_fp8_blocks", "strerror",
+    "quantize_fp8_blocks", "side_stream_count", "strerror",
     "trace_stage_names", "validate", "workspace_layout", "workspace_size",
 ]

@@ -106,6 +106,8 @@ def load_library():
     lib.moe_quantize_fp8_blocks.restype = ctypes.c_int
     lib.moe_bias_update.argtypes = [P, ctypes.c_int32, ctypes.c_float, P, P, P]
     lib.moe_bias_update.restype = ctypes.c_int
+    lib.moe_side_stream_count.argtypes = []
+    lib.moe_side_stream_count.restype = ctypes.c_int32
     lib.moe_strerror.argtypes = [ctypes.c_int]
     lib.moe_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -118,6 +120,13 @@ def header_functions() -> list:
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def side_stream_count() -> int:
+    """Side streams the library holds (one per host thread and device that ran
+    an untraced forward or backward with shared experts; each is destroyed
+    when its thread exits)."""
+    return int(load_library().moe_side_stream_count())
 
 
 def strerror(status: int) -> str:

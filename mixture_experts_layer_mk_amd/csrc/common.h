@@ -95,11 +95,12 @@ struct ScanArgs {
   int nblk, E, bm;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s);
 
 struct PermuteArgs {
-  const void* x; int dtype; int T, d, K, E, rt, nblk;   // rt: tokens per block
+  int T, K, rt, nblk;   // rt: tokens per router block
   const int32_t* topk_idx; const int32_t* rank; const int32_t* block_base;
-  const int32_t* offsets; int32_t* slot_row; int32_t* row_src; void* xp;
+  const int32_t* offsets; int32_t* slot_row; int32_t* row_src;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 

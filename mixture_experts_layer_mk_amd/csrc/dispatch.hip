@@ -10,114 +10,131 @@ namespace moe {
 
 namespace {
 
-// Scan over router blocks, one workgroup per expert: the block's rows for
-// expert e start at block_base[e][b] (relative to the expert's first row);
-// the expert's total goes to counts[e].  block_counts / block_base are
-// [E][nblk] (each expert's blocks contiguous).
-__global__ __launch_bounds__(256) void scan_blocks_kernel(ScanArgs a) {
-  __shared__ int part[256];
-  const int e = blockIdx.x, tid = threadIdx.x;
-  const int per = (a.nblk + 255) / 256;
-  const int b0 = min(tid * per, a.nblk), b1 = min(b0 + per, a.nblk);
-  const int32_t* bc = a.block_counts + (size_t)e * a.nblk;
-  int32_t* bb = a.block_base + (size_t)e * a.nblk;
-  int sum = 0;
-  for (int b = b0; b < b1; ++b) sum += bc[b];
-  part[tid] = sum;
-  __syncthreads();
-  // inclusive scan of the 256 partial sums (Hillis-Steele)
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = (tid >= off) ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+constexpr int SCAN_THREADS = 1024;   // one workgroup, 16 waves
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
   }
-  int run = part[tid] - sum;            // exclusive prefix of this thread's range
-  for (int b = b0; b < b1; ++b) {
-    bb[b] = run;
-    run += bc[b];
-  }
-  if (tid == 255) a.counts[e] = part[255];
+  return v;
 }
 
-// Exclusive scan over experts, user counts, and the GEMM M-tile schedule
-// (one workgroup; thread e owns expert e, E <= 256).
-__global__ __launch_bounds__(256) void scan_experts_kernel(ScanArgs a) {
+// The whole dispatch scan in one workgroup:
+//  (a) per expert e (wave w takes e = w, w + 16, ...), the exclusive prefix of
+//      the router blocks' counts: the block's rows for expert e start at
+//      block_base[e][b] (relative to the expert's first row); the expert's
+//      total goes to counts[e].  block_counts / block_base are [E][nblk].
+//  (b) wave 0: the exclusive scan over experts (offsets) and over their
+//      M-tile counts ceil(count / bm) (where each expert's tiles start).
+//  (c) the M-tile list, one tile per thread: expert found by binary search
+//      over the tile starts.
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   __shared__ int tot[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS + 1];
   __shared__ int tstart[MAX_EXPERTS + 1];
-  const int e = threadIdx.x;
-  if (e < a.E) tot[e] = a.counts[e];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NWAVE = SCAN_THREADS / 64;
+  for (int e = wave; e < a.E; e += NWAVE) {
+    const int32_t* bc = a.block_counts + (size_t)e * a.nblk;
+    int32_t* bb = a.block_base + (size_t)e * a.nblk;
+    int carry = 0;
+    for (int c = 0; c < a.nblk; c += 64) {
+      const int b = c + lane;
+      const int v = b < a.nblk ? bc[b] : 0;
+      const int incl = wave_incl_scan(v);
+      if (b < a.nblk) bb[b] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      tot[e] = carry;
+      a.counts[e] = carry;
+      if (a.user_counts) a.user_counts[e] = carry;
+    }
+  }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (wave == 0) {
     int o = 0, ts = 0;
-    for (int q = 0; q < a.E; ++q) {
-      off[q] = o;
-      tstart[q] = ts;
-      o += tot[q];
-      ts += (tot[q] + a.bm - 1) / a.bm;
+    for (int c = 0; c < a.E; c += 64) {
+      const int e = c + lane;
+      const int v = e < a.E ? tot[e] : 0;
+      const int nt = (v + a.bm - 1) / a.bm;
+      const int iv = wave_incl_scan(v), it = wave_incl_scan(nt);
+      if (e < a.E) {
+        off[e] = o + iv - v;
+        tstart[e] = ts + it - nt;
+        a.offsets[e] = o + iv - v;
+      }
+      o += __shfl(iv, 63, 64);
+      ts += __shfl(it, 63, 64);
     }
-    off[a.E] = o;
-    tstart[a.E] = ts;
+    if (lane == 0) {
+      off[a.E] = o;
+      tstart[a.E] = ts;
+      a.offsets[a.E] = o;
+      *a.n_tiles = ts;
+    }
   }
   __syncthreads();
-  if (e < a.E) {
-    const int c = tot[e];
-    if (a.user_counts) a.user_counts[e] = c;
-    a.offsets[e] = off[e];
-    const int nt = tstart[e + 1] - tstart[e];
-    for (int i = 0; i < nt; ++i) {
-      MTile t;
-      t.expert = e;
-      t.row0 = off[e] + i * a.bm;
-      t.rows = min(a.bm, c - i * a.bm);
-      t.pad = 0;
-      a.tiles[tstart[e] + i] = t;
+  const int n = tstart[a.E];
+  for (int i = tid; i < n; i += SCAN_THREADS) {
+    int lo = 0, hi = a.E - 1;   // last expert with tstart[e] <= i (it has >= 1 tile)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tstart[mid] <= i) lo = mid;
+      else hi = mid - 1;
     }
-  }
-  if (threadIdx.x == 0) {
-    a.offsets[a.E] = off[a.E];
-    *a.n_tiles = tstart[a.E];
+    const int e = lo, j = i - tstart[e];
+    MTile t;
+    t.expert = e;
+    t.row0 = off[e] + j * a.bm;
+    t.rows = min(a.bm, tot[e] - j * a.bm);
+    t.pad = 0;
+    a.tiles[i] = t;
   }
 }
 
-// One wave per token: compute the K destination rows, record the maps, and
-// copy the token's row into each of them (16-byte vectors).
+// One thread per (token, slot): the slot's row is the expert's first row,
+// plus the rows of the expert in earlier router blocks, plus the slot's rank
+// among the expert's slots in its own block (token order).  Writes the two
+// row maps.
 __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
-  const int t = blockIdx.x * 4 + threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  if (t >= a.T) return;
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= a.T * a.K) return;
+  const int t = q / a.K;
   const int b = t / a.rt;
-  const int esz = a.dtype == 1 ? 2 : 4;
-  const int nvec = a.d * esz / 16;
-  const uint4* src = reinterpret_cast<const uint4*>(
-      static_cast<const char*>(a.x) + (size_t)t * a.d * esz);
-  for (int k = 0; k < a.K; ++k) {
-    const int q = t * a.K + k;
-    const int e = a.topk_idx[q];
-    const int row = a.offsets[e] + a.block_base[(size_t)e * a.nblk + b] + a.rank[q];
-    if (lane == 0) {
-      a.slot_row[q] = row;
-      a.row_src[row] = t;
-    }
-    if (a.xp) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.xp) +
-                                            (size_t)row * a.d * esz);
-      for (int v = lane; v < nvec; v += 64) dst[v] = src[v];
-    }
-  }
+  const int e = a.topk_idx[q];
+  const int row = a.offsets[e] + a.block_base[(size_t)e * a.nblk + b] + a.rank[q];
+  a.slot_row[q] = row;
+  a.row_src[row] = t;
+}
+
+// counts[0 .. n) = 0 (a forward with no tokens still reports its counts).
+__global__ __launch_bounds__(256) void zero_counts_kernel(int32_t* counts, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) counts[i] = 0;
 }
 
 }  // namespace
 
+hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_counts_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counts, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scan_blocks_kernel, dim3(a.E), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(scan_experts_kernel, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  const int64_t n = (int64_t)a.T * a.K;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(permute_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

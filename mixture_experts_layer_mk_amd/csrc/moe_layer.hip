@@ -1,11 +1,12 @@
 // Host side of the C ABI (include/moe_layer.h): validation, workspace
 // layout, and the kernel sequence of one layer forward pass, enqueued on the
 // caller's stream with no host synchronisation and no device allocation.
-// bf16 layers run the shared experts on a side stream (one per host thread
-// and device, created on first use), forked from and joined back into the
-// caller's stream.
+// bf16 and FP8 layers run the shared experts on a side stream (one per host
+// thread and device, created on first use and destroyed when the thread
+// exits), forked from and joined back into the caller's stream.
 #include "moe_layer.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <unordered_map>
@@ -60,42 +61,68 @@ bool concurrent_shared(const moe_layer_desc_t& d) {
 }
 
 // Side stream and the fork / join events, per host thread and device (so
-// concurrent host threads never share them); never destroyed.  Default
-// priority, non-blocking with respect to the legacy default stream.
+// concurrent host threads never share them).  Default priority,
+// non-blocking with respect to the legacy default stream.  They live as long
+// as the host thread: its thread-exit destructor destroys them (HIP releases
+// a stream or event that still has work queued once that work completes).
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr;
   hipEvent_t qx = nullptr;   // FP8 layers: the E4M3 token rows are ready
 };
 
+std::atomic<int32_t> g_live_side_streams{0};   // across threads (introspection)
+
+void destroy_side(SideStream& ss) {
+  if (ss.qx) (void)hipEventDestroy(ss.qx);
+  if (ss.join2) (void)hipEventDestroy(ss.join2);
+  if (ss.join) (void)hipEventDestroy(ss.join);
+  if (ss.fork) (void)hipEventDestroy(ss.fork);
+  if (ss.s) {
+    (void)hipStreamDestroy(ss.s);
+    g_live_side_streams.fetch_sub(1, std::memory_order_relaxed);
+  }
+  ss = SideStream{};
+}
+
+struct SideStreamCache {
+  std::unordered_map<int, SideStream> by_device;
+  ~SideStreamCache() {
+    int cur = -1;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto& kv : by_device) {
+      (void)hipSetDevice(kv.first);
+      destroy_side(kv.second);
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+  }
+};
+
 // The side stream of the caller's stream's device (the null stream: the
 // current device); created with that device current.  nullptr on any
 // failure, and the call then runs every stage in order on `s`.
 SideStream* side_stream(hipStream_t s) {
-  thread_local std::unordered_map<int, SideStream> cache;
+  thread_local SideStreamCache cache;
   int dev = 0;
   if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
     return nullptr;
-  auto it = cache.find(dev);
-  if (it != cache.end()) return &it->second;
+  auto it = cache.by_device.find(dev);
+  if (it != cache.by_device.end()) return &it->second;
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return nullptr;
   if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
   SideStream ss;
   bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+  if (ok) g_live_side_streams.fetch_add(1, std::memory_order_relaxed);
+  else ss.s = nullptr;
   ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.qx, hipEventDisableTiming) == hipSuccess;
-  if (!ok) {
-    if (ss.join2) (void)hipEventDestroy(ss.join2);
-    if (ss.join) (void)hipEventDestroy(ss.join);
-    if (ss.fork) (void)hipEventDestroy(ss.fork);
-    if (ss.s) (void)hipStreamDestroy(ss.s);
-  }
+  if (!ok) destroy_side(ss);
   if (cur != dev) (void)hipSetDevice(cur);
   if (!ok) return nullptr;
-  return &cache.emplace(dev, ss).first->second;
+  return &cache.by_device.emplace(dev, ss).first->second;
 }
 
 moe_status_t validate(const moe_layer_desc_t* d) {
@@ -253,14 +280,12 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
   if (!mark(2)) return MOE_ERR_HIP;
   {
     PermuteArgs p{};
-    p.x = x; p.dtype = bf16 ? 1 : 0; p.T = d.T; p.d = d.d; p.K = d.top_k;
-    p.E = d.n_routed; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
+    p.T = d.T; p.K = d.top_k; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
     p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
     p.block_base = static_cast<const int32_t*>(at(L.block_base));
     p.offsets = static_cast<const int32_t*>(at(L.offsets));
     p.slot_row = static_cast<int32_t*>(at(L.slot_row));
     p.row_src = static_cast<int32_t*>(at(L.row_src));
-    p.xp = nullptr;
     MOE_CHECK(launch_permute(p, s));
   }
 #undef MOE_CHECK
@@ -288,8 +313,11 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   auto mark = [&](int i) -> bool {
     return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
   };
-  if (d.T == 0) {   // nothing to compute
-    for (int i = 0; i <= kStages; ++i)
+  if (d.T == 0) {   // nothing to compute; every expert's count is zero
+    if (!mark(0)) return MOE_ERR_HIP;
+    if (expert_counts && launch_zero_counts(expert_counts, d.n_routed, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    for (int i = 1; i <= kStages; ++i)
       if (!mark(i)) return MOE_ERR_HIP;
     return MOE_OK;
   }
@@ -801,6 +829,10 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
   return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
                       topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
                       stream, nullptr);
+}
+
+int32_t moe_side_stream_count(void) {
+  return g_live_side_streams.load(std::memory_order_relaxed);
 }
 
 int32_t moe_layer_trace_stage_count(void) { return kStages; }

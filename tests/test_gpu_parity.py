@@ -152,6 +152,29 @@ def test_T_zero_and_one():
     from mixture_experts_layer_mk_amd import moe_layer_forward
     out = moe_layer_forward(x0, d["w_gate"], d["routed"], d["shared"], 6)
     assert out.shape == (0, 2048)
+    # No tokens: the counts are still written (zeros), over whatever the
+    # buffer held before -- called through the C ABI with a buffer of our own.
+    import ctypes
+    from mixture_experts_layer_mk_amd import _lib
+    lib = _lib.load_library()
+    cfg = case.cfg
+    desc = _lib.make_desc(0, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner, cfg.n_shared,
+                          cfg.shared_inner)
+    cnt = torch.full((cfg.n_routed,), 0x5a5a5a5a, dtype=torch.int32, device="cuda")
+    w1, w3, w2 = d["routed"]
+    s1, s3, s2 = d["shared"]
+    ffn_r = _lib.FfnWeights(w1.data_ptr(), w3.data_ptr(), w2.data_ptr(), None, None, None)
+    ffn_s = _lib.FfnWeights(s1.data_ptr(), s3.data_ptr(), s2.data_ptr(), None, None, None)
+    torch.cuda.synchronize()
+    st = lib.moe_layer_forward(ctypes.byref(desc), None, d["w_gate"].data_ptr(), None, None,
+                               ffn_r, ffn_s, None, None, None, cnt.data_ptr(), None, 0,
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == 0, _lib.strerror(st)
+    torch.cuda.synchronize()
+    assert (cnt == 0).all(), "T = 0 left expert_counts unwritten"
+    _, routing = moe_layer_forward(x0, d["w_gate"], d["routed"], d["shared"], 6,
+                                   return_routing=True)
+    assert (routing["expert_counts"] == 0).all()
 
 
 def test_all_experts_kept_and_no_shared():

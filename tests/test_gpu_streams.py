@@ -118,3 +118,51 @@ def test_forward_concurrent_host_threads():
         for o in results[k]:
             assert torch.equal(o, ref)
     say("[threads] 2 threads x 4 calls equal")
+
+
+def test_forward_short_lived_threads_release_side_streams():
+    """Threads that call the layer once and exit: each gets its own side stream
+    (results bitwise equal to the main thread's) and destroys it on exit, so
+    the library's side-stream count returns to where it was."""
+    import mixture_experts_layer_mk_amd as moe
+    case = Case(C["deepseekmoe-16b"].replace(T=1200, seed=11))
+    ws0 = _workspace(case)
+    ref = torch.empty_like(case.dev["x"])
+    _forward(case, ref, ws0)
+    torch.cuda.synchronize()
+    base = moe.side_stream_count()
+    assert base >= 1            # the main thread's own
+    results, errors, during = {}, [], []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            ws = _workspace(case)
+            out = torch.empty_like(ref)
+            with torch.cuda.stream(s):
+                _forward(case, out, ws)
+            s.synchronize()
+            during.append(moe.side_stream_count())
+            results[k] = out
+        except Exception as e:   # reported below, in the main thread
+            errors.append(repr(e))
+
+    for wave in range(4):        # 4 waves of 3 concurrent short-lived threads
+        threads = [threading.Thread(target=worker, args=(3 * wave + j,)) for j in range(3)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == list(range(12))
+    for k, o in results.items():
+        assert torch.equal(o, ref), f"thread {k} differs"
+    assert min(during) >= base + 1
+    # join() returns when the Python thread is done; the thread-exit
+    # destructors run just after, as the OS thread ends
+    import time
+    deadline = time.time() + 10
+    while moe.side_stream_count() != base and time.time() < deadline:
+        time.sleep(0.05)
+    assert moe.side_stream_count() == base, "side streams of exited threads were kept"
+    say(f"[threads] 12 short-lived threads equal; side streams back to {base}")
