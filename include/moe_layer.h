@@ -61,7 +61,9 @@ typedef enum {
   MOE_ERR_WORKSPACE = -2,   /* workspace NULL or smaller than required       */
   MOE_ERR_UNSUPPORTED = -3, /* valid layer, but a shape this build rejects   */
   MOE_ERR_ALIAS = -4,       /* out overlaps x                                 */
-  MOE_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed     */
+  MOE_ERR_HIP = -5,         /* a HIP runtime call or kernel launch failed     */
+  MOE_ERR_SCRATCH = -6      /* moe_layer_forward_noalloc: the layer needs more
+                               than MOE_NOALLOC_SCRATCH_BYTES of workspace    */
 } moe_status_t;
 
 /* Layer precision.  MOE_FP8: x and out bf16, router fp32 as for bf16; the
@@ -194,6 +196,29 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
                                int32_t* topk_idx, float* topk_w,
                                int32_t* expert_counts, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * moe_layer_forward with the workspace taken from a fixed device buffer of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library, one per device (the library's
+ * own static device array; each GPU the library runs on holds it until the
+ * process ends; its address is resolved once per device, on the first call
+ * there).  Arguments as for moe_layer_forward, without the workspace.  The
+ * call allocates nothing and runs every stage in order on `stream` (no side
+ * stream).  A layer whose moe_layer_workspace_size exceeds the buffer gets
+ * MOE_ERR_SCRATCH before anything is enqueued (16B-shaped layer: up to 1168
+ * tokens; V3-shaped: 272).  Every call on a device shares that
+ * device's buffer, which keeps the last call's contents (the forward reads
+ * nothing it has not written in the same call): calls that overlap in time on
+ * one GPU -- concurrent streams or host threads -- race and must be ordered by
+ * the caller. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, const void* x,
+                                       const float* w_gate, const float* logit_bias,
+                                       const float* select_bias, moe_ffn_weights_t routed,
+                                       moe_ffn_weights_t shared, void* out,
+                                       int32_t* topk_idx, float* topk_w,
+                                       int32_t* expert_counts, void* stream);
 
 /* Side streams the library currently holds, over all host threads and
  * devices (each is destroyed when the host thread that created it exits).

@@ -21,6 +21,8 @@ MOE_ERR_WORKSPACE = -2
 MOE_ERR_UNSUPPORTED = -3
 MOE_ERR_ALIAS = -4
 MOE_ERR_HIP = -5
+MOE_ERR_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
@@ -83,6 +85,8 @@ def load_library():
     fwd = [D, P, P, P, P, FfnWeights, FfnWeights, P, P, P, P, P, ctypes.c_size_t, P]
     lib.moe_layer_forward.argtypes = fwd
     lib.moe_layer_forward.restype = ctypes.c_int
+    lib.moe_layer_forward_noalloc.argtypes = fwd[:11] + [P]
+    lib.moe_layer_forward_noalloc.restype = ctypes.c_int
     lib.moe_layer_forward_traced.argtypes = fwd + [ctypes.POINTER(P), ctypes.c_int32]
     lib.moe_layer_forward_traced.restype = ctypes.c_int
     lib.moe_layer_trace_stage_count.argtypes = []
@@ -305,7 +309,7 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
                       logit_bias=None, routed_scale: float = 1.0,
                       return_routing: bool = False, out=None, workspace=None,
                       stream=None, trace_events=None, expert_scales=None,
-                      shared_scales=None):
+                      shared_scales=None, _noalloc: bool = False):
     """DeepSeekMoE layer forward on the GPU.
 
     x [T, d] (bf16 or fp32), W_gate [E, d] fp32, experts = (w1 [E, I, d],
@@ -365,9 +369,13 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
         out = torch.empty_like(x)
     else:
         _check_tensor("out", out, dt, (T, d), dev)
-    nbytes = workspace_size(desc)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if _noalloc:
+        if workspace is not None or trace_events is not None:
+            raise ValueError("the no-allocation forward takes no workspace or trace events")
+    else:
+        nbytes = workspace_size(desc)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     idx = wts = cnt = None
     if return_routing:
         idx = torch.empty((T, K), dtype=torch.int32, device=dev)
@@ -383,10 +391,14 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
              if shared is not None else FfnWeights(None, None, None, None, None, None))
     args = [ctypes.byref(desc), _ptr(x), _ptr(W_gate), _ptr(logit_bias),
             _ptr(select_bias), ffn_r, ffn_s, _ptr(out), _ptr(idx), _ptr(wts),
-            _ptr(cnt), workspace.data_ptr(), workspace.numel(), stream]
-    if trace_events is None:
+            _ptr(cnt)]
+    if _noalloc:
+        st = lib.moe_layer_forward_noalloc(*args, stream)
+    elif trace_events is None:
+        args += [workspace.data_ptr(), workspace.numel(), stream]
         st = lib.moe_layer_forward(*args)
     else:
+        args += [workspace.data_ptr(), workspace.numel(), stream]
         arr = (ctypes.c_void_p * len(trace_events))(*trace_events)
         st = lib.moe_layer_forward_traced(*args, arr, len(trace_events))
     if st != MOE_OK:
@@ -394,6 +406,17 @@ def moe_layer_forward(x, W_gate, experts: Sequence, shared: Optional[Sequence],
     if return_routing:
         return out, {"topk_idx": idx, "topk_w": wts, "expert_counts": cnt}
     return out
+
+
+def moe_layer_forward_noalloc(x, W_gate, experts: Sequence, shared: Optional[Sequence],
+                              K: int, **kw):
+    """``moe_layer_forward`` through the C ABI's no-allocation entry point: the
+    library's fixed per-device workspace (``MOE_NOALLOC_SCRATCH_BYTES``)
+    instead of a caller's buffer, every stage in order on the stream.  Pass
+    ``out=`` (and read routing with ``return_routing``) as for the allocating
+    call; ``workspace`` and ``trace_events`` are not accepted.  Raises
+    MoeError with MOE_ERR_SCRATCH when the layer does not fit."""
+    return moe_layer_forward(x, W_gate, experts, shared, K, _noalloc=True, **kw)
 
 
 def quantize_fp8_blocks(w, stream=None):

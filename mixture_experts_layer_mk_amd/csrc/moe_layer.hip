@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <unordered_map>
 
 #include "common.h"
@@ -299,7 +300,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
                           int32_t* topk_idx, float* topk_w,
                           int32_t* expert_counts, void* workspace,
                           size_t workspace_bytes, void* stream_ptr,
-                          void* const* events) {
+                          void* const* events, bool allow_side = true) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_layer_desc_t& d = *desc;
@@ -389,7 +390,8 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
   // the dispatch instead, which then run alone on the GPU (measured on the
   // skewed 128-token batch: -9.5%; on the 16B shape the early fork is 1.2%
   // faster, on the V3 shape 2.2%).
-  SideStream* side = (!events && concurrent_shared(d)) ? side_stream(s) : nullptr;
+  SideStream* side =
+      (allow_side && !events && concurrent_shared(d)) ? side_stream(s) : nullptr;
   const bool late_fork = side && d.T < kLateForkTokens;
   // With `quant` the side stream first quantises the token rows of an FP8
   // layer, which the router does not read, and records `qx`; the caller's
@@ -780,6 +782,36 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   return MOE_OK;
 }
 
+// The no-allocation forward's workspace: one fixed array per device, resolved
+// to a device address once per device with that device current (the array's
+// name is a host-side stand-in and is never passed to a kernel).  Every call
+// on a device shares it; it keeps the last call's contents.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of stream s (null stream: the
+// current device); nullptr if it cannot be resolved.
+void* scratch_ptr(hipStream_t s) {
+  int dev = 0;
+  if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev] = p;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -829,6 +861,26 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* desc, const void* x,
   return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
                       topk_idx, topk_w, expert_counts, workspace, workspace_bytes,
                       stream, nullptr);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, const void* x,
+                                       const float* w_gate, const float* logit_bias,
+                                       const float* select_bias, moe_ffn_weights_t routed,
+                                       moe_ffn_weights_t shared, void* out,
+                                       int32_t* topk_idx, float* topk_w,
+                                       int32_t* expert_counts, void* stream) {
+  const moe_status_t st = validate(desc);
+  if (st != MOE_OK) return st;
+  const int64_t need = layout_of(*desc).total;
+  if (need > (int64_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (desc->T > 0) {
+    ws = scratch_ptr(static_cast<hipStream_t>(stream));
+    if (!ws) return MOE_ERR_HIP;
+  }
+  return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
+                      topk_idx, topk_w, expert_counts, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr, /*allow_side=*/false);
 }
 
 int32_t moe_side_stream_count(void) {
@@ -932,6 +984,8 @@ const char* moe_strerror(moe_status_t status) {
     case MOE_ERR_UNSUPPORTED: return "layer shape not supported by this build";
     case MOE_ERR_ALIAS: return "out overlaps x";
     case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+    case MOE_ERR_SCRATCH:
+      return "layer needs more workspace than the no-allocation forward's fixed buffer holds";
   }
   return "unknown status";
 }
