@@ -24,10 +24,13 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // The whole dispatch scan in one workgroup:
-//  (a) per expert e (wave w takes e = w, w + 16, ...), the exclusive prefix of
-//      the router blocks' counts: the block's rows for expert e start at
-//      block_base[e][b] (relative to the expert's first row); the expert's
-//      total goes to counts[e].  block_counts / block_base are [E][nblk].
+//  (a) per expert, the exclusive prefix of the router blocks' counts: the
+//      block's rows for expert e start at block_base[e][b] (relative to the
+//      expert's first row); the expert's total goes to counts[e].
+//      block_counts / block_base are [E][nblk].  G threads (a power of two,
+//      at most 64, so a group lies inside one wave) share an expert, each over
+//      a contiguous range of blocks: its loads are independent and go out
+//      together; the G range sums are scanned across the group's lanes.
 //  (b) wave 0: the exclusive scan over experts (offsets) and over their
 //      M-tile counts ceil(count / bm) (where each expert's tiles start).
 //  (c) the M-tile list, one tile per thread: expert found by binary search
@@ -37,22 +40,47 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   __shared__ int off[MAX_EXPERTS + 1];
   __shared__ int tstart[MAX_EXPERTS + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NWAVE = SCAN_THREADS / 64;
-  for (int e = wave; e < a.E; e += NWAVE) {
-    const int32_t* bc = a.block_counts + (size_t)e * a.nblk;
-    int32_t* bb = a.block_base + (size_t)e * a.nblk;
-    int carry = 0;
-    for (int c = 0; c < a.nblk; c += 64) {
-      const int b = c + lane;
-      const int v = b < a.nblk ? bc[b] : 0;
-      const int incl = wave_incl_scan(v);
-      if (b < a.nblk) bb[b] = carry + incl - v;
-      carry += __shfl(incl, 63, 64);
+  int e2 = 1;
+  while (e2 < a.E) e2 <<= 1;
+  const int G = min(64, SCAN_THREADS / e2);          // threads per expert
+  const int per_pass = SCAN_THREADS / G;             // experts per pass
+  const int j = tid & (G - 1);
+  const int per = (a.nblk + G - 1) / G;              // blocks per thread
+  const int b0 = min(j * per, a.nblk), b1 = min(b0 + per, a.nblk);
+  for (int e0 = 0; e0 < a.E; e0 += per_pass) {
+    const int e = e0 + tid / G;
+    const bool live = e < a.E;
+    const int32_t* bc = a.block_counts + (size_t)(live ? e : 0) * a.nblk;
+    int sum = 0;
+    if (live) {
+      int b = b0;
+      for (; b + 8 <= b1; b += 8) {
+        int v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = bc[b + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sum += v[q];
+      }
+      for (; b < b1; ++b) sum += bc[b];
     }
-    if (lane == 0) {
-      tot[e] = carry;
-      a.counts[e] = carry;
-      if (a.user_counts) a.user_counts[e] = carry;
+    // inclusive scan of the range sums over the G lanes of the group
+    int incl = sum;
+    for (int o = 1; o < G; o <<= 1) {
+      const int u = __shfl_up(incl, o, G);
+      if (j >= o) incl += u;
+    }
+    if (live) {
+      int32_t* bb = a.block_base + (size_t)e * a.nblk;
+      int run = incl - sum;
+      for (int b = b0; b < b1; ++b) {
+        bb[b] = run;
+        run += bc[b];
+      }
+      if (j == G - 1) {
+        tot[e] = incl;
+        a.counts[e] = incl;
+        if (a.user_counts) a.user_counts[e] = incl;
+      }
     }
   }
   __syncthreads();

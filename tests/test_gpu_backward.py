@@ -18,7 +18,8 @@ tiles, ragged tails of rows per expert), a few experts with ~1000 rows each
 (several M tiles and a long k loop in the weight gradients), the V3 routing
 (sigmoid, groups, selection bias, renormalised) at d = 512, the skewed small
 batch with a logit bias, no shared expert with every expert kept, a routed
-scale, T = 0, and bitwise reproducibility.
+scale, T = 0, bitwise reproducibility, and the full 16B-shaped layer on every
+token and every weight gradient.
 """
 import sys
 
@@ -195,48 +196,13 @@ def test_backward_no_tokens_gives_zero_weight_gradients():
         assert not t.any()
 
 
-def test_backward_full_size_sampled():
+def test_backward_full_size_all_tokens():
     """The full 16B-shaped layer (T = 16384, the shapes the benchmark times):
-    dx on 64 sampled tokens (a token's dx depends on its own row only); every
-    weight gradient of two sampled routed experts (over all their rows); and
-    eight sampled inner columns of the first shared expert's weight gradients
-    (over all tokens)."""
-    cfg = B16
+    dx of every token, every routed expert's weight gradients over all its
+    rows, every shared expert's over all tokens, and the gate gradients,
+    against the oracle run expert by expert."""
     say("[bwd-full] generating")
-    case = Case(cfg)
-    inp = workloads.make_inputs(cfg)
-    dout_np = inp.dout()
-    dout = torch.from_numpy(dout_np).to(torch.bfloat16).cuda()
+    case = Case(B16)
     say("[bwd-full] running")
-    gr = run_backward(case, dout)
-    torch.cuda.synchronize()
-    idx = gr["topk_idx"].cpu().numpy()
-    kw = case.oracle_kw()
-    host = lambda ws: tuple(w.float().numpy() for w in ws)
-    R, S = host(case.host["routed"]), host(case.host["shared"])
-    rng = np.random.default_rng(17)
-    info = {}
-
-    rows = np.sort(rng.choice(cfg.T, 64, replace=False))
-    ref = oracle.moe_backward(case.x[rows], case.w_gate, R, S, cfg.top_k, dout_np[rows],
-                              forced_idx=idx[rows], magnitudes=True, **kw)
-    _close("dx[sampled]", gr["dx"][rows].float().cpu().numpy(), ref.dx, info, ref.dx_mag)
-
-    s = oracle.exact_scores(case.x, case.w_gate, None, cfg.score)
-    g = np.take_along_axis(s, idx.astype(np.int64), 1)
-    x64, dy64 = case.x.astype(np.float64), dout_np.astype(np.float64)
-    for e in rng.choice(cfg.n_routed, 2, replace=False):
-        tt, kk = np.nonzero(idx == e)
-        o = oracle.expert_backward(x64[tt], g[tt, kk, None] * dy64[tt], R[0][e], R[1][e],
-                                   R[2][e], magnitudes=True)
-        for j, nm in enumerate(("dw1", "dw3", "dw2")):
-            _close(f"routed.{nm}[{e}]", gr["routed"][j][e].cpu().numpy(), o[j + 1], info,
-                   o[5][j + 1])
-
-    cols = np.sort(rng.choice(cfg.shared_inner, 8, replace=False))
-    o = oracle.expert_backward(x64, dy64, S[0][0][cols], S[1][0][cols], S[2][0][:, cols],
-                               magnitudes=True)
-    _close("shared.dw1[cols]", gr["shared"][0][0][cols].cpu().numpy(), o[1], info, o[5][1])
-    _close("shared.dw3[cols]", gr["shared"][1][0][cols].cpu().numpy(), o[2], info, o[5][2])
-    _close("shared.dw2[cols]", gr["shared"][2][0][:, cols].cpu().numpy(), o[3], info, o[5][3])
+    info, _ = check_backward(case)
     say(f"[bwd-full] {info}")

@@ -155,6 +155,43 @@ def test_group_limit_is_optimal_exhaustive():
             assert (keys[0, e] == -np.inf) == (e // gs not in best_groups)
 
 
+def test_group_limit_ties_take_lowest_indices():
+    """Equal group scores go to the lower group index and equal keys to the
+    lower expert index (a total order on both).  Written-out cases:
+
+    * every key equal (zero gate, sigmoid, no bias; 8 groups of 32, keep 4):
+      groups 0..3 stay and experts 0..7 are kept, in index order;
+    * groups 1 and 6 lead with equal scores, the other six tie below them:
+      groups 1 and 6 stay, then 0 and 2; the four raised experts come first
+      (index order), then the lowest-index experts of group 0."""
+    T, d, E, K = 3, 16, 256, 8
+    x = np.random.default_rng(21).standard_normal((T, d)).astype(np.float32)
+    wg = np.zeros((E, d), np.float32)
+    r = oracle.route(x, wg, K, score="sigmoid", n_groups=8, topk_groups=4, norm_topk=True)
+    assert (r.idx == np.arange(8)[None, :]).all()
+    assert np.all(r.g == 1.0 / 8)
+    assert (r.margin == 0).all() and (r.group_margin == 0).all()
+    bias = np.zeros(E, np.float32)
+    raised = [32 + 5, 32 + 17, 192 + 3, 192 + 30]
+    bias[raised] = np.float32(0.01)
+    r = oracle.route(x, wg, K, score="sigmoid", select_bias=bias, n_groups=8,
+                     topk_groups=4, norm_topk=True)
+    assert (r.idx == np.array(raised + [0, 1, 2, 3])[None, :]).all()
+    # the unbiased scores weigh the kept experts: all equal
+    assert np.all(r.g == 1.0 / 8)
+    ref = oracle.moe_forward_bruteforce(
+        x, wg, lambda e: (np.eye(4, d, dtype=np.float32),) * 2 + (np.eye(d, 4, dtype=np.float32),),
+        None, K, score="sigmoid", select_bias=bias, n_groups=8, topk_groups=4,
+        norm_topk=True)
+    y, _ = oracle.moe_forward(
+        x, wg, lambda e: (np.eye(4, d, dtype=np.float32),) * 2 + (np.eye(d, 4, dtype=np.float32),),
+        None, K, score="sigmoid", select_bias=bias, n_groups=8, topk_groups=4, norm_topk=True)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    # softmax with groups: a zero gate makes every softmax score 1/E
+    r = oracle.route(x, wg, 6, score="softmax", n_groups=4, topk_groups=2)
+    assert (r.idx == np.arange(6)[None, :]).all()
+
+
 def test_selection_bias_changes_choice_not_weight():
     """The selection bias steers the choice but the gate weight is the
     unbiased score: a large bias on expert 3 forces it in with weight s_3."""
@@ -298,7 +335,15 @@ def test_mac_count_closed_form():
     stats = {}
     oracle.moe_forward(x, wg, routed, shared, K, n_shared=Ks, stats=stats)
     assert stats["macs"] == T * oracle.activated_macs_per_token(d, E, K, I, Ks, Is)
-    assert oracle.expert_flops_per_token(d, K, I, Ks, Is) == 2 * 3 * d * (K * I + Ks * Is)
+    # The expert FLOPs the benchmark prices are 2 per multiply-add the oracle
+    # actually performed in the experts: its counter minus the gate's T d mN.
+    for (T2, K2, Ks2) in ((T, K, Ks), (17, 1, 0), (9, E, 1)):
+        x2, wg2, r2, s2 = rand_layer(rng, T2, d, E, I, Ks=max(Ks2, 1), Is=Is)
+        st = {}
+        oracle.moe_forward(x2, wg2, r2, s2, K2, n_shared=Ks2, stats=st)
+        expert_macs = st["macs"] - T2 * d * E
+        assert expert_macs % T2 == 0
+        assert oracle.expert_flops_per_token(d, K2, I, Ks2, Is) == 2 * expert_macs // T2
 
 
 def test_page_parameter_counts():
