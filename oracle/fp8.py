@@ -138,76 +138,119 @@ def quantize_experts(w1, w3, w2):
     return tuple(out)
 
 
-def requantisation_spread(h, margin: float) -> np.ndarray:
-    """How far the 1x128 quantisation of ``h`` [R][C] can move if every value
-    moves by at most ``margin`` times its group's largest magnitude: for each
-    element, the largest |Q(h') - Q(h)| over such h', where Q quantises and
-    dequantises as ``quantize_1x128`` does (the scale chosen from the moved
-    group's own maximum).
+def _silu_argmin() -> float:
+    """The point where silu(a) = a / (1 + e^-a) is smallest: the root of
+    silu'(a) = sigmoid(a) (1 + a sigmoid(-a)), i.e. of 1 + a / (1 + e^a),
+    by Newton's method from -1.3."""
+    a = -1.3
+    for _ in range(50):
+        ea = math.exp(a)
+        f = 1.0 + a / (1.0 + ea)
+        df = (1.0 + ea - a * ea) / (1.0 + ea) ** 2
+        step = f / df
+        a -= step
+        if abs(step) < 1e-17:
+            break
+    return a
 
-    Q is monotone in each value for a fixed scale, so the extremes are taken
-    at h -/+ delta, under every scale exponent the moved maximum (within
-    delta of the original) can pick."""
-    h = np.asarray(h, np.float64)
-    R, C = h.shape
-    g = h.reshape(R, C // GROUP, GROUP)
-    gmax = np.abs(g).max(axis=2)
-    delta = margin * gmax
+
+SILU_ARGMIN = _silu_argmin()
+
+
+def silu_range(lo, hi):
+    """Smallest and largest value of silu over each interval [lo, hi]: silu
+    falls on (-inf, SILU_ARGMIN] and rises after it."""
+    lo = np.asarray(lo, np.float64)
+    hi = np.asarray(hi, np.float64)
+    s_lo, s_hi = silu(lo), silu(hi)
+    vmin = np.where((lo < SILU_ARGMIN) & (hi > SILU_ARGMIN), silu(SILU_ARGMIN),
+                    np.minimum(s_lo, s_hi))
+    return vmin, np.maximum(s_lo, s_hi)
+
+
+def activation_interval(a_deq, W1, W3, acc_rel: float, eval_rel: float = 2.0 ** -20):
+    """The SwiGLU activations h = silu(a1) * a3 of rows ``a_deq`` [R, d]
+    (dequantised token rows) with dequantised weights W1, W3 [I, d], and for
+    each one the interval [h_lo, h_hi] of values it can take when each
+    pre-activation a = sum_j t_j (t_j = u_j W_j) is off by at most
+    ``acc_rel`` * sum_j |t_j| (an accumulation that loses that much), widened
+    by ``eval_rel`` of its largest magnitude for the evaluation of silu and
+    the product in fp32.  Returns (h, h_lo, h_hi), each [R, I], fp64."""
+    u = np.asarray(a_deq, np.float64)
+    W1 = np.asarray(W1, np.float64)
+    W3 = np.asarray(W3, np.float64)
+    a1, a3 = u @ W1.T, u @ W3.T
+    au = np.abs(u)
+    d1 = acc_rel * (au @ np.abs(W1).T)
+    d3 = acc_rel * (au @ np.abs(W3).T)
+    s_lo, s_hi = silu_range(a1 - d1, a1 + d1)
+    b_lo, b_hi = a3 - d3, a3 + d3
+    p = np.stack([s_lo * b_lo, s_lo * b_hi, s_hi * b_lo, s_hi * b_hi])
+    h_lo, h_hi = p.min(axis=0), p.max(axis=0)
+    slack = eval_rel * np.maximum(np.abs(h_lo), np.abs(h_hi))
+    return silu(a1) * a3, h_lo - slack, h_hi + slack
+
+
+def admissible_1x128(h_lo, h_hi, codes, scales):
+    """Is each given E4M3 code (with its 1x128 group's scale byte) the
+    quantisation of some value inside its interval [h_lo, h_hi]?
+
+    The group's scale must be one the quantiser can pick for some values
+    inside the intervals: 2^E with E between the exponents of the largest
+    smallest-magnitude and the largest largest-magnitude (E = 0 also allowed
+    when every interval can be zero).  Given that scale, quantisation is
+    monotone in the value, so the code must lie between the quantisations of
+    the interval's two ends.  Returns (ok [R, C] bool, scale_ok [R, C/128]
+    bool); ok is False wherever its group's scale is not admissible."""
+    h_lo = np.asarray(h_lo, np.float64)
+    h_hi = np.asarray(h_hi, np.float64)
+    R, C = h_lo.shape
+    G = C // GROUP
+    mag_lo = np.where((h_lo <= 0) & (h_hi >= 0), 0.0, np.minimum(np.abs(h_lo), np.abs(h_hi)))
+    mag_hi = np.maximum(np.abs(h_lo), np.abs(h_hi))
+    m_lo = mag_lo.reshape(R, G, GROUP).max(axis=2)
+    m_hi = mag_hi.reshape(R, G, GROUP).max(axis=2)
     pe = np.vectorize(pow2_exponent, otypes=[np.int64])
-    if gmax.size == 0:
-        return np.zeros_like(h)
-    E_lo = pe(np.maximum(gmax - delta, 0.0))
-    E_hi = pe(gmax + delta)
-    E0 = pe(gmax)
-    v = dequantize_1x128(*quantize_1x128(h)).reshape(R, C // GROUP, GROUP)
-    spread = np.zeros_like(g)
-    for dE in range(int((E_lo - E0).min()), int((E_hi - E0).max()) + 1):
-        E = E0 + dE
-        live = (E >= E_lo) & (E <= E_hi)
-        sc = np.exp2(E.astype(np.float64))[:, :, None]
-        for sgn in (-1.0, 1.0):
-            moved = np.clip((g + sgn * delta[:, :, None]) / sc, -E4M3_MAX, E4M3_MAX)
-            q = e4m3_decode(e4m3_encode(moved)) * sc
-            spread = np.where(live[:, :, None], np.maximum(spread, np.abs(q - v)), spread)
-    return spread.reshape(R, C)
+    E_lo = np.where(m_lo > 0, pe(m_lo), -127)
+    E_hi = pe(m_hi)
+    E = np.asarray(scales, np.int64) - 127
+    scale_ok = ((E >= E_lo) & (E <= E_hi)) | ((m_lo == 0) & (E == 0))
+    sc = np.repeat(np.exp2(E.astype(np.float64)), GROUP, axis=1)
+    q = lambda v: e4m3_decode(e4m3_encode(np.clip(v / sc, -E4M3_MAX, E4M3_MAX))) * sc
+    val = e4m3_decode(codes) * sc
+    ok = (val >= q(h_lo)) & (val <= q(h_hi)) & np.repeat(scale_ok, GROUP, axis=1)
+    return ok, scale_ok
 
 
-def fp8_ffn(a_deq, w1q, w3q, w2q, quantize_h: bool = True, h_margin=None):
+def fp8_ffn(a_deq, w1q, w3q, w2q, quantize_h: bool = True):
     """One expert on FP8 operands: token rows ``a_deq`` (already quantised
     per 1x128 and dequantised), weights (codes, block scales).  H is quantised
     per 1x128 of the inner dimension before the down-projection (skipped with
-    ``quantize_h=False``).  Accumulation is exact (fp64).
-
-    With ``h_margin`` also returns, per output element, the largest change
-    that moving H by ``h_margin`` of its groups' maxima before quantising it
-    (``requantisation_spread``) can make to it."""
+    ``quantize_h=False``).  Accumulation is exact (fp64)."""
     W1 = dequantize_blocks(*w1q)
     W3 = dequantize_blocks(*w3q)
     W2 = dequantize_blocks(*w2q)
     h = silu(a_deq @ W1.T) * (a_deq @ W3.T)
-    allow = None
     if quantize_h:
-        if h_margin is not None:
-            allow = requantisation_spread(h, h_margin) @ np.abs(W2).T
         h = dequantize_1x128(*quantize_1x128(h))
-    y = h @ W2.T
-    if h_margin is None:
-        return y
-    return y, (allow if allow is not None else np.zeros_like(y))
+    return h @ W2.T
 
 
 def moe_forward_fp8(x, w_gate, routed_q, shared_q, top_k: int, *, n_shared: int = 0,
                     score: str = "softmax", logit_bias=None, select_bias=None,
                     n_groups: int = 1, topk_groups: int = 1, norm_topk: bool = False,
                     routed_scale: float = 1.0, forced_idx=None, quantize_h: bool = True,
-                    h_margin=None):
+                    forced_h=None):
     """The FP8 layer.  ``routed_q`` / ``shared_q`` are the results of
     ``quantize_experts`` (((codes, scales) for w1, w3, w2), stacked per expert).
     Routing is the bf16 layer's (on the input rows); the experts see the
-    quantised token rows.  Returns (y [T, d] fp64, Routing), and with
-    ``h_margin`` also, per output element, the largest change that moving
-    each expert's H by ``h_margin`` of its 1x128 groups' maxima can make
-    (weighted like the experts' contributions)."""
+    quantised token rows.  Returns (y [T, d] fp64, Routing).
+
+    ``forced_h`` = (shared [K_s][T][I_s], routed [T][K][I]) replaces the
+    quantised SwiGLU activations (dequantised values) that enter the
+    down-projections -- where the gate/up products admit several correct
+    E4M3 codes, the layer is evaluated on a given admissible choice (see
+    ``admissible_1x128``), as ``forced_idx`` does for the expert choice."""
     x64 = np.asarray(x, np.float64)
     T, d = x64.shape
     r = route(x, w_gate, top_k, score=score, logit_bias=logit_bias,
@@ -219,27 +262,21 @@ def moe_forward_fp8(x, w_gate, routed_q, shared_q, top_k: int, *, n_shared: int 
         (c1, s1), (c3, s3), (c2, s2) = q
         return (c1[e], s1[e]), (c3[e], s3[e]), (c2[e], s2[e])
 
-    track = h_margin is not None
-    allow = np.zeros((T, d))
     y = x64.copy()
     for s_i in range(n_shared):
-        out = fp8_ffn(xd, *expert(shared_q, s_i), quantize_h=quantize_h, h_margin=h_margin)
-        if track:
-            out, a = out
-            allow += a
-        y += out
+        if forced_h is not None:
+            W2 = dequantize_blocks(*expert(shared_q, s_i)[2])
+            y += np.asarray(forced_h[0][s_i], np.float64) @ W2.T
+        else:
+            y += fp8_ffn(xd, *expert(shared_q, s_i), quantize_h=quantize_h)
     contrib = np.zeros((T, top_k, d))
-    c_allow = np.zeros((T, top_k, d)) if track else None
     for e in np.unique(r.idx):
         tt, kk = np.nonzero(r.idx == e)
-        out = fp8_ffn(xd[tt], *expert(routed_q, int(e)), quantize_h=quantize_h,
-                      h_margin=h_margin)
-        if track:
-            out, a = out
-            c_allow[tt, kk] = a
-        contrib[tt, kk] = out
+        if forced_h is not None:
+            W2 = dequantize_blocks(*expert(routed_q, int(e))[2])
+            contrib[tt, kk] = np.asarray(forced_h[1][tt, kk], np.float64) @ W2.T
+        else:
+            contrib[tt, kk] = fp8_ffn(xd[tt], *expert(routed_q, int(e)), quantize_h=quantize_h)
     for k in range(top_k):
         y += r.g[:, k, None] * contrib[:, k]
-        if track:
-            allow += np.abs(r.g[:, k, None]) * c_allow[:, k]
-    return (y, r, allow) if track else (y, r)
+    return y, r

@@ -169,42 +169,129 @@ def _requant(h):
     return fp8.dequantize_1x128(*fp8.quantize_1x128(h))
 
 
-def test_requantisation_spread_bounds_every_move():
-    """``requantisation_spread`` against brute force: random moves of every
-    value by at most margin x its group's maximum never change the quantised
-    value by more than the spread; moving a whole group by +/- the margin
-    reaches it where the scale cannot change; zero margin gives zero."""
-    rng = np.random.default_rng(11)
-    h = rng.standard_normal((6, 384)) * np.exp(rng.uniform(-6, 6, (6, 1)))
-    h[0, :128] *= 56.0 / np.abs(h[0, :128]).max()         # max exactly 448 x 2^-3
-    h[1, 128:256] = 0.0                                   # a group of zeros ...
-    h[1, 130] = 1e-3                                      # ... but one tiny value
-    h[2, 256:] *= 1e-4                                    # tiny values: subnormal codes
-    v = _requant(h)
-    assert np.array_equal(fp8.requantisation_spread(h, 0.0), np.zeros_like(h))
-    margin = 1e-3
-    spread = fp8.requantisation_spread(h, margin)
-    R, C = h.shape
-    gmax = np.abs(h.reshape(R, C // 128, 128)).max(2)
-    delta = np.repeat(margin * gmax, 128, axis=1)
-    worst = np.zeros_like(h)
-    moves = [np.full_like(h, 1.0), np.full_like(h, -1.0)]
-    moves += [rng.uniform(-1, 1, h.shape) for _ in range(300)]
-    moves += [np.sign(rng.uniform(-1, 1, h.shape)) for _ in range(100)]
-    for m in moves:
-        dev = np.abs(_requant(h + m * delta) - v)
-        assert np.all(dev <= spread * (1 + 1e-12)), np.argwhere(dev > spread)[0]
-        worst = np.maximum(worst, dev)
-    # the group on the scale boundary: moving up changes its scale
-    assert fp8.quantize_1x128(h + delta)[1][0, 0] == fp8.quantize_1x128(h)[1][0, 0] + 1
-    # where the scale is fixed the two uniform moves attain the spread
-    E = lambda a: np.repeat(fp8.quantize_1x128(a)[1], 128, axis=1)
-    fixed = (E(h + delta) == E(h)) & (E(h - delta) == E(h))
-    fixed &= np.repeat(np.abs(gmax) * (1 + margin) < 448.0 * np.exp2(
-        fp8.quantize_1x128(h)[1].astype(np.int64) - 127), 128, axis=1)
-    fixed &= np.repeat(np.abs(gmax) * (1 - margin) > 224.0 * np.exp2(
-        fp8.quantize_1x128(h)[1].astype(np.int64) - 127), 128, axis=1)
-    assert fixed.sum() > 0.5 * h.size
-    np.testing.assert_array_equal(worst[fixed], spread[fixed])
-    # tiny values near zero: a move can flip the sign of a subnormal code
-    assert spread[1, 131] > 0 and spread[1, 131] <= 2 * margin * 1e-3
+def test_silu_minimum_and_range_brute_force():
+    """SILU_ARGMIN is where silu is smallest (a dense grid agrees, and the
+    derivative vanishes there); silu_range over random intervals equals the
+    extremes of silu on a dense sampling of each interval."""
+    a = fp8.SILU_ARGMIN
+    grid = np.linspace(-3.0, 1.0, 400001)
+    sg = oracle.silu(grid)
+    assert abs(grid[np.argmin(sg)] - a) < 2e-5
+    sig = 1.0 / (1.0 + math.exp(-a))
+    assert abs(sig * (1.0 + a * (1.0 - sig))) < 1e-14
+    assert oracle.silu(a) <= sg.min() and sg.min() - oracle.silu(a) < 1e-10
+    rng = np.random.default_rng(5)
+    lo = rng.uniform(-6, 4, 300)
+    hi = lo + rng.uniform(0, 3, 300)
+    vmin, vmax = fp8.silu_range(lo, hi)
+    for i in range(300):
+        v = oracle.silu(np.linspace(lo[i], hi[i], 20001))
+        assert vmin[i] <= v.min() + 1e-15 and v.min() - vmin[i] < 1e-8
+        assert vmax[i] >= v.max() - 1e-15 and vmax[i] - v.max() < 1e-15
+
+
+def test_activation_interval_holds_every_perturbed_accumulation():
+    """Brute force: pre-activations moved anywhere inside acc_rel x their sums
+    of |terms| (corners, random interior points) give SwiGLU values inside
+    [h_lo, h_hi]; the interval is no wider than those moves reach (its ends
+    are attained up to the fp32-evaluation slack); acc_rel = 0 leaves only
+    the slack; the centre value is the exact activation."""
+    rng = np.random.default_rng(8)
+    R, d, I = 24, 256, 128
+    u = rng.standard_normal((R, d))
+    W1 = rng.standard_normal((I, d)) / 16
+    W3 = rng.standard_normal((I, d)) / 16
+    acc = 2.0 ** -6
+    h, lo, hi = fp8.activation_interval(u, W1, W3, acc)
+    a1, a3 = u @ W1.T, u @ W3.T
+    np.testing.assert_array_equal(h, oracle.silu(a1) * a3)
+    m1 = np.abs(u) @ np.abs(W1).T
+    m3 = np.abs(u) @ np.abs(W3).T
+    reach_lo, reach_hi = np.full_like(h, np.inf), np.full_like(h, -np.inf)
+    moves = [(s1, s3) for s1 in (-1.0, 1.0) for s3 in (-1.0, 1.0)]
+    moves += [(rng.uniform(-1, 1, h.shape), rng.uniform(-1, 1, h.shape)) for _ in range(200)]
+    # the point where silu is smallest, wherever the a1 range contains it
+    inside = np.abs(fp8.SILU_ARGMIN - a1) <= acc * m1
+    t_min = np.where(inside, (fp8.SILU_ARGMIN - a1) / np.maximum(acc * m1, 1e-300), 1.0)
+    moves += [(t_min, s3) for s3 in (-1.0, 1.0)]
+    for e1, e3 in moves:
+        hp = oracle.silu(a1 + e1 * acc * m1) * (a3 + e3 * acc * m3)
+        assert np.all(hp >= lo) and np.all(hp <= hi)
+        reach_lo, reach_hi = np.minimum(reach_lo, hp), np.maximum(reach_hi, hp)
+    slack = 2.0 ** -20 * np.maximum(np.abs(lo), np.abs(hi))
+    assert np.all(reach_lo - lo <= 1.0001 * slack + 1e-15)
+    assert np.all(hi - reach_hi <= 1.0001 * slack + 1e-15)
+    _, lo0, hi0 = fp8.activation_interval(u, W1, W3, 0.0)
+    assert np.all(hi0 - lo0 <= 2.0 ** -19 * np.abs(h) * 1.0001 + 1e-300)
+
+
+def test_admissible_codes():
+    """The oracle's own quantisation of a value inside its interval is
+    admissible; so is the quantisation of any other value inside it; a code two
+    steps outside, a scale the group cannot have, and a flipped sign are
+    not; a group whose intervals allow zero may take the zero group's scale."""
+    rng = np.random.default_rng(9)
+    h = rng.standard_normal((8, 256)) * np.exp(rng.uniform(-5, 5, (8, 1)))
+    width = 1e-3 * np.abs(h) + 1e-6 * np.abs(h).max(axis=1, keepdims=True)
+    lo, hi = h - width, h + width
+    codes, scales = fp8.quantize_1x128(h)
+    ok, sok = fp8.admissible_1x128(lo, hi, codes, scales)
+    assert ok.all() and sok.all()
+    for _ in range(20):
+        inner = h + rng.uniform(-1, 1, h.shape) * width
+        c2, s2 = fp8.quantize_1x128(inner)
+        assert fp8.admissible_1x128(lo, hi, c2, s2)[0].all()
+    # two code steps away from both interval ends (same sign, magnitude
+    # below the largest code), for values well inside a code interval
+    mag = codes & 0x7F
+    movable = (mag >= 8) & (mag <= 0x7C)
+    bumped = np.where(movable, codes + 2, codes).astype(np.uint8)
+    bad, _ = fp8.admissible_1x128(lo, hi, bumped, scales)
+    assert not bad[movable].any() and bad[~movable].all()
+    wrong_scale = scales.copy()
+    wrong_scale[0, 0] += 3
+    ok2, sok2 = fp8.admissible_1x128(lo, hi, codes, wrong_scale)
+    assert not sok2[0, 0] and not ok2[0, :128].any() and ok2[0, 128:].all()
+    flipped = codes.copy()
+    big = np.argmax(np.abs(h[1]))
+    flipped[1, big] ^= 0x80
+    assert not fp8.admissible_1x128(lo, hi, flipped, scales)[0][1, big]
+    # intervals around zero: the all-zero group's scale byte (127) is allowed
+    z_lo, z_hi = -np.full((1, 128), 1e-9), np.full((1, 128), 1e-9)
+    zc = np.zeros((1, 128), np.uint8)
+    assert fp8.admissible_1x128(z_lo, z_hi, zc, np.array([[127]], np.uint8))[0].all()
+
+
+def test_forced_activations_reproduce_the_layer():
+    """moe_forward_fp8 evaluated on its own quantised activations (given as
+    forced_h) equals the plain evaluation; on other codes it follows them."""
+    rng = np.random.default_rng(10)
+    T, d, E, I, K = 48, 256, 6, 128, 2
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d)) / 16
+    w1, w3 = (rng.standard_normal((E, I, d)) / 16 for _ in range(2))
+    w2 = rng.standard_normal((E, d, I)) / 11
+    s1, s3 = (rng.standard_normal((1, 128, d)) / 16 for _ in range(2))
+    s2 = rng.standard_normal((1, d, 128)) / 11
+    rq, sq = fp8.quantize_experts(w1, w3, w2), fp8.quantize_experts(s1, s3, s2)
+    y, r = fp8.moe_forward_fp8(x, wg, rq, sq, K, n_shared=1)
+    xd = _requant(x)
+
+    def h_of(q, e, rows):
+        W1 = fp8.dequantize_blocks(q[0][0][e], q[0][1][e])
+        W3 = fp8.dequantize_blocks(q[1][0][e], q[1][1][e])
+        return _requant(oracle.silu(rows @ W1.T) * (rows @ W3.T))
+    hs = [h_of(sq, 0, xd)]
+    hr = np.zeros((T, K, I))
+    for e in np.unique(r.idx):
+        tt, kk = np.nonzero(r.idx == e)
+        hr[tt, kk] = h_of(rq, e, xd[tt])
+    y2, _ = fp8.moe_forward_fp8(x, wg, rq, sq, K, n_shared=1, forced_h=(hs, hr))
+    np.testing.assert_allclose(y2, y, rtol=1e-13, atol=1e-13)
+    hr2 = hr.copy()
+    hr2[3, 1] *= 2.0
+    y3, _ = fp8.moe_forward_fp8(x, wg, rq, sq, K, n_shared=1, forced_h=(hs, hr2))
+    W2 = fp8.dequantize_blocks(rq[2][0][r.idx[3, 1]], rq[2][1][r.idx[3, 1]])
+    np.testing.assert_allclose(y3[3] - y[3], r.g[3, 1] * (hr[3, 1] @ W2.T), rtol=1e-10,
+                               atol=1e-12)
+    assert np.array_equal(np.delete(y3, 3, 0), np.delete(y, 3, 0))
