@@ -59,6 +59,12 @@ constexpr int MAX_GROUPS = 64;
 // ---------------------------------------------------------------------------
 // Launchers (each in the .hip file that holds its kernel)
 // ---------------------------------------------------------------------------
+struct ScanArgs {
+  const int32_t* block_counts; int32_t* block_base; int32_t* counts;
+  int32_t* user_counts; int32_t* offsets; MTile* tiles; int32_t* n_tiles;
+  int nblk, E, bm;
+};
+
 struct RouterArgs {
   const void* x; int dtype;   // 0 = f32, 1 = bf16
   const float* w_gate; const float* logit_bias; const float* select_bias;
@@ -89,16 +95,11 @@ int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits G
 // True when logits and selection run fused (no partial-logit buffer).
 bool router_fused(int T, int E, int K, int n_groups, int dtype);
 
-struct ScanArgs {
-  const int32_t* block_counts; int32_t* block_base; int32_t* counts;
-  int32_t* user_counts; int32_t* offsets; MTile* tiles; int32_t* n_tiles;
-  int nblk, E, bm;
-};
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s);
 
 struct PermuteArgs {
-  int T, K, rt, nblk;   // rt: tokens per router block
+  int T, K, E, rt, nblk;   // rt: tokens per router block
   const int32_t* topk_idx; const int32_t* rank; const int32_t* block_base;
   const int32_t* offsets; int32_t* slot_row; int32_t* row_src;
 };

@@ -10,8 +10,6 @@ namespace moe {
 
 namespace {
 
-constexpr int SCAN_THREADS = 1024;   // one workgroup, 16 waves
-
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -25,62 +23,70 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // The whole dispatch scan in one workgroup:
 //  (a) per expert, the exclusive prefix of the router blocks' counts: the
-//      block's rows for expert e start at block_base[e][b] (relative to the
+//      block's rows for expert e start at block_base[b][e] (relative to the
 //      expert's first row); the expert's total goes to counts[e].
-//      block_counts / block_base are [E][nblk].  G threads (a power of two,
-//      at most 64, so a group lies inside one wave) share an expert, each over
-//      a contiguous range of blocks: its loads are independent and go out
-//      together; the G range sums are scanned across the group's lanes.
+//      block_counts / block_base are [nblk][E] (one router block's counts
+//      contiguous), so thread (g, e) -- expert e, one of NT / EP groups of
+//      consecutive blocks -- reads and writes with the lanes of a wave on
+//      consecutive experts.  The groups' sums are scanned through LDS.
 //  (b) wave 0: the exclusive scan over experts (offsets) and over their
 //      M-tile counts ceil(count / bm) (where each expert's tiles start).
 //  (c) the M-tile list, one tile per thread: expert found by binary search
 //      over the tile starts.
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
+template <int NT>
+__device__ __forceinline__ void dispatch_scan(const ScanArgs& a) {
   __shared__ int tot[MAX_EXPERTS];
   __shared__ int off[MAX_EXPERTS + 1];
   __shared__ int tstart[MAX_EXPERTS + 1];
+  __shared__ int part[NT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int e2 = 1;
-  while (e2 < a.E) e2 <<= 1;
-  const int G = min(64, SCAN_THREADS / e2);          // threads per expert
-  const int per_pass = SCAN_THREADS / G;             // experts per pass
-  const int j = tid & (G - 1);
-  const int per = (a.nblk + G - 1) / G;              // blocks per thread
-  const int b0 = min(j * per, a.nblk), b1 = min(b0 + per, a.nblk);
-  for (int e0 = 0; e0 < a.E; e0 += per_pass) {
-    const int e = e0 + tid / G;
-    const bool live = e < a.E;
-    const int32_t* bc = a.block_counts + (size_t)(live ? e : 0) * a.nblk;
-    int sum = 0;
-    if (live) {
-      int b = b0;
-      for (; b + 8 <= b1; b += 8) {
-        int v[8];
+  const int E = a.E;
+  int ep = 1;                                   // E rounded up to a power of two
+  while (ep < E) ep <<= 1;
+  const int ng = NT / ep;                       // block groups (E <= 256 <= NT)
+  const int e = tid % ep, g = tid / ep;
+  const int per = (a.nblk + ng - 1) / ng;
+  const int b0 = min(g * per, a.nblk), b1 = min(b0 + per, a.nblk);
+  const bool live = e < E && g < ng;
+  const int32_t* __restrict__ bc = a.block_counts;
+  int32_t* __restrict__ bb = a.block_base;
+  // The first RR counts of the thread's range are loaded at once (one
+  // latency) and kept in registers for the second pass; a longer range
+  // (more than RR blocks per group) streams the rest.
+  constexpr int RR = 16384 / NT;
+  int v[RR];
+  int sum = 0;
+  if (live) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = bc[b + q];
+    for (int q = 0; q < RR; ++q) v[q] = b0 + q < b1 ? bc[(size_t)(b0 + q) * E + e] : 0;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sum += v[q];
-      }
-      for (; b < b1; ++b) sum += bc[b];
+    for (int q = 0; q < RR; ++q) sum += v[q];
+    for (int b = b0 + RR; b < b1; ++b) sum += bc[(size_t)b * E + e];
+  }
+  part[tid] = sum;
+  __syncthreads();
+  if (live) {
+    int base = 0, total = 0;
+    for (int h = 0; h < ng; ++h) {
+      const int w = part[h * ep + e];
+      base += h < g ? w : 0;
+      total += w;
     }
-    // inclusive scan of the range sums over the G lanes of the group
-    int incl = sum;
-    for (int o = 1; o < G; o <<= 1) {
-      const int u = __shfl_up(incl, o, G);
-      if (j >= o) incl += u;
+    int run = base;
+#pragma unroll
+    for (int q = 0; q < RR; ++q) {
+      if (b0 + q < b1) bb[(size_t)(b0 + q) * E + e] = run;
+      run += v[q];
     }
-    if (live) {
-      int32_t* bb = a.block_base + (size_t)e * a.nblk;
-      int run = incl - sum;
-      for (int b = b0; b < b1; ++b) {
-        bb[b] = run;
-        run += bc[b];
-      }
-      if (j == G - 1) {
-        tot[e] = incl;
-        a.counts[e] = incl;
-        if (a.user_counts) a.user_counts[e] = incl;
-      }
+    for (int b = b0 + RR; b < b1; ++b) {
+      const int w = bc[(size_t)b * E + e];
+      bb[(size_t)b * E + e] = run;
+      run += w;
+    }
+    if (g == 0) {
+      tot[e] = total;
+      a.counts[e] = total;
+      if (a.user_counts) a.user_counts[e] = total;
     }
   }
   __syncthreads();
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   }
   __syncthreads();
   const int n = tstart[a.E];
-  for (int i = tid; i < n; i += SCAN_THREADS) {
+  for (int i = tid; i < n; i += NT) {
     int lo = 0, hi = a.E - 1;   // last expert with tstart[e] <= i (it has >= 1 tile)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -125,6 +131,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   }
 }
 
+constexpr int SCAN_THREADS = 1024;   // one workgroup, 16 waves
+
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
+  dispatch_scan<SCAN_THREADS>(a);
+}
+
 // One thread per (token, slot): the slot's row is the expert's first row,
 // plus the rows of the expert in earlier router blocks, plus the slot's rank
 // among the expert's slots in its own block (token order).  Writes the two
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
   const int t = q / a.K;
   const int b = t / a.rt;
   const int e = a.topk_idx[q];
-  const int row = a.offsets[e] + a.block_base[(size_t)e * a.nblk + b] + a.rank[q];
+  const int row = a.offsets[e] + a.block_base[(size_t)b * a.E + e] + a.rank[q];
   a.slot_row[q] = row;
   a.row_src[row] = t;
 }

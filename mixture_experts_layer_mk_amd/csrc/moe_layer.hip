@@ -281,7 +281,8 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
   if (!mark(2)) return MOE_ERR_HIP;
   {
     PermuteArgs p{};
-    p.T = d.T; p.K = d.top_k; p.rt = router_tokens_per_block(d.T); p.nblk = L.nblk;
+    p.T = d.T; p.K = d.top_k; p.E = d.n_routed; p.rt = router_tokens_per_block(d.T);
+    p.nblk = L.nblk;
     p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
     p.block_base = static_cast<const int32_t*>(at(L.block_base));
     p.offsets = static_cast<const int32_t*>(at(L.offsets));

@@ -24,6 +24,7 @@
 // bf16 layers with at most 64 experts, K <= 8 and no group limit run 2 and 3
 // fused in one kernel per 64-token block (4 below).
 #include "common.h"
+#include "gemm_common.h"
 
 namespace moe {
 
@@ -377,8 +378,8 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
   __syncthreads();
 
   // e. block histogram and in-block ranks (token order)
-  for (int e = tid; e < E; e += 512)   // layout [E][blocks]
-    a.block_counts[(size_t)e * gridDim.x + blockIdx.x] = __popcll(masks[e]);
+  for (int e = tid; e < E; e += 512)   // layout [blocks][E]
+    a.block_counts[(size_t)blockIdx.x * E + e] = __popcll(masks[e]);
   if (live) {
     const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
 #pragma unroll
@@ -417,111 +418,138 @@ __device__ __forceinline__ int quad_xor2i(int v) {
 __device__ __forceinline__ float quad_xor1(float v) { return __int_as_float(quad_xor1i(__float_as_int(v))); }
 __device__ __forceinline__ float quad_xor2(float v) { return __int_as_float(quad_xor2i(__float_as_int(v))); }
 
+// Ring depths of the fused router's logits: token-row chunks (HBM) and gate
+// plane chunks (L2-resident: every workgroup reads all of them).
+constexpr int FR_NSX = 4, FR_NSW = 4;
+
+template <int KT>
 __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
-  __shared__ float red[4][FR_TOK][65];          // quarter sums, then logits in red[0]
-  __shared__ int sel[FR_TOK][MAX_TOPK];
+  using gemm::u32x4;
+  // LDS: token rows [NSX][64 rows][8 chunks of 16 B] (64 hidden columns per
+  // chunk), gate planes [NSW][3][64 rows][8 chunks]; both XOR-swizzled by
+  // chunk as in the expert GEMMs; then the 64 x 64 logits.
+  // One LDS object per ring slot (eight in all: the compiler's wait
+  // insertion tells apart that many direct-load destinations), selected
+  // statically in an unrolled period of four chunks, so the direct loads
+  // into one slot and the operand reads of another need no wait.
+  __shared__ u32x4 xs0[FR_TOK * 8], xs1[FR_TOK * 8], xs2[FR_TOK * 8], xs3[FR_TOK * 8];
+  __shared__ u32x4 ws0[3 * 64 * 8], ws1[3 * 64 * 8], ws2[3 * 64 * 8], ws3[3 * 64 * 8];
+  __shared__ float lg[FR_TOK][65];
+  __shared__ int sel[FR_TOK][FR_KMAX];
   __shared__ uint64_t masks[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int t0 = blockIdx.x * FR_TOK;
-  const int E = a.E, K = a.K, T = a.T;
+  const int E = a.E, T = a.T;
+  constexpr int K = KT;
 
-  // a. logits of the wave's quarter of the hidden dimension
+  // a. logits, 64 tokens x 64 experts: wave w computes the 32 x 32 tile
+  // (experts 32 (w & 1) .., tokens 32 (w >> 1) ..) over the whole hidden
+  // dimension, l = x.hi + x.mid + x.lo on the matrix cores (bf16 x times the
+  // bf16 parts of the fp32 gate: exact products, fp32 sums).  Chunks of 64
+  // columns stream global -> LDS (direct loads: 8 rows of 128 B per wave
+  // instruction); chunk kc + NSX - 1 of the rows and kc + NSW - 1 of the
+  // planes are issued while chunk kc is multiplied.  Loads past the last
+  // chunk re-read it (uniform op counts for the waits; never used).
   {
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
-    const int kq = a.d / 4;                      // multiple of 16
-    const int k0 = wave * kq;
     const size_t pn = (size_t)E * a.d;
-    const bf16_t* xp[2];
-    const bf16_t* wp[2];
+    const int nch = a.d / 64;
+    const int lr = lane >> 3;
+    const int pos = lane & 7;
+    // this lane's source rows: x blocks 2 wave + j (j < 2), plane blocks
+    // 6 wave + j (j < 6; plane q / 8, row block q % 8)
+    const bf16_t* xsrc[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      xp[b] = x + (size_t)min(t0 + b * 32 + l32, T - 1) * a.d + k0 + 8 * hi;
-      wp[b] = a.planes + (size_t)min(b * 32 + l32, E - 1) * a.d + k0 + 8 * hi;
+    for (int j = 0; j < 2; ++j) {
+      const int blk = 2 * wave + j, row = blk * 8 + lr;
+      const int cg = pos ^ gemm::swz_x(row);
+      xsrc[j] = x + (size_t)min(t0 + row, T - 1) * a.d + cg * 8;
     }
-    f32x16 acc[2][2];
+    const bf16_t* wsrc[6];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 6; ++j) {
+      const int q = 6 * wave + j, pl = q >> 3, row = (q & 7) * 8 + lr;
+      const int cg = pos ^ gemm::swz_x(row);
+      wsrc[j] = a.planes + pl * pn + (size_t)min(row, E - 1) * a.d + cg * 8;
+    }
+    auto issue_x = [&](u32x4* dst, int kc) {
+      const size_t ko = (size_t)min(kc, nch - 1) * 64;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    constexpr int U = 2;   // k-steps of 16 per batch; two batches in flight
-    int k = 0;
-    auto step = [&](const bf16x8 (&xf)[2], const bf16x8 (&w)[2][3]) {
-#pragma unroll
-      for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][2], xf[tb], acc[eb][tb], 0, 0, 0);
-          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][1], xf[tb], acc[eb][tb], 0, 0, 0);
-          acc[eb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[eb][0], xf[tb], acc[eb][tb], 0, 0, 0);
-        }
+        __builtin_amdgcn_global_load_lds((const gemm::glb_void*)(xsrc[j] + ko),
+                                         (gemm::lds_void*)&dst[(2 * wave + j) * 64], 16, 0, 0);
     };
-    // software pipeline: the loads of batch i+1 are issued before the matrix
-    // ops of batch i (each wave is alone on its SIMD: nothing else hides them)
-    auto load_batch = [&](bf16x8 (&xf)[U][2], bf16x8 (&w)[U][2][3], int kb) {
+    auto issue_w = [&](u32x4* dst, int kc) {
+      const size_t ko = (size_t)min(kc, nch - 1) * 64;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          xf[u][b] = *reinterpret_cast<const bf16x8*>(xp[b] + kb + 16 * u);
-#pragma unroll
-          for (int p = 0; p < 3; ++p)
-            w[u][b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + kb + 16 * u);
-        }
+      for (int j = 0; j < 6; ++j)
+        __builtin_amdgcn_global_load_lds((const gemm::glb_void*)(wsrc[j] + ko),
+                                         (gemm::lds_void*)&dst[(6 * wave + j) * 64], 16, 0, 0);
     };
-    const int nb = kq / (16 * U);                // whole batches
-    if (nb > 0) {
-      bf16x8 xa[U][2], wa[U][2][3], xb[U][2], wb[U][2][3];
-      load_batch(xa, wa, 0);
-      int i = 0;
-      for (; i + 2 <= nb; i += 2) {
-        load_batch(xb, wb, (i + 1) * 16 * U);
+    f32x16 acc;
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(xa[u], wa[u]);
-        if (i + 2 < nb) load_batch(xa, wa, (i + 2) * 16 * U);
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int er = (wave & 1) * 32 + l32;     // expert row of this lane's A fragments
+    const int tr = (wave >> 1) * 32 + l32;    // token row of its B fragment
+    auto mult = [&](const u32x4* xb, const u32x4* wb) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) step(xb[u], wb[u]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int c = 2 * kk + hi;
+        const bf16x8 bx = __builtin_bit_cast(bf16x8, xb[tr * 8 + (c ^ gemm::swz_x(tr))]);
+        bf16x8 w[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          w[p] = __builtin_bit_cast(bf16x8, wb[(p * 64 + er) * 8 + (c ^ gemm::swz_x(er))]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[2], bx, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[1], bx, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[0], bx, acc, 0, 0, 0);
       }
-      if (i < nb) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) step(xa[u], wa[u]);
-      }
-      k = nb * 16 * U;
+    };
+    // one chunk: (after the first) wait for its loads and for every wave to
+    // be done with the previous chunk, refill the previous chunk's slots
+    // (rows NSX - 1 ahead, planes NSW - 1 ahead), multiply
+    auto chunk = [&](int kc, const u32x4* xb, const u32x4* wb, u32x4* xf, u32x4* wf) {
+      if (kc > 0) gemm::stage_sync<8>();
+      issue_x(xf, kc + FR_NSX - 1);
+      issue_w(wf, kc + FR_NSW - 1);
+      mult(xb, wb);
+    };
+    issue_x(xs0, 0); issue_x(xs1, 1); issue_x(xs2, 2);
+    issue_w(ws0, 0); issue_w(ws1, 1); issue_w(ws2, 2);
+    // chunk 0: everything but chunks 1 and 2 (16 ops) has landed
+    gemm::stage_sync<16>();
+    // The slots of chunk k0 + j are xs[j], ws[j].  The loop body is straight
+    // line (a conditional chunk inside it made the compiler wait for every
+    // outstanding load before the operand reads); the remainder follows it.
+    int k0 = 0;
+    for (; k0 + 4 <= nch; k0 += 4) {
+      chunk(k0 + 0, xs0, ws0, xs3, ws3);
+      chunk(k0 + 1, xs1, ws1, xs0, ws0);
+      chunk(k0 + 2, xs2, ws2, xs1, ws1);
+      chunk(k0 + 3, xs3, ws3, xs2, ws2);
     }
-    for (; k < kq; k += 16) {
-      bf16x8 xf[2], w[2][3];
+    if (k0 < nch) chunk(k0, xs0, ws0, xs3, ws3);
+    if (k0 + 1 < nch) chunk(k0 + 1, xs1, ws1, xs0, ws0);
+    if (k0 + 2 < nch) chunk(k0 + 2, xs2, ws2, xs1, ws1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the redundant tail loads
+    // acc[r] = D[e][t]: e = 32 (w & 1) + 8 (r / 4) + 4 hi + r % 4, t = tr
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        xf[b] = *reinterpret_cast<const bf16x8*>(xp[b] + k);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) w[b][p] = *reinterpret_cast<const bf16x8*>(wp[b] + p * pn + k);
-      }
-      step(xf, w);
+    for (int r = 0; r < 16; ++r) {
+      const int e = (wave & 1) * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+      float v = acc[r];
+      if (a.logit_bias && e < E) v += a.logit_bias[e];
+      lg[tr][e] = v;
     }
-    // acc[eb][tb][r] = D[e][t]: e = eb*32 + 8*(r/4) + 4*hi + r%4, t = tb*32 + l32
-#pragma unroll
-    for (int eb = 0; eb < 2; ++eb)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          red[wave][tb * 32 + l32][eb * 32 + 8 * (r / 4) + 4 * hi + (r % 4)] = acc[eb][tb][r];
-  }
-  __syncthreads();
-  for (int i = tid; i < FR_TOK * 64; i += 256) {
-    const int tt = i >> 6, e = i & 63;
-    float v = ((red[0][tt][e] + red[1][tt][e]) + red[2][tt][e]) + red[3][tt][e];
-    if (a.logit_bias && e < E) v += a.logit_bias[e];
-    red[0][tt][e] = v;
   }
   __syncthreads();
 
   // b. selection: four lanes per token (16 tokens per wave); lane quarter q
   // scans experts 16q .. 16q + 15: softmax max and sum over the quad, a
   // local top-K in registers, then K rounds merging the four lists' heads
-  // with quad permutes (no LDS traffic).
+  // with quad permutes (no LDS traffic).  K is a compile-time constant and
+  // every step selects with v_cndmask instead of branching.
   {
     const int tt = wave * 16 + (lane >> 2), q = lane & 3;
     const int t = t0 + tt;
@@ -529,7 +557,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = q * 16 + i;
-      l[i] = e < E ? red[0][tt][e] : -INFINITY;
+      l[i] = e < E ? lg[tt][e] : -INFINITY;
     }
     float s[16];
     if (a.score == 0) {
@@ -546,70 +574,83 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
       }
       z += quad_xor1(z);
       z += quad_xor2(z);
+      const float rz = 1.f / z;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = s[i] / z;
+      for (int i = 0; i < 16; ++i) s[i] = s[i] * rz;
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = q * 16 + i < E ? 1.f / (1.f + expf(-l[i])) : 0.f;
     }
-    // local top-K, sorted by (key descending, index ascending)
-    float tk[FR_KMAX], ts[FR_KMAX];
-    int ti[FR_KMAX];
+    // local top-K, sorted by (key descending, index ascending).  The lane's
+    // experts arrive in index order, so a new one goes below every kept one
+    // of equal key: it lands at the first slot whose key is smaller.
+    float tk[KT], ts[KT];
+    int ti[KT];
 #pragma unroll
-    for (int j = 0; j < FR_KMAX; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
+    for (int j = 0; j < KT; ++j) { tk[j] = -INFINITY; ti[j] = 0x7fffffff; ts[j] = 0.f; }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = q * 16 + i;
-      if (e >= E) break;
-      float ck = s[i] + (a.select_bias ? a.select_bias[e] : 0.f);
+      float ck = e < E ? s[i] + (a.select_bias ? a.select_bias[e] : 0.f) : -INFINITY;
       if (ck != ck) ck = -INFINITY;             // NaN never outranks a score
-      float cs = s[i];
-      int ci = e;
+      const float cs = s[i];
+      // bottom-up, so slot j - 1 is read before it is overwritten: slot j
+      // keeps its entry, takes the new one (it lands exactly at j), or takes
+      // slot j - 1's (it lands above j - 1)
 #pragma unroll
-      for (int j = 0; j < FR_KMAX; ++j) {
-        if (j < K && better(ck, ci, tk[j], ti[j])) {   // carry the loser down
-          const float k2 = tk[j], s2 = ts[j];
-          const int i2 = ti[j];
-          tk[j] = ck; ts[j] = cs; ti[j] = ci;
-          ck = k2; cs = s2; ci = i2;
+      for (int j = KT - 1; j >= 0; --j) {
+        const bool keep_j = tk[j] >= ck;
+        const bool keep_prev = j == 0 ? true : (tk[j - 1] >= ck);
+        if (j > 0) {
+          const float nk = keep_j ? tk[j] : (keep_prev ? ck : tk[j - 1]);
+          const float ns = keep_j ? ts[j] : (keep_prev ? cs : ts[j - 1]);
+          const int ni = keep_j ? ti[j] : (keep_prev ? e : ti[j - 1]);
+          tk[j] = nk; ts[j] = ns; ti[j] = ni;
+        } else {
+          tk[0] = keep_j ? tk[0] : ck;
+          ts[0] = keep_j ? ts[0] : cs;
+          ti[0] = keep_j ? ti[0] : e;
         }
       }
     }
     // merge: round j takes the best head of the quad's four lists
-    float gsum = 0.f, os[FR_KMAX];
-    int oi[FR_KMAX];
+    float gsum = 0.f, os[KT];
+    int oi[KT];
 #pragma unroll
-    for (int j = 0; j < FR_KMAX; ++j) {
-      if (j >= K) break;
+    for (int j = 0; j < KT; ++j) {
       float bk = tk[0], bs = ts[0];
       int bi = ti[0];
       {
         const float ok = quad_xor1(bk), os1 = quad_xor1(bs);
         const int oi1 = quad_xor1i(bi);
-        if (better(ok, oi1, bk, bi)) { bk = ok; bi = oi1; bs = os1; }
+        const bool c = better(ok, oi1, bk, bi);
+        bk = c ? ok : bk; bi = c ? oi1 : bi; bs = c ? os1 : bs;
       }
       {
         const float ok = quad_xor2(bk), os2 = quad_xor2(bs);
         const int oi2 = quad_xor2i(bi);
-        if (better(ok, oi2, bk, bi)) { bk = ok; bi = oi2; bs = os2; }
+        const bool c = better(ok, oi2, bk, bi);
+        bk = c ? ok : bk; bi = c ? oi2 : bi; bs = c ? os2 : bs;
       }
       oi[j] = bi; os[j] = bs;
       gsum += bs;
-      if (ti[0] == bi) {                        // this lane's head was taken
+      const bool taken = ti[0] == bi;             // this lane's head was taken
 #pragma unroll
-        for (int u = 0; u + 1 < FR_KMAX; ++u) { tk[u] = tk[u + 1]; ts[u] = ts[u + 1]; ti[u] = ti[u + 1]; }
-        tk[FR_KMAX - 1] = -INFINITY; ti[FR_KMAX - 1] = 0x7fffffff; ts[FR_KMAX - 1] = 0.f;
+      for (int u = 0; u < KT; ++u) {
+        const float nk = u + 1 < KT ? tk[u + 1] : -INFINITY;
+        const float ns = u + 1 < KT ? ts[u + 1] : 0.f;
+        const int ni = u + 1 < KT ? ti[u + 1] : 0x7fffffff;
+        tk[u] = taken ? nk : tk[u]; ts[u] = taken ? ns : ts[u]; ti[u] = taken ? ni : ti[u];
       }
     }
     if (q == 0 && t < T) {
 #pragma unroll
-      for (int j = 0; j < FR_KMAX; ++j) {
-        if (j >= K) break;
+      for (int j = 0; j < KT; ++j) {
         float g = os[j];
         if (a.norm_topk) g = g / gsum;
         g *= a.routed_scale;
-        a.topk_idx[(size_t)t * K + j] = oi[j];
-        a.topk_w[(size_t)t * K + j] = g;
+        a.topk_idx[(size_t)t * KT + j] = oi[j];
+        a.topk_w[(size_t)t * KT + j] = g;
         sel[tt][j] = oi[j];
       }
     }
@@ -627,12 +668,13 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
     if (lane == 0) masks[ee] = m;
   }
   __syncthreads();
-  if (tid < E) a.block_counts[(size_t)tid * gridDim.x + blockIdx.x] = __popcll(masks[tid]);
+  if (tid < E) a.block_counts[(size_t)blockIdx.x * E + tid] = __popcll(masks[tid]);   // [blocks][E]
   if (wave == 0 && live) {
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j = 0; j < K; ++j)
       a.rank[(size_t)t * K + j] = __popcll(masks[sel[lane][j]] & below);
   }
+
 }
 
 }  // namespace
@@ -673,8 +715,17 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
     const int64_t n = (int64_t)r.E * r.d;
     hipLaunchKernelGGL(split_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        r.w_gate, r.planes, n);
-    hipLaunchKernelGGL(router_fused_kernel, dim3((r.T + FR_TOK - 1) / FR_TOK), dim3(256), 0, s,
-                       r);
+    const dim3 grid((r.T + FR_TOK - 1) / FR_TOK), block(256);
+    switch (r.K) {
+      case 1: hipLaunchKernelGGL(router_fused_kernel<1>, grid, block, 0, s, r); break;
+      case 2: hipLaunchKernelGGL(router_fused_kernel<2>, grid, block, 0, s, r); break;
+      case 3: hipLaunchKernelGGL(router_fused_kernel<3>, grid, block, 0, s, r); break;
+      case 4: hipLaunchKernelGGL(router_fused_kernel<4>, grid, block, 0, s, r); break;
+      case 5: hipLaunchKernelGGL(router_fused_kernel<5>, grid, block, 0, s, r); break;
+      case 6: hipLaunchKernelGGL(router_fused_kernel<6>, grid, block, 0, s, r); break;
+      case 7: hipLaunchKernelGGL(router_fused_kernel<7>, grid, block, 0, s, r); break;
+      default: hipLaunchKernelGGL(router_fused_kernel<8>, grid, block, 0, s, r); break;
+    }
     return hipGetLastError();
   }
   // 1 + 2: partial logits
