@@ -11,7 +11,10 @@ layer's stream during the timed steps, a roofline entry for the dominant
 kernel, the FP8 variant of the same layer (E4M3 expert GEMMs, its own
 stage times and roofline against the fp8 matrix peak), the layer backward on
 the same workload (stage times, matrix TFLOP/s, the roofline of its slowest
-GEMM stage), and the CPU oracle timed on a bounded token sample.
+GEMM stage), the other layer shapes (2B-shaped: tokens/s and fraction of the
+bf16 peak; V3-shaped: per-call median against the HBM roofline; the skewed
+128-token batch: the same with a cold cache), and the CPU oracle timed on a
+bounded token sample.
 """
 from __future__ import annotations
 
@@ -30,18 +33,25 @@ METRIC = ("MoE layer fwd tokens/s + activated TFLOP/s (% bf16 MFMA peak), "
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak (TFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (GB/s)
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 matrix peak (TFLOP/s)
-DOMINANT = "gemm_gateup_routed"
+DOMINANT = "gemm_gateup"
 # The dominant kernel of each variant: (name prefix in a trace, sources,
 # committed traffic summary).
 GATEUP = {
     "bf16": ("gemm_bf16_kernel<0", ("common.h", "gemm_common.h", "gemm_bf16.hip"),
-             os.path.join(ROOT, "profiles", "traffic_gemm_gateup_routed.json")),
+             os.path.join(ROOT, "profiles", "traffic_gemm_gateup_16b.json")),
     "fp8": ("gemm_fp8_kernel<0", ("common.h", "gemm_common.h", "gemm_fp8.hip"),
-            os.path.join(ROOT, "profiles", "traffic_gemm_fp8_gateup_routed.json")),
+            os.path.join(ROOT, "profiles", "traffic_gemm_fp8_gateup_16b.json")),
     # the backward's slowest GEMM stage: routed dW1/dW3
     "bwd": ("gemm_bwd_kernel<3, false>", ("common.h", "gemm_common.h", "gemm_bwd.hip"),
-            os.path.join(ROOT, "profiles", "traffic_gemm_bwd_dw13_routed.json")),
+            os.path.join(ROOT, "profiles", "traffic_gemm_bwd_dw13_routed_16b.json")),
 }
+
+
+def gateup_flops(cfg) -> float:
+    """FLOPs of the gate/up launch: 2 d (2 inner) per routed (token, slot) and
+    2 d (2 K_s I_s) per token for the shared experts."""
+    return 2.0 * cfg.d * 2 * (cfg.T * cfg.top_k * cfg.inner +
+                              cfg.T * cfg.n_shared * cfg.shared_inner)
 
 
 def log(msg):
@@ -76,7 +86,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_mb):
     counter files (FETCH_SIZE run, WRITE_SIZE run, both of a bench run with
     --copy-calibration-mb copy_mb).  Each counter is scaled by what it reads
     for the plain device copy of copy_mb MiB; of the launches of a kernel the
-    one with the largest grid is the routed gate/up launch."""
+    one with the largest grid is the gate/up launch (routed and shared tiles)."""
     import csv
     import collections
 
@@ -90,7 +100,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_mb):
     vals = {"fetch": per_kernel(fetch_csv, "FETCH_SIZE"),
             "write": per_kernel(write_csv, "WRITE_SIZE")}
     for kind, (prefix, _, path) in GATEUP.items():
-        what = "routed dW1/dW3 launch" if kind == "bwd" else "routed gate/up launch"
+        what = "routed dW1/dW3 launch" if kind == "bwd" else "gate/up launch (routed + shared)"
         out = {"source_hash": source_hash(kind), "kernel": prefix.rstrip(">") + ">, " + what,
                "copy_calibration_mib": copy_mb}
         for name in ("fetch", "write"):
@@ -221,7 +231,7 @@ def time_fp8(moe, cfg, d, steps, warmup, fpt):
     for ev in events:
         ev.close()
     tflops = fpt * cfg.T / (ms / 1e3) / 1e12
-    dom_flops = 2.0 * cfg.T * cfg.top_k * cfg.d * 2 * cfg.inner
+    dom_flops = gateup_flops(cfg)
     dom_ms = stage_ms[DOMINANT]
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     return {
@@ -229,7 +239,8 @@ def time_fp8(moe, cfg, d, steps, warmup, fpt):
         "activated_tflops": round(tflops, 1),
         "frac_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "gemm_fp8_kernel<GATEUP> (routed launch)", "bound": "mfma",
+        "roofline": {"kernel": "gemm_fp8_kernel<GATEUP> (routed + shared launch)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": measured_traffic("fp8"), "flops_per_launch": dom_flops,
@@ -237,6 +248,76 @@ def time_fp8(moe, cfg, d, steps, warmup, fpt):
         "recipe": "E4M3 codes; token rows and SwiGLU activations per 1x128, weights per "
                   "128x128 block, power-of-two scales; fp32 accumulation across instructions",
     }
+
+
+# The other layer shapes, reported beside the headline (key: workload, timing).
+OTHER_SHAPES = (
+    ("deepseekmoe_2b", "deepseekmoe-2b", False),       # MFMA-bound, back-to-back steps
+    ("deepseek_v3", "deepseek-v3", False),             # weight streaming, warm calls
+    ("skewed_16b_small", "skewed-16b-small", True),    # weight streaming, cold cache
+)
+
+
+def time_shape(moe, cfg, dev, steps, warmup, reps, cold_cache):
+    """One more workload: back-to-back steps (tokens/s, activated TFLOP/s and
+    its fraction of the bf16 peak) and calls timed one by one (median; with
+    ``cold_cache`` L2 and MALL are flushed before each), with the whole layer
+    against the HBM roofline (weights of the experts that receive tokens)."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    log(f"[bench] {cfg.name}: generating")
+    host = workloads.make_inputs(cfg).torch_tensors("cpu")
+    d = {k: (tuple(t.to(dev) for t in v) if isinstance(v, tuple)
+             else (v.to(dev) if v is not None else None)) for k, v in host.items()}
+    del host
+    desc = moe.make_desc(cfg.T, cfg.d, cfg.n_routed, cfg.top_k, cfg.inner,
+                         cfg.n_shared, cfg.shared_inner, n_groups=cfg.n_groups,
+                         topk_groups=cfg.topk_groups, score=cfg.score,
+                         norm_topk=cfg.norm_topk, routed_scale=cfg.routed_scale,
+                         dtype=cfg.dtype)
+    ws = torch.empty(moe.workspace_size(desc), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["x"])
+    counts = torch.empty(cfg.n_routed, dtype=torch.int32, device=dev)
+
+    def step(routing=False):
+        return moe.moe_layer_forward(
+            d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k, score=cfg.score,
+            norm_topk=cfg.norm_topk, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+            select_bias=d["select_bias"], logit_bias=d["logit_bias"],
+            routed_scale=cfg.routed_scale, out=out, workspace=ws, return_routing=routing)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: timing")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    _, rt = step(routing=True)
+    counts = rt["expert_counts"].cpu().numpy()
+    calls = per_call_ms(step, reps, cold_cache, dev)
+    med = float(np.median(calls))
+    hbm, nonempty = layer_hbm_bytes(cfg, counts)
+    fpt = oracle.expert_flops_per_token(cfg.d, cfg.top_k, cfg.inner, cfg.n_shared,
+                                        cfg.shared_inner)
+    tfl = fpt * cfg.T / (ms / 1e3) / 1e12
+    res = {"workload": f"T={cfg.T}, d={cfg.d}, {cfg.n_routed} routed (inner {cfg.inner}, "
+                       f"top-{cfg.top_k}) + {cfg.n_shared} shared",
+           "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
+           "activated_tflops": round(tfl, 1),
+           "frac_bf16_peak": round(tfl / PEAK_BF16_TFLOPS, 4),
+           "per_call_median_ms": round(med, 4), "cold_cache": bool(cold_cache),
+           "hbm_roofline": {"bytes": hbm, "nonempty_experts": nonempty,
+                            "achieved_gbs": round(hbm / (med / 1e3) / 1e9, 1),
+                            "peak_gbs": PEAK_HBM_GBS,
+                            "frac": round(hbm / (med / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
+    del d, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 BWD_KERNEL = {
@@ -345,6 +426,9 @@ def main():
                     help="skip the layer backward on the same workload")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3) variant of the same workload")
+    ap.add_argument("--no-other-shapes", action="store_true",
+                    help="skip the 2B-shaped, V3-shaped and skewed small-batch layers "
+                         "reported beside the 16B-shaped headline")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for "
                          "scaling HBM byte counters)")
@@ -402,8 +486,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Stage breakdown from a traced pass of as many steps: a traced call runs
-    # the stages one after the other on the layer's stream (an untraced call
-    # of a weight-streaming bf16 layer runs the shared experts concurrently).
+    # the same launches as an untraced one, with events between them.
     log(f"[bench] traced pass {args.steps} steps")
     for i in range(args.steps):
         step(events[i])
@@ -423,11 +506,12 @@ def main():
     act_tflops = fpt * cfg.T / (ms / 1e3) / 1e12
     router_gflop = 2 * cfg.T * cfg.d * cfg.n_routed / 1e9
 
-    # dominant kernel: routed gate/up GEMM, 2 * (T*K) * d * (2 * inner) flops
-    dom_flops = 2.0 * cfg.T * cfg.top_k * cfg.d * 2 * cfg.inner
+    # dominant kernel: the gate/up GEMM launch (routed and shared tiles),
+    # 2 * d * 2 * (T*K * inner + T * K_s * I_s) flops
+    dom_flops = gateup_flops(cfg)
     dom_ms = stage_ms[DOMINANT]
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
-    roofline = {"kernel": "gemm_bf16_kernel<GATEUP> (routed launch)", "bound": "mfma",
+    roofline = {"kernel": "gemm_bf16_kernel<GATEUP> (routed + shared launch)", "bound": "mfma",
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("bf16"),
@@ -516,9 +600,10 @@ def main():
                                               (stage_ms["router"] / 1e3) / 1e12, 2),
                    "gbs": rate(router_bytes, stage_ms["router"])},
         "permute": {"gbs": rate(TKn * 4 * 3, stage_ms["permute"])},
-        "combine": ("fused into the shared down-projection" if cfg.n_shared > 0 and
-                    cfg.dtype == "bf16" else
-                    {"gbs": rate(TKn * cfg.d * 2 + cfg.T * cfg.d * 8, stage_ms["combine"])}),
+        # S (fp32) or x read, the fp16 Y rows and their scales read, out written
+        "combine": {"gbs": rate((cfg.T * cfg.d * 4 if cfg.n_shared else cfg.T * cfg.d * xb) +
+                                TKn * cfg.d * 2 + TKn * (cfg.d // 64) * 4 +
+                                cfg.T * cfg.d * xb, stage_ms["combine"])},
     }
 
     fp8 = None
@@ -530,6 +615,12 @@ def main():
     if not args.no_backward and cfg.dtype == "bf16" and not args.cold_cache:
         log(f"[bench] backward: {args.steps} steps")
         bwd = time_backward(moe, cfg, d, args.steps, args.warmup)
+
+    others = {}
+    if not args.no_other_shapes and args.config == "deepseekmoe-16b" and not args.cold_cache:
+        for key, name, cold in OTHER_SHAPES:
+            others[key] = time_shape(moe, workloads.CONFIGS[name], dev, args.steps,
+                                     args.warmup, args.reps, cold)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -565,6 +656,7 @@ def main():
                                    "how": "vendor GEMM (torch.matmul / hipBLASLt), bf16 8192^3"},
         "fp8": fp8,
         "backward": bwd,
+        "other_shapes": others or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -24,22 +24,20 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP), row-major, densely packed,
  *    unless stated otherwise.  The caller owns all memory; the library never
- *    allocates or frees device memory.  Its only state is one side stream and
- *    four events per host thread and device, created on first use by an
- *    untraced bf16 or FP8 forward (or backward) with shared experts, and
+ *    allocates or frees device memory.  Its only state is the backward pass's
+ *    side stream: one stream and three events per host thread and device,
+ *    created on the first untraced bf16 backward with shared experts and
  *    destroyed when that host thread exits (moe_side_stream_count reports how
  *    many exist).  Calls on different streams may run concurrently (with
- *    distinct workspaces); calls made from one host thread on different
- *    streams share that thread's side stream, so their shared-expert branches
- *    run one after the other (each call's result is unaffected).
+ *    distinct workspaces); backward calls made from one host thread on
+ *    different streams share that thread's side stream, so their
+ *    shared-expert branches run one after the other (results unaffected).
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
- *    For bf16 and FP8 layers with shared experts the untraced forward runs
- *    the shared experts on the side stream, forked from `stream` at the start
- *    of the call (batches of fewer than 1024 tokens: after the router and the
- *    dispatch) and joined back before the combine (which then runs as its own
- *    kernel).  The call as a whole stays ordered on `stream`, under stream
- *    capture too.
+ *    The forward enqueues, in order: the router, the dispatch scan, the row
+ *    maps, one grouped gate/up GEMM launch over the routed experts' tiles
+ *    and the shared experts', one grouped down-projection launch (routed
+ *    rows and the shared experts' sum), and the combine.
  *  - Validation errors are returned before anything is enqueued.  A failed
  *    kernel launch returns MOE_ERR_HIP.
  *  - Results are bitwise reproducible for identical inputs and shapes (no
@@ -143,9 +141,8 @@ typedef struct {
                                two (value = half * y_scale)                   */
   int64_t y_scale_f32;      /* [T * top_k][d / 64] those inverse scales (bf16
                                layers; -1 otherwise)                          */
-  int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32); -1 for
-                               bf16 / FP8 layers, whose combine is fused into
-                               the shared down-projection                     */
+  int64_t s_f32;            /* [T][d] x + sum of shared experts (fp32); -1
+                               without shared experts                         */
   int64_t x_q;              /* FP8: [T][d] E4M3 token rows (-1 otherwise)     */
   int64_t x_scale;          /* FP8: [T][d / 128] their scale bytes            */
   int64_t h_routed_scale;   /* FP8: [T * top_k][inner / 128] scale bytes of
@@ -231,11 +228,11 @@ int32_t moe_layer_trace_stage_count(void);
 const char* moe_layer_trace_stage_name(int32_t i);
 
 /* moe_layer_forward, with hipEvent_t events[i] recorded on `stream` before
- * stage i and events[n] after the last stage (n = stage count), so the
- * caller can time every stage.  `events` holds n + 1 created events
- * (MOE_ERR_INVALID_ARG if n_events is smaller).  Every stage runs in order
- * on `stream` (no side stream); the results are bitwise equal to the
- * untraced call's.  Otherwise identical. */
+ * stage i and events[n] after the last stage (n = stage count: router, scan,
+ * permute, gemm_gateup, gemm_down, combine), so the caller can time every
+ * stage.  `events` holds n + 1 created events (MOE_ERR_INVALID_ARG if
+ * n_events is smaller).  The same launches as the untraced call; the
+ * results are bitwise equal.  Otherwise identical. */
 moe_status_t moe_layer_forward_traced(
     const moe_layer_desc_t* desc, const void* x, const float* w_gate,
     const float* logit_bias, const float* select_bias,

@@ -120,13 +120,9 @@ struct GemmArgs {
   void* out; int ldo;            // H (dtype) / Y / S (f32)
   // bf16 layers: routed Y is stored as fp16 scaled by a power of two per 64
   // columns of a row; yscale[row][d / 64] holds the inverse scales (written
-  // by DOWN, read by the fused combine).  fp32 layers: Y is fp32.
+  // by DOWN, read by the combine).  fp32 layers: Y is fp32.
   float* yscale;
   const void* x;                 // DOWN_SHARED residual
-  // DOWN_SHARED with the combine fused (ybuf != NULL): out2[t] =
-  //   x[t] + shared(t) + sum_k gw[t,k] * Y[slot_row[t,k]]   (dtype out)
-  const void* ybuf; const float* gw; const int32_t* slot_row; int K;
-  void* out2;
   const MTile* tiles; const int32_t* n_tiles; int max_mtiles;
   int T;                          // rows for shared group
   int bm;
@@ -151,7 +147,10 @@ struct GemmArgs {
   bf16_t* da; int ldda;
   float* dg_part; int n_part;
 };
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// One launch of stage a.mode on `a`, plus, when `b` is given, the shared
+// experts' tiles of the same stage in the same launch (b->mode == a.mode for
+// GATEUP / GATEUP_BWD; DOWN takes a DOWN_SHARED part writing S).
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GemmArgs* b = nullptr);
 
 // Grouped GEMMs of the backward pass (bf16 operands, fp32 results), C = A B
 // with either operand k-major (rows of the operand hold consecutive k) or
@@ -210,7 +209,7 @@ hipError_t launch_router_bwd(const BwdAuxArgs& a, hipStream_t s);    // dg, dl, 
 hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s);     // dw_gate
 hipError_t launch_dx_combine(const BwdAuxArgs& a, hipStream_t s);    // dx
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s, const GemmArgs* b = nullptr);
 
 // E4M3 quantisation with power-of-two scales: rows of `src` [R][C] (bf16 or
 // f32) per 1 x 128 (quant_rows), or [batch][R][C] per 128 x 128 block.

@@ -8,8 +8,8 @@
 //               routed tiles gather their token rows straight from x
 //   DOWN        Y = H W2^T (routed rows; fp16 scaled by a power of two per
 //               64 columns of a row, inverse scales beside)
-//   DOWN_SHARED with the combine fused:
-//               out = x + sum_s H_s W2_s^T + sum_k g_k Y_k
+//   DOWN_SHARED S = x + sum_s H_s W2_s^T (fp32; the shared experts, which
+//               the combine then adds the kept experts to)
 //   GATEUP_BWD  the gate/up tile recomputed for the backward pass, with the
 //               SwiGLU backward in the epilogue (see GemmArgs)
 //
@@ -30,6 +30,8 @@
 // Blocks are remapped so that each XCD (blocks are dealt round-robin over the
 // 8 XCDs) runs a contiguous range of tiles, with the M-tiles of one weight
 // tile adjacent: the weight tile is then fetched into that XCD's L2 once.
+// One launch holds the routed experts' tiles of a stage and, after them, the
+// shared experts' (one grouped GEMM over all experts of the layer).
 #include "gemm_common.h"
 
 namespace moe {
@@ -406,19 +408,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       }
     }
   } else {
-    // Combine fused: out = RNE(x + shared + sum_k g_k Y_k), the same fp32
-    // operations in the same order as the separate combine (residual plus
-    // shared experts first, then the kept experts in slot order, each Y
-    // element decoded as fp16 times its group's inverse scale).  The kept
-    // experts' rows are fetched one slot ahead, their row indices two ahead.
-    // Without out2 the tile writes S = x + shared experts (fp32) to out
-    // instead, for the separate combine.
-    bf16_t* out = static_cast<bf16_t*>(a.out2);
+    // Shared experts' down-projection: S = x + sum_s H_s W2_s^T in fp32
+    // (the residual and the shared experts; the combine adds the kept
+    // experts).  The rows of x are read in 16-byte chunks, 8 consecutive
+    // columns per lane, then swapped into the accumulator layout (a block
+    // past d reads the row's last block; its values are never stored).
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
-    const uint16_t* ybuf = static_cast<const uint16_t*>(a.ybuf);
-    const float* ysc = a.yscale;
-    const int gpr = a.d / Y_GROUP;
-    const int K = a.K;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       __builtin_amdgcn_sched_barrier(0);
@@ -426,127 +421,44 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
       if (m >= rows) continue;
       const int t = row0 + m;
       const bf16_t* xrow = x + (size_t)t * a.d;
-      const int32_t* srt = a.slot_row + (size_t)t * K;
-      const float* gwt = a.gw + (size_t)t * K;
-      // The rows of x are read in 16-byte chunks, 8 consecutive columns per
-      // lane, then swapped into the accumulator layout (a block past d reads
-      // the row's last block; its values are never stored).  The Y rows below
-      // keep 8-byte reads: the swapped form needs more registers than the
-      // four-wave tile has left.
-      int cblk[NB];
-      float o[NB][4][4];
+      float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        cblk[nb] = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
+        const int cblk = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
         uint32_t p[4][2];
-        load_block(xrow + cblk[nb], p);
+        load_block(xrow + cblk, p);
         swap_halves(p);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          o[nb][g][0] = bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0];
-          o[nb][g][1] = bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1];
-          o[nb][g][2] = bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2];
-          o[nb][g][3] = bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3];
+          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+          if (n >= a.d) continue;
+          *reinterpret_cast<float4*>(srow + n) = make_float4(
+              bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0],
+              bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1],
+              bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2],
+              bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3]);
         }
-      }
-      if (!out) {   // combine not fused: S = x + shared experts in fp32 to a.out
-        float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-            if (n >= a.d) continue;
-            *reinterpret_cast<float4*>(srow + n) =
-                make_float4(o[nb][g][0], o[nb][g][1], o[nb][g][2], o[nb][g][3]);
-          }
-        continue;
-      }
-      // Scale group of column block nb: columns nb*32 .. nb*32+31 of the
-      // wave's range lie in one 64-column group.
-      int sgrp[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sgrp[nb] = min(n0 + wn * WN + nb * 32, a.d - 1) / Y_GROUP;
-      uint2 ycur[NB][4], ynxt[NB][4];
-      float scur[NB], snxt[NB];
-      auto fetch = [&](uint2 (&y)[NB][4], float (&sc)[NB], int row) {
-        const uint16_t* yr = ybuf + (size_t)row * a.d;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          sc[nb] = ysc[(size_t)row * gpr + sgrp[nb]];
-          for (int g = 0; g < 4; ++g) y[nb][g] = *reinterpret_cast<const uint2*>(yr + min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4));
-        }
-      };
-      fetch(ycur, scur, srt[0]);
-      float gcur = gwt[0];
-      int s1 = srt[min(1, K - 1)];
-      float g1 = gwt[min(1, K - 1)];
-      for (int k = 0; k < K; ++k) {
-        const int s2 = srt[min(k + 2, K - 1)];
-        const float g2 = gwt[min(k + 2, K - 1)];
-        if (k + 1 < K) fetch(ynxt, snxt, s1);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            o[nb][g][0] = fmaf(gcur, h_lo(ycur[nb][g].x) * scur[nb], o[nb][g][0]);
-            o[nb][g][1] = fmaf(gcur, h_hi(ycur[nb][g].x) * scur[nb], o[nb][g][1]);
-            o[nb][g][2] = fmaf(gcur, h_lo(ycur[nb][g].y) * scur[nb], o[nb][g][2]);
-            o[nb][g][3] = fmaf(gcur, h_hi(ycur[nb][g].y) * scur[nb], o[nb][g][3]);
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          scur[nb] = snxt[nb];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) ycur[nb][g] = ynxt[nb][g];
-        }
-        gcur = g1; g1 = g2; s1 = s2;
-      }
-      bf16_t* orow = out + (size_t)t * a.d;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // d is a multiple of 64: a 32-column block is all in or all out.
-        const int n = n0 + wn * WN + nb * 32;
-        if (n >= a.d) continue;
-        uint32_t p[4][2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          p[g][0] = pack2(o[nb][g][0], o[nb][g][1]);
-          p[g][1] = pack2(o[nb][g][2], o[nb][g][3]);
-        }
-        swap_halves(p);
-        store_block(orow + n + 8 * hi, p);
       }
     }
   }
 }
 
-// The grouped GEMM: one workgroup per tile.  Routed tail tiles of at most
-// BM / 2 rows (an expert's last rows) run the half-height tile layout, which
-// does half the matrix work.
-template <int MODE, int BM, int WAVES_M, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
-  // Two LDS buffers per operand as distinct objects: accesses name their
-  // buffer statically, so the compiler can tell the direct loads into one
-  // buffer from the operand reads of the other and need not wait between.
-  // Tiles of at most 128 rows stream their weights and keep three stages
-  // in flight-or-compute (3 x (BM + 256) x 128 B <= 144 KB of LDS).
-  constexpr int NS = (BM <= 128) ? 3 : 2;
-  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
-  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
-  // Row sums of GATEUP_BWD (the A buffers are free by the epilogue, but a
-  // separate array keeps the buffers' accesses static).
-  __shared__ float red[MODE == 3 ? 4 * BM : 1];
-
+// One part of a grouped GEMM launch: block `blk` of `nblk` runs one tile of
+// stage MODE.  Routed tail tiles of at most BM / 2 rows (an expert's last
+// rows) run the half-height tile layout, which does half the matrix work.
+template <int MODE, int BM, int WAVES_M, int NW, int NS>
+__device__ __forceinline__ void gemm_part(const GemmArgs& a, int blk, int nblk, u32x4* As0,
+                                          u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
+                                          u32x4* Bs2, float* red) {
   const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = xcd_remap(blk, nblk);
   // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
   // one M-tile are adjacent, then the next M-tile (same expert, same weight
   // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
   // both its token-row tiles and its weight tiles in L2.
   const int ndim = n_tiles_of<MODE, BM>(a);
+  if (L >= mdim * ndim) return;              // padding of a launch's first part
   int mt, nt;
   constexpr int NGRP = ngrp_for<BM>();
   {
@@ -576,36 +488,81 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
-template <int MODE, int BM, int WAVES_M, int NW>
-void launch_mode(const GemmArgs& a, hipStream_t s) {
-  const bool routed = !(a.mode == 2 || ((a.mode == 0 || a.mode == 3) && a.shared));
-  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int ndim = n_tiles_of<MODE, BM>(a);
-  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, BM, WAVES_M, NW>), dim3(mdim * ndim),
-                     dim3(NW * 64), 0, s, a);
+// The grouped GEMM: one workgroup per tile.  A launch holds up to two parts:
+// blocks [0, a_blocks) run stage MODE on `a` (the routed experts), the rest
+// stage MODE_B on `b` (the shared experts), so the shared tiles fill the GPU
+// beside the routed ones.  a_blocks is a multiple of 8: blocks are dealt
+// round-robin over the 8 XCDs, so both parts' tile orders stay XCD-aware.
+template <int MODE, int MODE_B, int BM, int WAVES_M, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a, GemmArgs b,
+                                                               int a_blocks) {
+  // Two LDS buffers per operand as distinct objects: accesses name their
+  // buffer statically, so the compiler can tell the direct loads into one
+  // buffer from the operand reads of the other and need not wait between.
+  // Tiles of at most 128 rows stream their weights and keep three stages
+  // in flight-or-compute (3 x (BM + 256) x 128 B <= 144 KB of LDS).
+  constexpr int NS = (BM <= 128) ? 3 : 2;
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
+  // Row sums of GATEUP_BWD (the A buffers are free by the epilogue, but a
+  // separate array keeps the buffers' accesses static).
+  __shared__ float red[MODE == 3 ? 4 * BM : 1];
+  // Each part reads its own argument struct (a run-time choice of struct
+  // made the compiler copy both to scratch memory).
+  const int blk = blockIdx.x;
+  if (blk >= a_blocks)
+    gemm_part<MODE_B, BM, WAVES_M, NW, NS>(b, blk - a_blocks, (int)gridDim.x - a_blocks, As0,
+                                           As1, As2, Bs0, Bs1, Bs2, red);
+  else
+    gemm_part<MODE, BM, WAVES_M, NW, NS>(a, blk, a_blocks, As0, As1, As2, Bs0, Bs1, Bs2, red);
+}
+
+// Blocks of one part: the routed M-tile bound (or the shared experts' row
+// tiles) times the part's N-tiles.
+template <int MODE, int BM>
+int part_blocks(const GemmArgs& g) {
+  const bool routed = !(MODE == 2 || (is_gateup<MODE>() && g.shared));
+  const int mdim = routed ? g.max_mtiles : (g.T + BM - 1) / BM;
+  return mdim * n_tiles_of<MODE, BM>(g);
+}
+
+template <int MODE, int MODE_B, int BM, int WAVES_M, int NW>
+void launch_pair(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
+  if (!b) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<MODE, MODE, BM, WAVES_M, NW>),
+                       dim3(part_blocks<MODE, BM>(a)), dim3(NW * 64), 0, s, a, a,
+                       part_blocks<MODE, BM>(a));
+    return;
+  }
+  const int na = (part_blocks<MODE, BM>(a) + 7) & ~7;
+  const int nb = part_blocks<MODE_B, BM>(*b);
+  hipLaunchKernelGGL((gemm_bf16_kernel<MODE, MODE_B, BM, WAVES_M, NW>), dim3(na + nb),
+                     dim3(NW * 64), 0, s, a, *b, na);
 }
 
 // Waves per workgroup: the 256-row gate/up tiles (forward and backward) run
 // eight waves, two per SIMD, each with a 128 x 64 sub-tile (measured: shared
 // gate/up -3%, backward gate/up -6%, routed gate/up even); the
-// down-projections keep four waves of 128 x 128 (eight were 6% slower with the
-// fused combine).  Tiles of at most 128 rows keep four waves.
+// down-projections keep four waves of 128 x 128 (eight measured even).
+// Tiles of at most 128 rows keep four waves.
 template <int BM, int WAVES_M>
-void launch_bm(const GemmArgs& a, hipStream_t s) {
+void launch_bm(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
   constexpr int NWG = (BM == 256) ? 8 : 4;
-  if (a.mode == 0) launch_mode<0, BM, WAVES_M, NWG>(a, s);
-  else if (a.mode == 1) launch_mode<1, BM, WAVES_M, 4>(a, s);
-  else if (a.mode == 2) launch_mode<2, BM, WAVES_M, 4>(a, s);
-  else launch_mode<3, BM, WAVES_M, NWG>(a, s);
+  if (a.mode == 0) launch_pair<0, 0, BM, WAVES_M, NWG>(a, b, s);
+  else if (a.mode == 1) launch_pair<1, 2, BM, WAVES_M, 4>(a, b, s);
+  else if (a.mode == 2) launch_pair<2, 2, BM, WAVES_M, 4>(a, nullptr, s);
+  else launch_pair<3, 3, BM, WAVES_M, NWG>(a, b, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GemmArgs* b) {
+  if (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode) || a.mode == 2))
+    return hipErrorInvalidValue;
   switch (a.bm) {
-    case 256: launch_bm<256, 2>(a, s); break;
-    case 128: launch_bm<128, 1>(a, s); break;
-    case 64: launch_bm<64, 1>(a, s); break;
+    case 256: launch_bm<256, 2>(a, b, s); break;
+    case 128: launch_bm<128, 1>(a, b, s); break;
+    case 64: launch_bm<64, 1>(a, b, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

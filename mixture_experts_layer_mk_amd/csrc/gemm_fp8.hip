@@ -15,7 +15,7 @@
 //               power-of-two scale per 128 inner columns of a row (the max
 //               over the group is exchanged between the waves that hold it)
 //   DOWN        Y = H W2^T (fp16 with a power-of-two scale per 64 columns)
-//   DOWN_SHARED with the combine fused
+//   DOWN_SHARED S = x + sum_s H_s W2_s^T (fp32)
 //
 // Tiling is the bf16 kernel's with the k step doubled: a 128-wide k-block is
 // one 128-byte LDS row per operand row and one scale group; it feeds two
@@ -383,16 +383,11 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
       }
     }
   } else {
-    // Combine fused, exactly as in the bf16 layer: out = RNE(x + shared +
-    // sum_k g_k Y_k), residual and shared first, then the kept experts in
-    // slot order; kept experts' rows fetched one slot ahead.  Without out2
-    // the tile writes S = x + shared experts (fp32) to out instead.
-    bf16_t* out = static_cast<bf16_t*>(a.out2);
+    // Shared experts' down-projection: S = x + sum_s H_s W2_s^T in fp32 (as
+    // in the bf16 layer; the combine adds the kept experts).  The rows of x
+    // are read in 16-byte chunks swapped into the accumulator layout (a block
+    // past d reads the row's last block; its values are never stored).
     const bf16_t* x = static_cast<const bf16_t*>(a.x);
-    const uint16_t* ybuf = static_cast<const uint16_t*>(a.ybuf);
-    const float* ysc = a.yscale;
-    const int gpr = a.d / Y_GROUP;
-    const int K = a.K;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       __builtin_amdgcn_sched_barrier(0);
@@ -400,117 +395,39 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
       if (m >= rows) continue;
       const int t = row0 + m;
       const bf16_t* xrow = x + (size_t)t * a.d;
-      const int32_t* srt = a.slot_row + (size_t)t * K;
-      const float* gwt = a.gw + (size_t)t * K;
-      // The rows of x are read in 16-byte chunks, 8 consecutive columns per
-      // lane, then swapped into the accumulator layout (a block past d reads
-      // the row's last block; its values are never stored).  The Y rows below
-      // keep 8-byte reads: the swapped form needs more registers than the
-      // four-wave tile has left.
-      int cblk[NB];
-      float o[NB][4][4];
+      float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        cblk[nb] = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
+        const int cblk = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
         uint32_t p[4][2];
-        load_block(xrow + cblk[nb], p);
+        load_block(xrow + cblk, p);
         swap_halves(p);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          o[nb][g][0] = bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0];
-          o[nb][g][1] = bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1];
-          o[nb][g][2] = bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2];
-          o[nb][g][3] = bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3];
+          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+          if (n >= a.d) continue;
+          *reinterpret_cast<float4*>(srow + n) = make_float4(
+              bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0],
+              bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1],
+              bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2],
+              bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3]);
         }
-      }
-      if (!out) {   // combine not fused: S = x + shared experts in fp32 to a.out
-        float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-            if (n >= a.d) continue;
-            *reinterpret_cast<float4*>(srow + n) =
-                make_float4(o[nb][g][0], o[nb][g][1], o[nb][g][2], o[nb][g][3]);
-          }
-        continue;
-      }
-      int sgrp[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sgrp[nb] = min(n0 + wn * WN + nb * 32, a.d - 1) / Y_GROUP;
-      uint2 ycur[NB][4], ynxt[NB][4];
-      float scur[NB], snxt[NB];
-      auto fetch = [&](uint2 (&y)[NB][4], float (&sc)[NB], int row) {
-        const uint16_t* yr = ybuf + (size_t)row * a.d;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          sc[nb] = ysc[(size_t)row * gpr + sgrp[nb]];
-          for (int g = 0; g < 4; ++g) y[nb][g] = *reinterpret_cast<const uint2*>(yr + min(n0 + wn * WN + nb * 32 + 8 * g + 4 * hi, a.d - 4));
-        }
-      };
-      fetch(ycur, scur, srt[0]);
-      float gcur = gwt[0];
-      int s1 = srt[min(1, K - 1)];
-      float g1 = gwt[min(1, K - 1)];
-      for (int k = 0; k < K; ++k) {
-        const int s2 = srt[min(k + 2, K - 1)];
-        const float g2 = gwt[min(k + 2, K - 1)];
-        if (k + 1 < K) fetch(ynxt, snxt, s1);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            o[nb][g][0] = fmaf(gcur, h_lo(ycur[nb][g].x) * scur[nb], o[nb][g][0]);
-            o[nb][g][1] = fmaf(gcur, h_hi(ycur[nb][g].x) * scur[nb], o[nb][g][1]);
-            o[nb][g][2] = fmaf(gcur, h_lo(ycur[nb][g].y) * scur[nb], o[nb][g][2]);
-            o[nb][g][3] = fmaf(gcur, h_hi(ycur[nb][g].y) * scur[nb], o[nb][g][3]);
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          scur[nb] = snxt[nb];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) ycur[nb][g] = ynxt[nb][g];
-        }
-        gcur = g1; g1 = g2; s1 = s2;
-      }
-      bf16_t* orow = out + (size_t)t * a.d;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // d is a multiple of 128: a 32-column block is all in or all out.
-        const int n = n0 + wn * WN + nb * 32;
-        if (n >= a.d) continue;
-        uint32_t p[4][2];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          p[g][0] = pack2(o[nb][g][0], o[nb][g][1]);
-          p[g][1] = pack2(o[nb][g][2], o[nb][g][3]);
-        }
-        swap_halves(p);
-        store_block(orow + n + 8 * hi, p);
       }
     }
   }
 }
 
-// The grouped FP8 GEMM: one workgroup per tile; routed tail tiles of at most
-// BM / 2 rows run the half-height layout.
-template <int MODE, int BM, int WAVES_M>
-__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
-  // Tiles of at most 128 rows keep a third stage (3 x (BM + 256) x 128 B
-  // <= 144 KB of LDS).
-  constexpr int NS = (BM <= 128) ? 3 : 2;
-  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
-  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
-  __shared__ uint8_t sA[BM * MAX_NK];
-  __shared__ uint8_t sB[2 * MAX_NK];
-  __shared__ float gmax[4 * BM];
-
+// One part of a grouped FP8 GEMM launch (block `blk` of `nblk`): routed tail
+// tiles of at most BM / 2 rows run the half-height layout.
+template <int MODE, int BM, int WAVES_M, int NS>
+__device__ __forceinline__ void gemm8_part(const GemmArgs& a, int blk, int nblk, u32x4* As0,
+                                           u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
+                                           u32x4* Bs2, uint8_t* sA, uint8_t* sB, float* gmax) {
   const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
   const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = xcd_remap(blk, nblk);
   const int ndim = n_tiles_of<MODE, BM>(a);
+  if (L >= mdim * ndim) return;              // padding of a launch's first part
   int mt, nt;
   constexpr int NGRP = ngrp_for<BM>();
   {
@@ -540,29 +457,68 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a) {
   }
 }
 
-template <int MODE, int BM, int WAVES_M>
-void launch_mode8(const GemmArgs& a, hipStream_t s) {
-  const bool routed = !(a.mode == 2 || (a.mode == 0 && a.shared));
-  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int ndim = n_tiles_of<MODE, BM>(a);
-  hipLaunchKernelGGL((gemm_fp8_kernel<MODE, BM, WAVES_M>), dim3(mdim * ndim), dim3(256), 0, s,
-                     a);
+// The grouped FP8 GEMM: one workgroup per tile; blocks [0, a_blocks) run
+// stage MODE on `a` (routed experts), the rest stage MODE_B on `b` (shared
+// experts), a_blocks a multiple of 8 (XCD-aware orders in both parts).
+template <int MODE, int MODE_B, int BM, int WAVES_M>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(GemmArgs a, GemmArgs b,
+                                                          int a_blocks) {
+  // Tiles of at most 128 rows keep a third stage (3 x (BM + 256) x 128 B
+  // <= 144 KB of LDS).
+  constexpr int NS = (BM <= 128) ? 3 : 2;
+  __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
+  __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
+  __shared__ uint8_t sA[BM * MAX_NK];
+  __shared__ uint8_t sB[2 * MAX_NK];
+  __shared__ float gmax[4 * BM];
+  // Each part reads its own argument struct (a run-time choice of struct
+  // made the compiler copy both to scratch memory).
+  const int blk = blockIdx.x;
+  if (blk >= a_blocks)
+    gemm8_part<MODE_B, BM, WAVES_M, NS>(b, blk - a_blocks, (int)gridDim.x - a_blocks, As0, As1,
+                                        As2, Bs0, Bs1, Bs2, sA, sB, gmax);
+  else
+    gemm8_part<MODE, BM, WAVES_M, NS>(a, blk, a_blocks, As0, As1, As2, Bs0, Bs1, Bs2, sA, sB,
+                                      gmax);
+}
+
+template <int MODE, int BM>
+int part_blocks8(const GemmArgs& g) {
+  const bool routed = !(MODE == 2 || (MODE == 0 && g.shared));
+  const int mdim = routed ? g.max_mtiles : (g.T + BM - 1) / BM;
+  return mdim * n_tiles_of<MODE, BM>(g);
+}
+
+template <int MODE, int MODE_B, int BM, int WAVES_M>
+void launch_pair8(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
+  if (!b) {
+    hipLaunchKernelGGL((gemm_fp8_kernel<MODE, MODE, BM, WAVES_M>),
+                       dim3(part_blocks8<MODE, BM>(a)), dim3(256), 0, s, a, a,
+                       part_blocks8<MODE, BM>(a));
+    return;
+  }
+  const int na = (part_blocks8<MODE, BM>(a) + 7) & ~7;
+  const int nb = part_blocks8<MODE_B, BM>(*b);
+  hipLaunchKernelGGL((gemm_fp8_kernel<MODE, MODE_B, BM, WAVES_M>), dim3(na + nb), dim3(256), 0,
+                     s, a, *b, na);
 }
 
 template <int BM, int WAVES_M>
-void launch_bm8(const GemmArgs& a, hipStream_t s) {
-  if (a.mode == 0) launch_mode8<0, BM, WAVES_M>(a, s);
-  else if (a.mode == 1) launch_mode8<1, BM, WAVES_M>(a, s);
-  else launch_mode8<2, BM, WAVES_M>(a, s);
+void launch_bm8(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
+  if (a.mode == 0) launch_pair8<0, 0, BM, WAVES_M>(a, b, s);
+  else if (a.mode == 1) launch_pair8<1, 2, BM, WAVES_M>(a, b, s);
+  else launch_pair8<2, 2, BM, WAVES_M>(a, nullptr, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s, const GemmArgs* b) {
+  if (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode) || a.mode == 2))
+    return hipErrorInvalidValue;
   switch (a.bm) {
-    case 256: launch_bm8<256, 2>(a, s); break;
-    case 128: launch_bm8<128, 1>(a, s); break;
-    case 64: launch_bm8<64, 1>(a, s); break;
+    case 256: launch_bm8<256, 2>(a, b, s); break;
+    case 128: launch_bm8<128, 1>(a, b, s); break;
+    case 64: launch_bm8<64, 1>(a, b, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

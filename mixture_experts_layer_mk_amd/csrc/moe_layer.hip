@@ -1,9 +1,11 @@
 // Host side of the C ABI (include/moe_layer.h): validation, workspace
 // layout, and the kernel sequence of one layer forward pass, enqueued on the
 // caller's stream with no host synchronisation and no device allocation.
-// bf16 and FP8 layers run the shared experts on a side stream (one per host
-// thread and device, created on first use and destroyed when the thread
-// exits), forked from and joined back into the caller's stream.
+// Each GEMM stage of the forward is one launch over the routed experts' tiles
+// and the shared experts'.  The backward runs its shared experts' branch on a
+// side stream (one per host thread and device, created on first use and
+// destroyed when the thread exits), forked from and joined back into the
+// caller's stream.
 #include "moe_layer.h"
 
 #include <atomic>
@@ -18,11 +20,9 @@ using namespace moe;
 
 namespace {
 
-constexpr int kStages = 8;
-const char* const kStageNames[kStages] = {
-    "router",            "scan",             "permute",
-    "gemm_gateup_routed", "gemm_gateup_shared", "gemm_down_routed",
-    "gemm_down_shared",  "combine"};
+constexpr int kStages = 6;
+const char* const kStageNames[kStages] = {"router",      "scan",      "permute",
+                                          "gemm_gateup", "gemm_down", "combine"};
 
 // Stages of the backward pass (moe_layer_backward_traced).
 constexpr int kBwdStages = 13;
@@ -51,31 +51,19 @@ int choose_bm(const moe_layer_desc_t& d) {
   return 64;
 }
 
-// The shared experts of bf16 and FP8 layers run concurrently with the router, the
-// dispatch and the routed experts (their combine then separate, on S = x +
-// shared experts in fp32).  Measured against the in-order sequence with the
-// combine fused into the shared down-projection: skewed 128-token batch
-// -16%, V3-shaped -3.6%, 2B-shaped -5%, 16B-shaped even.
-constexpr int kLateForkTokens = 1024;
-bool concurrent_shared(const moe_layer_desc_t& d) {
-  return d.dtype != MOE_F32 && d.n_shared > 0;
-}
-
-// Side stream and the fork / join events, per host thread and device (so
-// concurrent host threads never share them).  Default priority,
+// The backward's side stream and its fork / join events, per host thread and
+// device (so concurrent host threads never share them).  Default priority,
 // non-blocking with respect to the legacy default stream.  They live as long
 // as the host thread: its thread-exit destructor destroys them (HIP releases
 // a stream or event that still has work queued once that work completes).
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr;
-  hipEvent_t qx = nullptr;   // FP8 layers: the E4M3 token rows are ready
 };
 
 std::atomic<int32_t> g_live_side_streams{0};   // across threads (introspection)
 
 void destroy_side(SideStream& ss) {
-  if (ss.qx) (void)hipEventDestroy(ss.qx);
   if (ss.join2) (void)hipEventDestroy(ss.join2);
   if (ss.join) (void)hipEventDestroy(ss.join);
   if (ss.fork) (void)hipEventDestroy(ss.fork);
@@ -119,7 +107,6 @@ SideStream* side_stream(hipStream_t s) {
   ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipEventCreateWithFlags(&ss.join2, hipEventDisableTiming) == hipSuccess;
-  ok = ok && hipEventCreateWithFlags(&ss.qx, hipEventDisableTiming) == hipSuccess;
   if (!ok) destroy_side(ss);
   if (cur != dev) (void)hipSetDevice(cur);
   if (!ok) return nullptr;
@@ -196,10 +183,9 @@ Layout layout_of(const moe_layer_desc_t& d) {
   const bool bf16 = d.dtype != MOE_F32;   // bf16 activations (bf16, FP8)
   L.y = take(TK * d.d * (bf16 ? 2 : 4));
   L.y_scale = bf16 ? take(TK * (d.d / Y_GROUP) * 4) : -1;
-  // S = x + shared experts (fp32) only materialised for fp32 layers; bf16
-  // layers fuse the combine into the shared down-projection.
-  L.s = (d.n_shared > 0 && (d.dtype == MOE_F32 || concurrent_shared(d)))
-            ? take((int64_t)d.T * d.d * 4) : -1;
+  // S = x + shared experts (fp32), written by the shared down-projection and
+  // read by the combine.
+  L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
   L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
   L.planes = bf16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
@@ -228,14 +214,12 @@ hipError_t quant_x_rows(const moe_layer_desc_t& d, const Layout& L, char* ws, co
 // Router, per-expert scan and tile schedule, and the row maps (steps 1-3
 // of the forward; the backward re-runs them to recover the same expert
 // choice).  mark(i) records trace event i before step i.
-// (FP8 layers: also the token rows in E4M3 unless quant_x is false, when the
-// caller has quantised them already.)
+// (FP8 layers: also the token rows in E4M3.)
 template <class Mark>
 moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws,
                             const void* x, const float* w_gate, const float* logit_bias,
                             const float* select_bias, int32_t* idx, float* gw,
-                            int32_t* expert_counts, hipStream_t s, Mark mark,
-                            bool quant_x = true) {
+                            int32_t* expert_counts, hipStream_t s, Mark mark) {
   auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
   const bool bf16 = d.dtype != MOE_F32;
   const bool fp8 = d.dtype == MOE_FP8;
@@ -261,7 +245,7 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
     r.rank = static_cast<int32_t*>(at(L.rank));
     r.block_counts = static_cast<int32_t*>(at(L.block_counts));
     MOE_CHECK(launch_router(r, s));
-    if (fp8 && quant_x) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
+    if (fp8) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
   }
   // 2. scan + tile schedule
   if (!mark(1)) return MOE_ERR_HIP;
@@ -301,7 +285,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
                           int32_t* topk_idx, float* topk_w,
                           int32_t* expert_counts, void* workspace,
                           size_t workspace_bytes, void* stream_ptr,
-                          void* const* events, bool allow_side = true) {
+                          void* const* events) {
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_layer_desc_t& d = *desc;
@@ -345,84 +329,27 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
 
   MTile* tiles = static_cast<MTile*>(at(L.tiles));
   int32_t* n_tiles = static_cast<int32_t*>(at(L.n_tiles));
-  auto gemm_on = [&](const GemmArgs& g, hipStream_t st_) {
-    return fp8 ? launch_gemm_fp8(g, st_) : bf16 ? launch_gemm_bf16(g, st_)
-                                                : launch_gemm_f32(g, st_);
+  // One launch per GEMM stage holds the routed experts' tiles and, after
+  // them, the shared experts' (bf16 and FP8 layers): the shared tiles fill
+  // the GPU beside the routed ones (the routed experts' tile count is only
+  // known on the device).  fp32 layers launch the two groups one after the
+  // other.
+  auto gemm = [&](const GemmArgs& g, const GemmArgs* sh) -> hipError_t {
+    if (fp8) return launch_gemm_fp8(g, s, sh);
+    if (bf16) return launch_gemm_bf16(g, s, sh);
+    hipError_t e = launch_gemm_f32(g, s);
+    if (e == hipSuccess && sh) e = launch_gemm_f32(*sh, s);
+    return e;
   };
-  auto gemm = [&](const GemmArgs& g) { return gemm_on(g, s); };
   const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
   GemmArgs base{};
   base.d = d.d; base.tiles = tiles; base.n_tiles = n_tiles;
   base.max_mtiles = L.max_mtiles; base.T = d.T; base.bm = L.bm; base.x = x;
 
-  // The shared experts' two GEMMs (both paths below).
-  auto shared_gateup = [&]() {
-    GemmArgs g = base;
-    g.mode = 0; g.shared = true; g.a = x; g.lda = d.d;
-    g.w1 = shared.w1; g.w3 = shared.w3; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-    g.out = at(L.h_shared); g.ldo = (int)ksi;
-    if (fp8) {
-      g.a = at(L.x_q);
-      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
-      g.s1 = shared.s1; g.s3 = shared.s3;
-      g.out_scale = static_cast<uint8_t*>(at(L.h_shared_scale)); g.ldo_s = (int)(ksi / 128);
-    }
-    return g;
-  };
-  auto shared_down = [&]() {   // S (fp32) for fp32 layers and the side stream
-    GemmArgs g = base;
-    g.mode = 2; g.a = at(L.h_shared); g.lda = (int)ksi;
-    g.w2 = shared.w2; g.inner = d.shared_inner; g.n_experts = d.n_shared;
-    g.out = at(L.s); g.ldo = d.d;
-    if (fp8) {
-      g.a_scale = static_cast<const uint8_t*>(at(L.h_shared_scale)); g.lda_s = (int)(ksi / 128);
-      g.s2 = shared.s2;
-    }
-    return g;
-  };
-
-  // Shared experts on the side stream (untraced calls of bf16 and FP8
-  // layers): fork, shared gate/up and shared down -> S, join before the
-  // combine.  The shared stages touch only x (its E4M3 rows for FP8 layers,
-  // quantised before the fork), the shared weights, h_shared and S, which
-  // nothing on the caller's stream touches before the join.
-  //
-  // Batches of fewer than kLateForkTokens tokens fork after the router and
-  // the dispatch instead, which then run alone on the GPU (measured on the
-  // skewed 128-token batch: -9.5%; on the 16B shape the early fork is 1.2%
-  // faster, on the V3 shape 2.2%).
-  SideStream* side =
-      (allow_side && !events && concurrent_shared(d)) ? side_stream(s) : nullptr;
-  const bool late_fork = side && d.T < kLateForkTokens;
-  // With `quant` the side stream first quantises the token rows of an FP8
-  // layer, which the router does not read, and records `qx`; the caller's
-  // stream waits on it before the routed gate/up.  Done when the router takes
-  // its split path (group limit or many experts: the longer router hides the
-  // quantiser; V3-shaped FP8 layer -4%); behind the fused router the
-  // quantiser runs first on the caller's stream (2B-shaped: 1.4% faster so).
-  auto fork_shared = [&](bool quant) -> hipError_t {
-    hipError_t e = hipEventRecord(side->fork, s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
-    if (e == hipSuccess && quant) e = quant_x_rows(d, L, ws, x, side->s);
-    if (e == hipSuccess && quant) e = hipEventRecord(side->qx, side->s);
-    if (e == hipSuccess) e = gemm_on(shared_gateup(), side->s);
-    if (e == hipSuccess) e = gemm_on(shared_down(), side->s);   // no out2: S, combined separately
-    if (e == hipSuccess) e = hipEventRecord(side->join, side->s);
-    return e;
-  };
-  const bool quant_on_side =
-      fp8 && side && !late_fork &&
-      !router_fused(d.T, d.n_routed, d.top_k, d.n_groups, /*dtype=*/1);
-  if (side && !late_fork) {
-    if (fp8 && !quant_on_side) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
-    MOE_CHECK(fork_shared(quant_on_side));
-  }
-
   st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, expert_counts,
-                      s, mark, /*quant_x=*/side == nullptr || late_fork);
+                      s, mark);
   if (st != MOE_OK) return st;
-  if (late_fork) MOE_CHECK(fork_shared(false));   // the E4M3 rows of FP8 layers are ready
-  // 4. routed gate/up
+  // 4. gate/up: H = silu(A W1^T) * (A W3^T), routed rows gathered from x
   if (!mark(3)) return MOE_ERR_HIP;
   {
     GemmArgs g = base;
@@ -430,52 +357,44 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     g.a_rows = static_cast<const int32_t*>(at(L.row_src));
     g.w1 = routed.w1; g.w3 = routed.w3; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.h_routed); g.ldo = d.inner;
+    GemmArgs h = base;
+    h.mode = 0; h.shared = true; h.a = x; h.lda = d.d;
+    h.w1 = shared.w1; h.w3 = shared.w3; h.inner = d.shared_inner; h.n_experts = d.n_shared;
+    h.out = at(L.h_shared); h.ldo = (int)ksi;
     if (fp8) {
-      g.a = at(L.x_q);
-      g.a_scale = static_cast<const uint8_t*>(at(L.x_scale)); g.lda_s = d.d / 128;
+      g.a = h.a = at(L.x_q);
+      g.a_scale = h.a_scale = static_cast<const uint8_t*>(at(L.x_scale));
+      g.lda_s = h.lda_s = d.d / 128;
       g.s1 = routed.s1; g.s3 = routed.s3;
       g.out_scale = static_cast<uint8_t*>(at(L.h_routed_scale)); g.ldo_s = d.inner / 128;
+      h.s1 = shared.s1; h.s3 = shared.s3;
+      h.out_scale = static_cast<uint8_t*>(at(L.h_shared_scale)); h.ldo_s = (int)(ksi / 128);
     }
-    if (quant_on_side) MOE_CHECK(hipStreamWaitEvent(s, side->qx, 0));
-    MOE_CHECK(gemm(g));
+    MOE_CHECK(gemm(g, d.n_shared > 0 ? &h : nullptr));
   }
-  // 5. shared gate/up
+  // 5. down: Y = H W2^T of the routed rows; S = x + sum of the shared experts
   if (!mark(4)) return MOE_ERR_HIP;
-  if (d.n_shared > 0 && !side) MOE_CHECK(gemm(shared_gateup()));
-  // 6. routed down
-  if (!mark(5)) return MOE_ERR_HIP;
   {
     GemmArgs g = base;
     g.mode = 1; g.a = at(L.h_routed); g.lda = d.inner;
     g.w2 = routed.w2; g.inner = d.inner; g.n_experts = d.n_routed;
     g.out = at(L.y); g.ldo = d.d;
     g.yscale = bf16 ? static_cast<float*>(at(L.y_scale)) : nullptr;
+    GemmArgs h = base;
+    h.mode = 2; h.a = at(L.h_shared); h.lda = (int)ksi;
+    h.w2 = shared.w2; h.inner = d.shared_inner; h.n_experts = d.n_shared;
+    h.out = at(L.s); h.ldo = d.d;
     if (fp8) {
       g.a_scale = static_cast<const uint8_t*>(at(L.h_routed_scale)); g.lda_s = d.inner / 128;
       g.s2 = routed.s2;
+      h.a_scale = static_cast<const uint8_t*>(at(L.h_shared_scale)); h.lda_s = (int)(ksi / 128);
+      h.s2 = shared.s2;
     }
-    MOE_CHECK(gemm(g));
+    MOE_CHECK(gemm(g, d.n_shared > 0 ? &h : nullptr));
   }
-  // 7. shared down (+ residual); for bf16 layers the combine is fused here
-  // (not with the side stream: there the join comes first)
-  if (!mark(6)) return MOE_ERR_HIP;
-  const bool fused = bf16 && d.n_shared > 0 && !side;
-  if (side) MOE_CHECK(hipStreamWaitEvent(s, side->join, 0));
-  if (d.n_shared > 0 && !side) {
-    GemmArgs g = shared_down();
-    if (fused) {
-      g.ybuf = at(L.y);
-      g.yscale = static_cast<float*>(at(L.y_scale));
-      g.gw = gw;
-      g.slot_row = static_cast<const int32_t*>(at(L.slot_row));
-      g.K = d.top_k;
-      g.out2 = out;
-    }
-    MOE_CHECK(gemm(g));
-  }
-  // 8. combine (separate when not fused above)
-  if (!mark(7)) return MOE_ERR_HIP;
-  if (!fused) {
+  // 6. combine: out = RNE(base + sum_k g_k Y[slot_row[t, k]]), base = S or x
+  if (!mark(5)) return MOE_ERR_HIP;
+  {
     CombineArgs c{};
     c.base = d.n_shared > 0 ? at(L.s) : x;
     c.base_f32 = d.n_shared > 0;
@@ -485,7 +404,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
     c.out = out; c.dtype = bf16 ? 1 : 0; c.T = d.T; c.d = d.d; c.K = d.top_k;
     MOE_CHECK(launch_combine(c, s));
   }
-  if (!mark(8)) return MOE_ERR_HIP;
+  if (!mark(6)) return MOE_ERR_HIP;
 #undef MOE_CHECK
   return MOE_OK;
 }
@@ -881,7 +800,7 @@ moe_status_t moe_layer_forward_noalloc(const moe_layer_desc_t* desc, const void*
   }
   return forward_impl(desc, x, w_gate, logit_bias, select_bias, routed, shared, out,
                       topk_idx, topk_w, expert_counts, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
-                      nullptr, /*allow_side=*/false);
+                      nullptr);
 }
 
 int32_t moe_side_stream_count(void) {

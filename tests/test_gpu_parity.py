@@ -90,16 +90,12 @@ def test_deterministic_bitwise():
                                         ("16b-T2600", None), ("16b-T2600", "fp8"),
                                         ("skewed-16b-small", "fp8"), ("16b-T1023", None),
                                         ("16b-T1024", None), ("v3-d512-T4096", "fp8")])
-def test_side_stream_matches_in_order(name, dtype):
-    """bf16 layers with shared experts run them on a side stream when the
-    call is not traced (S = x + shared experts in fp32, then the separate
-    combine), for weight-streaming tiles and 256-row tiles (16b-T2600)
-    alike, and for FP8 layers (the E4M3 token rows are quantised before the
-    fork, or on the side stream behind the split router: v3-d512-T4096).  Batches of fewer than 1024 tokens fork after the router and the
-    dispatch, larger ones at the start of the call (16b-T1023 / 16b-T1024).  A traced call runs every stage in order with the combine fused
-    into the shared down-projection.  Both add the same fp32 terms in the same order, so the
-    outputs are bitwise equal, on repeated calls too (the side stream's
-    writes of one call never overtake the previous call's reads)."""
+def test_traced_matches_untraced(name, dtype):
+    """A traced call (events recorded between the stages) runs the same
+    launches as an untraced one: the outputs are bitwise equal, on repeated
+    calls too.  Cases: weight-streaming tiles (skewed batch, V3 routing),
+    256-row tiles, FP8 layers, the router's split/fused switch at 1023/1024
+    tokens."""
     from mixture_experts_layer_mk_amd import HipEvents, trace_stage_names
     cfg = REDUCED[name] if dtype is None else REDUCED[name].replace(dtype=dtype)
     case = Case(cfg)

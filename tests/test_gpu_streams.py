@@ -1,14 +1,15 @@
-"""GPU tests of the forward's stream behaviour: bf16 layers with shared
-experts run the shared experts on a side stream (one per host thread and
-device), forked from the caller's stream and joined back into it.
+"""GPU tests of the layer's stream behaviour.
 
-* Stream capture: the call captured into a graph on a side stream of torch's
-  own, replayed several times with eager work and synchronisations in
+* Stream capture: the forward captured into a graph on a side stream of
+  torch's own, replayed several times with eager work and synchronisations in
   between, gives the eager result bitwise on every replay (the library
-  enqueues no memset or copy, only kernels and event waits).
+  enqueues no memset or copy, only kernels).
 * Host threads: two threads, each with its own stream and workspace, calling
   the layer repeatedly at the same time, give the single-threaded result
-  bitwise (each thread has its own side stream and events).
+  bitwise; threads that call the forward once and exit match too, and leave
+  no side stream behind (the forward uses none).
+* The backward runs its shared experts' branch on a side stream, one per
+  host thread and device: threads that call it once and exit destroy theirs.
 """
 import sys
 import threading
@@ -120,10 +121,9 @@ def test_forward_concurrent_host_threads():
     say("[threads] 2 threads x 4 calls equal")
 
 
-def test_forward_short_lived_threads_release_side_streams():
-    """Threads that call the layer once and exit: each gets its own side stream
-    (results bitwise equal to the main thread's) and destroys it on exit, so
-    the library's side-stream count returns to where it was."""
+def test_forward_short_lived_threads():
+    """Threads that call the forward once and exit: results bitwise equal to
+    the main thread's, and no side stream is created."""
     import mixture_experts_layer_mk_amd as moe
     case = Case(C["deepseekmoe-16b"].replace(T=1200, seed=11))
     ws0 = _workspace(case)
@@ -131,8 +131,7 @@ def test_forward_short_lived_threads_release_side_streams():
     _forward(case, ref, ws0)
     torch.cuda.synchronize()
     base = moe.side_stream_count()
-    assert base >= 1            # the main thread's own
-    results, errors, during = {}, [], []
+    results, errors = {}, []
 
     def worker(k):
         try:
@@ -142,7 +141,6 @@ def test_forward_short_lived_threads_release_side_streams():
             with torch.cuda.stream(s):
                 _forward(case, out, ws)
             s.synchronize()
-            during.append(moe.side_stream_count())
             results[k] = out
         except Exception as e:   # reported below, in the main thread
             errors.append(repr(e))
@@ -157,12 +155,60 @@ def test_forward_short_lived_threads_release_side_streams():
     assert sorted(results) == list(range(12))
     for k, o in results.items():
         assert torch.equal(o, ref), f"thread {k} differs"
+    assert moe.side_stream_count() == base
+    say("[threads] 12 short-lived forward threads equal")
+
+
+def test_backward_short_lived_threads_release_side_streams():
+    """Threads that call the backward once and exit: each gets its own side
+    stream (gradients bitwise equal to the main thread's) and destroys it on
+    exit, so the library's side-stream count returns to where it was."""
+    import time
+    import mixture_experts_layer_mk_amd as moe
+    import workloads as wl
+    cfg = C["deepseekmoe-16b"].replace(T=300, d=256, inner=128, shared_inner=128, seed=12)
+    case = Case(cfg)
+    d = case.dev
+    dout = torch.from_numpy(wl.make_inputs(cfg).dout()).to(torch.bfloat16).cuda()
+
+    def bwd():
+        return moe.moe_layer_backward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k,
+                                      dout)
+    ref = bwd()
+    torch.cuda.synchronize()
+    base = moe.side_stream_count()
+    assert base >= 1            # the main thread's own
+    results, errors, during = {}, [], []
+
+    def worker(k):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                g = bwd()
+            s.synchronize()
+            during.append(moe.side_stream_count())
+            results[k] = g
+        except Exception as e:   # reported below, in the main thread
+            errors.append(repr(e))
+
+    for wave in range(4):
+        threads = [threading.Thread(target=worker, args=(3 * wave + j,)) for j in range(3)]
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join(timeout=120)
+    assert not errors, errors
+    assert sorted(results) == list(range(12))
+    for k, g in results.items():
+        assert torch.equal(g["dx"], ref["dx"]), f"thread {k}: dx differs"
+        for part in ("routed", "shared"):
+            for a, b in zip(g[part], ref[part]):
+                assert torch.equal(a, b), f"thread {k}: {part} gradients differ"
     assert min(during) >= base + 1
     # join() returns when the Python thread is done; the thread-exit
     # destructors run just after, as the OS thread ends
-    import time
     deadline = time.time() + 10
     while moe.side_stream_count() != base and time.time() < deadline:
         time.sleep(0.05)
     assert moe.side_stream_count() == base, "side streams of exited threads were kept"
-    say(f"[threads] 12 short-lived threads equal; side streams back to {base}")
+    say(f"[threads] 12 short-lived backward threads equal; side streams back to {base}")
