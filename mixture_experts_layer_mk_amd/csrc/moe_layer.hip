@@ -897,7 +897,12 @@ moe_status_t moe_bias_update(const int32_t* counts, int32_t n_routed, float gamm
 }
 
 const char* moe_strerror(moe_status_t status) {
-  switch (status) {
+  // A C caller may pass any int: read the bits as one, since an enum value
+  // outside the enumerators' range may not be loaded as the enum in C++.
+  int32_t v;
+  static_assert(sizeof(v) == sizeof(status), "status is an int");
+  std::memcpy(&v, &status, sizeof v);
+  switch (v) {
     case MOE_OK: return "success";
     case MOE_ERR_INVALID_ARG: return "invalid argument";
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
