@@ -17,6 +17,8 @@
 // Tile: 256 (M) x 256 (N) per workgroup of 4 waves (2 x 2, 128 x 128 each),
 // k in steps of 64, LDS double-buffered (2 x 64 KB), operand fragments
 // double-buffered in registers as in the forward kernels.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -26,7 +28,8 @@ namespace {
 using namespace gemm;
 
 constexpr int TM = 256;     // tile rows (M)
-constexpr int TK = 64;      // k per stage
+constexpr int TK = 32;      // k per stage
+constexpr int NS = 4;       // stages in the LDS ring: NS - 1 in flight while one is computed
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -38,20 +41,36 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // bank groups (one full pass over the banks, no conflict).
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
+// Chunk swizzle of k-major LDS rows (32 k = 4 chunks of 16 B per row).  A
+// fragment load reads the same chunk of consecutive rows; 8 consecutive
+// rows span 512 B and 16 span 1 KB, and in either group the rows sharing a
+// 128-byte (respectively 256-byte) bank window get 4 different chunks from
+// f(r) = 2 r2 + (r1 ^ r3) (r_i: bit i of the row), so a pass over 8 or 16
+// lanes hits each 16-byte bank group once.
+__device__ __forceinline__ int swz_k(int r) {
+  return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+}
+
 // A 32 (mn) x 16 (k) operand fragment for the matrix op from an mn-major
-// LDS tile (64 k-rows x 32 chunks): lanes 0-31 hold mn = base + lane % 32 at
-// k = 16 kk + 0..7, lanes 32-63 the same mn at k + 8.
-__device__ __forceinline__ bf16x8 frag_mn(const u32x4* T, int base, int kk, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int mn = base + 16 * (g & 1) + 4 * (s & 3);
-  const int chunk = mn >> 3, half = (mn >> 2) & 1;
-  const int k0 = kk * 16 + 8 * (g >> 1) + (s >> 2);
-  const char* t = reinterpret_cast<const char*>(T);
-  const int o0 = k0 * 512 + ((chunk ^ swz_mn(k0)) << 4) + half * 8;
-  const int k1 = k0 + 4;
-  const int o1 = k1 * 512 + ((chunk ^ swz_mn(k1)) << 4) + half * 8;
-  const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + o0));
-  const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + o1));
+// LDS tile (32 k-rows x 32 chunks): lanes 0-31 hold mn = base + lane % 32 at
+// k = 16 kk + 0..7, lanes 32-63 the same mn at k + 8.  With base = 128 w +
+// 32 i, lane (g = lane / 16, s = lane % 16) reads 4 consecutive mn at k-rows
+// k0 = 16 kk + 8 (g / 2) + s / 4 and k0 + 4, chunk 16 w + 4 i + 2 (g % 2) +
+// (s % 4) / 2, half s % 2.  The chunk swizzle 4 (k0 mod 4) = 4 (s / 4) only
+// flips bits 2-3, the bits of i, so the byte offset is a lane term for each
+// i plus 8192 kk (+ 2048 for the second k-row): the lane terms are computed
+// once per tile and the k-step parts are instruction immediates.
+__device__ __forceinline__ uint32_t frag_mn_off(int w, int i, int lane) {
+  const int g = lane >> 4, s = lane & 15, q = s >> 2;
+  const int chunk = 16 * w + ((i ^ q) << 2) + 2 * (g & 1) + ((s & 3) >> 1);
+  return (uint32_t)((8 * (g >> 1) + q) * 512 + (chunk << 4) + (s & 1) * 8);
+}
+
+template <int KK>
+__device__ __forceinline__ bf16x8 frag_mn(const u32x4* T, uint32_t off) {
+  const char* t = reinterpret_cast<const char*>(T) + off + KK * 8192;
+  const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)t);
+  const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(t + 2048));
   const v4s r[2] = {r0, r1};
   return __builtin_bit_cast(bf16x8, r);
 }
@@ -112,55 +131,58 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
 
 template <int KIND, bool SH>
 __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
-  __shared__ u32x4 As0[2048], As1[2048];   // 32 KB each: 256 x 8 or 64 x 32 chunks
-  __shared__ u32x4 Bs0[2048], Bs1[2048];
+  // The LDS ring: NS stages of A and B, 16 KB each (256 x 4 or 32 x 32
+  // chunks).  Distinct objects, so that the compiler's waits for the direct
+  // loads tell the stages apart.
+  __shared__ u32x4 A0[1024], A1[1024], A2[NS > 2 ? 1024 : 1], A3[NS > 3 ? 1024 : 1], A4[NS > 4 ? 1024 : 1];
+  __shared__ u32x4 B0[1024], B1[1024], B2[NS > 2 ? 1024 : 1], B3[NS > 3 ? 1024 : 1], B4[NS > 4 ? 1024 : 1];
 
   TileDesc t;
   if (!decode<KIND, SH>(a, t)) return;
 
   constexpr bool AK = (KIND == 0 || KIND == 1);   // A k-major; B is always mn-major
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform: the LDS destinations of the direct loads stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int l32 = lane & 31, hi = lane >> 5;
   const int nk = (t.K + TK - 1) / TK;
 
-  // ---- k-major A (KIND 0, 1): 256 rows x 8 chunks per stage ----
-  // Lane slot: LDS row (wave * 8 + j) * 8 + lr, chunk (lane & 7) after the
-  // row swizzle, as in the forward kernels.  Element offsets from the
-  // operand's base (32 bits: validation bounds every operand below 2^32
-  // elements); each stage adds k0.
-  const int lr = lane >> 3;
-  const int cg0 = (lane & 7) ^ lr, cg1 = cg0 ^ 1;
+  // ---- k-major A (KIND 0, 1): 256 rows x 4 chunks per stage ----
+  // Direct load j of the wave fills LDS slots (4 wave + j) 64 + lane: row
+  // (4 wave + j) 16 + lane / 4, slot chunk lane % 4, which holds global
+  // chunk (lane % 4) ^ swz_k(row).  Element offsets from the operand's base
+  // (validation keeps every activation below 2^31 elements); a stage adds k0.
   const bf16_t* abase = nullptr;
-  uint32_t aoff[8];
+  uint32_t aoff[4];
   if constexpr (AK) {
     int ld;
     if (KIND == 0) { abase = a.dy; ld = a.d; }
     else { abase = a.da; ld = a.ldda; }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = wave * 8 + j;
-      const int r = min(blk * 8 + lr, t.mval - 1);
+    for (int j = 0; j < 4; ++j) {
+      const int r = (wave * 4 + j) * 16 + (lane >> 2);
+      const int rc = min(r, t.mval - 1);
       // routed dy rows: the row's token (a gather resolved once per tile)
-      const int row = (KIND == 0 && !SH) ? a.row_src[t.row0 + r] : t.row0 + r;
-      aoff[j] = (uint32_t)row * (uint32_t)ld + ((blk & 1) ? cg1 : cg0) * 8;
+      const int row = (KIND == 0 && !SH) ? a.row_src[t.row0 + rc] : t.row0 + rc;
+      aoff[j] = (uint32_t)row * (uint32_t)ld + (uint32_t)(((lane & 3) ^ swz_k(r)) * 8);
     }
   }
 
-  // ---- mn-major operands: 64 k-rows x 32 chunks per stage ----
-  // Lane slot: k-row kr_j = 2 (wave * 8 + j) + (lane >> 5), chunk (lane & 31),
-  // which holds global chunk (lane & 31) ^ swz_mn(kr_j) of that row (the
-  // tile's first chunk past the operand's last column: never stored).  The
-  // offset of the lane's chunk inside the stage's first k-row is fixed; a
+  // ---- mn-major operands: 32 k-rows x 32 chunks per stage ----
+  // Direct load j fills k-row kr_j = 2 (4 wave + j) + (lane >> 5), slot
+  // chunk (lane & 31), which holds global chunk (lane & 31) ^ swz_mn(kr_j)
+  // of that row (the tile's first chunk past the operand's last column: never
+  // stored).  The lane's offset inside the stage's first k-row is fixed; a
   // stage adds its uniform row base, and k-rows past the end read zeros.
   const int ks = lane >> 5, cs = lane & 31;
   auto mn_off = [&](int j, int col0, int extent, int ld) -> uint32_t {
-    const int kr = 2 * (wave * 8 + j) + ks;
+    const int kr = 2 * (wave * 4 + j) + ks;
     int c = cs ^ swz_mn(kr);
     if (col0 + c * 8 >= extent) c = 0;
     return (uint32_t)kr * (uint32_t)ld + (uint32_t)(col0 + c * 8);
   };
-  uint32_t moff_a[8], moff_b[8];
+  uint32_t moff_a[4], moff_b[4];
   int lda_mn = 0, ldb_mn;
   if (KIND == 0) ldb_mn = a.inner;
   else if (KIND == 1) ldb_mn = a.d;
@@ -168,25 +190,35 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   else { lda_mn = a.ldda; ldb_mn = a.d; }
   // Routed weight gradients read one operand's k-rows from token rows (dy
   // for KIND 2's A, x for KIND 3's B): that operand's offsets hold only the
-  // column part, and the tokens of the next stage's k-rows are loaded one
-  // stage ahead (the wait before each stage's barrier covers them).
+  // column part, and each stage adds its k-rows' tokens.
   constexpr bool gath = (KIND == 2 || KIND == 3) && !SH;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 4; ++j) {
     if constexpr (!AK) moff_a[j] = mn_off(j, t.m0, t.mval, (KIND == 2 && gath) ? 0 : lda_mn);
     moff_b[j] = mn_off(j, t.n0, t.nval, (KIND == 3 && gath) ? 0 : ldb_mn);
   }
-  int tok[8];
-  auto load_tokens = [&](int kb) {
+  // The tokens of a stage's k-rows: wave-uniform addresses, read through the
+  // scalar cache, so that their wait is the LDS counter's, not the direct
+  // loads'.  A block reads the tokens of the stage it issues at its start;
+  // the wait before its barrier covers them.
+  const __attribute__((address_space(4))) int32_t* rsrc = nullptr;
+  if constexpr (gath)
+    rsrc = (const __attribute__((address_space(4))) int32_t*)(a.row_src + t.koff + t.kbeg);
+  struct Tok { int t0[4], t1[4]; };   // tokens of k-rows 2 (4 wave + j) and 2 (4 wave + j) + 1
+  auto load_tok = [&](int kb) {
+    Tok tk;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int k = kb * TK + 2 * (wave * 8 + j) + ks;
-      tok[j] = (k < t.K) ? a.row_src[t.koff + t.kbeg + k] : 0;
+    for (int j = 0; j < 4; ++j) {
+      tk.t0[j] = tk.t1[j] = 0;
+      if constexpr (gath) {
+        const int k = kb * TK + 2 * (wave * 4 + j);
+        // k-rows past the end read the last token (never used: zero rows)
+        tk.t0[j] = rsrc[min(k, t.K - 1)];
+        tk.t1[j] = rsrc[min(k + 1, t.K - 1)];
+      }
     }
+    return tk;
   };
-  if constexpr (gath) {
-    if (nk > 0) load_tokens(0);
-  }
   // uniform base of the stage's first k-row (k0 relative to the tile's k range)
   auto a_stage = [&](int k0) -> const bf16_t* {
     const size_t row = (size_t)t.koff + t.kbeg + k0;
@@ -207,25 +239,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
     return SH ? a.x + row * a.d : a.x;                      // KIND 3; routed: gathered
   };
 
-  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb) {
+  // Direct loads of stage kb into (Ab, Bb): 4 + 4 per wave.  Stages past the
+  // end load the zero row (their buffers are never read).
+  auto issue = [&](int kb, u32x4* Ab, u32x4* Bb, const Tok& tk) {
     const int k0 = kb * TK;
+    const bool stage_live = k0 < t.K;
+    const int kc = stage_live ? k0 : 0;   // keeps the unused stage bases in range
     const bf16_t* zr = a.zero + cs * 8;
     const bf16_t* as = nullptr;
-    if constexpr (!AK) as = a_stage(k0);
-    const bf16_t* bs = b_stage(k0);
+    if constexpr (!AK) as = a_stage(kc);
+    const bf16_t* bs = b_stage(kc);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = wave * 8 + j;
-      const bool live = k0 + 2 * blk + ks < t.K;   // k-major A: K is whole stages
-      const uint32_t trow = (uint32_t)tok[j] * (uint32_t)a.d;
+    for (int j = 0; j < 4; ++j) {
+      const int blk = wave * 4 + j;
+      const bool live = k0 + 2 * blk + ks < t.K;
+      uint32_t trow = 0;
+      if constexpr (gath) trow = (uint32_t)(ks ? tk.t1[j] : tk.t0[j]) * (uint32_t)a.d;
       const bf16_t* ga;
-      if constexpr (AK) ga = abase + aoff[j] + k0;
+      if constexpr (AK) ga = stage_live ? abase + aoff[j] + k0 : zr;   // K is whole stages
       else ga = live ? as + moff_a[j] + ((KIND == 2 && gath) ? trow : 0u) : zr;
       __builtin_amdgcn_global_load_lds((const glb_void*)ga, (lds_void*)&Ab[blk * 64], 16, 0, 0);
       const bf16_t* gb = live ? bs + moff_b[j] + ((KIND == 3 && gath) ? trow : 0u) : zr;
       __builtin_amdgcn_global_load_lds((const glb_void*)gb, (lds_void*)&Bb[blk * 64], 16, 0, 0);
     }
-    if constexpr (gath) load_tokens(min(kb + 1, nk - 1));    // the next stage issued
   };
 
   f32x16 acc[4][4];
@@ -236,21 +272,38 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Byte offsets of the lane's fragments inside an LDS buffer at k-step 0.
+  // k-major A: row r = 128 wm + 32 mb + l32 holds k-step kk's chunk
+  // (2 kk + hi) ^ swz_k(r) at byte 64 r + 16 chunk; swz_k(r) depends only on
+  // l32, so one lane term per kk with 2048 mb as an immediate.
+  uint32_t fo_a[4], fo_b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (AK) {
+      const int r = wm * 128 + l32;
+      fo_a[i] = (uint32_t)(r * 64 + ((((2 * i + hi) & 3) ^ swz_k(r)) << 4));
+    } else {
+      fo_a[i] = frag_mn_off(wm, i, lane);
+    }
+    fo_b[i] = frag_mn_off(wn, i, lane);
+  }
   bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto load_frags = [&](bf16x8* fa, bf16x8* fb, const u32x4* Ab, const u32x4* Bb, int kk) {
-    const int c = 2 * kk + hi;
+  auto load_frags = [&](bf16x8* fa, bf16x8* fb, const u32x4* Ab, const u32x4* Bb, auto kk_c) {
+    constexpr int kk = decltype(kk_c)::value;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if constexpr (AK) {
-        const int r = wm * 128 + mb * 32 + l32;
-        fa[mb] = __builtin_bit_cast(bf16x8, Ab[r * 8 + (c ^ swz_x(r))]);
+        const char* p = reinterpret_cast<const char*>(Ab) + fo_a[kk] + mb * 2048;
+        fa[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
       } else {
-        fa[mb] = frag_mn(Ab, wm * 128 + mb * 32, kk, lane);
+        fa[mb] = frag_mn<kk>(Ab, fo_a[mb]);
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) fb[nb] = frag_mn(Bb, wn * 128 + nb * 32, kk, lane);
+    for (int nb = 0; nb < 4; ++nb) fb[nb] = frag_mn<kk>(Bb, fo_b[nb]);
   };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
   auto mma = [&](const bf16x8* fa, const bf16x8* fb) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
@@ -260,78 +313,113 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
                                                              0, 0, 0);
   };
   constexpr int N_DS = (AK ? 4 : 8) + 8;
-  auto sched_ds = [&]() { sched_groups<16, N_DS, 0>(); };
-  auto sched_ds_vm = [&]() { sched_groups<16, N_DS, 16>(); };
+  constexpr int N_VM = 8;   // direct loads per stage and wave
 
-  // Same pipeline as the forward kernels: block kb from (Ac, Bc) while kb+1
-  // streams into (An, Bn); kb+2 is issued into (Ac, Bc) once every wave
-  // holds its last fragments of kb.  Blocks past the end re-load the last.
-  auto block = [&](int next2, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
-    load_frags(fa1, fb1, Ac, Bc, 1);
+  // Stage kb from (Ac, Bc); stage kb+1 is in (An, Bn) or streaming into it,
+  // with the NS - 2 stages after it.  Half-way through (every wave holds its
+  // last fragments of kb), the wait for stage kb+1 and the barrier; then
+  // stage kb+NS streams into (Ac, Bc) while the second half runs.
+  auto block = [&](int kb, u32x4* Ac, u32x4* Bc, const u32x4* An, const u32x4* Bn) {
+    const Tok tk = load_tok(kb + NS);
+    load_frags(fa1, fb1, Ac, Bc, K1{});
     mma(fa0, fb0);
-    sched_ds();
-    load_frags(fa0, fb0, Ac, Bc, 2);
+    sched_groups<16, N_DS, 0>();
+    stage_sync<(NS - 2) * N_VM>();
+    issue(kb + NS, Ac, Bc, tk);
+    load_frags(fa0, fb0, An, Bn, K0{});
     mma(fa1, fb1);
-    sched_ds();
-    load_frags(fa1, fb1, Ac, Bc, 3);
-    mma(fa0, fb0);
-    sched_ds();
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue(next2, Ac, Bc);
-    load_frags(fa0, fb0, An, Bn, 0);
-    mma(fa1, fb1);
-    sched_ds_vm();
+    sched_groups<16, N_DS, N_VM>();
   };
 
   if (nk > 0) {
-    issue(0, As0, Bs0);
-    issue(min(1, nk - 1), As1, Bs1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<16>());
-    __syncthreads();
-    load_frags(fa0, fb0, As0, Bs0, 0);
-    int kb = 0;
-    for (; kb + 2 <= nk; kb += 2) {
-      block(min(kb + 2, nk - 1), As0, Bs0, As1, Bs1);
-      block(min(kb + 3, nk - 1), As1, Bs1, As0, Bs0);
+    Tok tp[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) tp[i] = load_tok(i);
+    issue(0, A0, B0, tp[0]);
+    issue(1, A1, B1, tp[1]);
+    if constexpr (NS > 2) issue(2, A2, B2, tp[2]);
+    if constexpr (NS > 3) issue(3, A3, B3, tp[3]);
+    if constexpr (NS > 4) issue(4, A4, B4, tp[4]);
+    stage_sync<(NS - 1) * N_VM>();   // stage 0 landed
+    load_frags(fa0, fb0, A0, B0, K0{});
+    // NS blocks per iteration, each with its own static buffers.  Stages
+    // past the tile's end (at most NS - 1, in the last iteration) hold zero
+    // rows and add nothing; running them keeps the loop free of branches.
+    for (int kb = 0; kb < nk; kb += NS) {
+      block(kb, A0, B0, A1, B1);
+      if constexpr (NS == 2) {
+        block(kb + 1, A1, B1, A0, B0);
+      } else {
+        block(kb + 1, A1, B1, A2, B2);
+        if constexpr (NS == 3) {
+          block(kb + 2, A2, B2, A0, B0);
+        } else {
+          block(kb + 2, A2, B2, A3, B3);
+          if constexpr (NS == 4) {
+            block(kb + 3, A3, B3, A0, B0);
+          } else {
+            block(kb + 3, A3, B3, A4, B4);
+            block(kb + 4, A4, B4, A0, B0);
+          }
+        }
+      }
     }
-    if (kb < nk) block(nk - 1, As0, Bs0, As1, Bs1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load left in flight
   }
 
   // ---- epilogue: acc[nb][mb][r] = C[m][n], m = mb*32 + l32 and
-  // n = nb*32 + 8*(r/4) + 4*hi + r%4 inside the wave's 128 x 128 ----
+  // n = nb*32 + 8*(r/4) + 4*hi + r%4 inside the wave's 128 x 128.  A lane
+  // holds one row, so direct stores would write 32 bytes into each of 32
+  // rows per instruction.  Each 32 x 64 half block (one mb, two nb) goes
+  // through the wave's own LDS buffer instead (rows padded to 68 floats) and
+  // leaves as four whole 256-byte row segments per store instruction.  The
+  // buffers are free once every wave has passed the barrier (each wave's
+  // direct loads have completed above); a wave's LDS operations run in
+  // order, so the buffers need no further barrier. ----
+  __syncthreads();
+  constexpr int SP = 68;
+  float* stg = reinterpret_cast<float*>(wave == 0 ? A0 : wave == 1 ? A1 : wave == 2 ? A2 : A3);
+  const int rq = lane >> 4, cq = (lane & 15) * 4;   // read-back: row rq + 4 i, columns cq..+3
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int m = t.m0 + wm * 128 + mb * 32 + l32;
-    if (m >= t.mval) continue;
-    float* crow;
-    if (KIND == 0) {
-      const size_t col = SH ? (size_t)t.grp * a.inner : 0;
-      crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
-    } else if (KIND == 1) {
-      crow = a.c + (size_t)(t.row0 + m) * a.ldc;
-    } else if (a.splits > 1) {   // partial sums [split][group][M][N], reduced later
-      crow = a.part + (((size_t)t.split * a.n_experts + t.grp) * t.mval + m) * t.nval;
-    } else if (KIND == 2) {
-      crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
-    } else {
-      crow = (m < a.inner) ? a.dw1 + ((size_t)t.grp * a.inner + m) * a.d
-                           : a.dw3 + ((size_t)t.grp * a.inner + (m - a.inner)) * a.d;
-    }
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = t.n0 + wn * 128 + nb * 32 + 8 * g + 4 * hi;
-        if (n >= t.nval) continue;
-        float4 v;
-        v.x = acc[nb][mb][4 * g + 0];
-        v.y = acc[nb][mb][4 * g + 1];
-        v.z = acc[nb][mb][4 * g + 2];
-        v.w = acc[nb][mb][4 * g + 3];
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nb = 2 * h + q;
+          float4 v;
+          v.x = acc[nb][mb][4 * g + 0];
+          v.y = acc[nb][mb][4 * g + 1];
+          v.z = acc[nb][mb][4 * g + 2];
+          v.w = acc[nb][mb][4 * g + 3];
+          *reinterpret_cast<float4*>(stg + l32 * SP + q * 32 + 8 * g + 4 * hi) = v;
+        }
+      const int n = t.n0 + wn * 128 + h * 64 + cq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int rr = rq + 4 * i;
+        const float4 v = *reinterpret_cast<const float4*>(stg + rr * SP + cq);
+        const int m = t.m0 + wm * 128 + mb * 32 + rr;
+        if (m >= t.mval || n >= t.nval) continue;
+        float* crow;
+        if (KIND == 0) {
+          const size_t col = SH ? (size_t)t.grp * a.inner : 0;
+          crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
+        } else if (KIND == 1) {
+          crow = a.c + (size_t)(t.row0 + m) * a.ldc;
+        } else if (a.splits > 1) {   // partial sums [split][group][M][N], reduced later
+          crow = a.part + (((size_t)t.split * a.n_experts + t.grp) * t.mval + m) * t.nval;
+        } else if (KIND == 2) {
+          crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
+        } else {
+          crow = (m < a.inner) ? a.dw1 + ((size_t)t.grp * a.inner + m) * a.d
+                               : a.dw3 + ((size_t)t.grp * a.inner + (m - a.inner)) * a.d;
+        }
         *reinterpret_cast<float4*>(crow + n) = v;
       }
+    }
   }
 }
 
