@@ -41,16 +41,6 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 // bank groups (one full pass over the banks, no conflict).
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
-// Chunk swizzle of k-major LDS rows (32 k = 4 chunks of 16 B per row).  A
-// fragment load reads the same chunk of consecutive rows; 8 consecutive
-// rows span 512 B and 16 span 1 KB, and in either group the rows sharing a
-// 128-byte (respectively 256-byte) bank window get 4 different chunks from
-// f(r) = 2 r2 + (r1 ^ r3) (r_i: bit i of the row), so a pass over 8 or 16
-// lanes hits each 16-byte bank group once.
-__device__ __forceinline__ int swz_k(int r) {
-  return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
-}
-
 // A 32 (mn) x 16 (k) operand fragment for the matrix op from an mn-major
 // LDS tile (32 k-rows x 32 chunks): lanes 0-31 hold mn = base + lane % 32 at
 // k = 16 kk + 0..7, lanes 32-63 the same mn at k + 8.  With base = 128 w +

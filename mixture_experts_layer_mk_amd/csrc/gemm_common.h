@@ -20,6 +20,16 @@ constexpr int BN = 256;   // weight rows per workgroup
 // 8 consecutive rows, and 16 rows split by bank half, hit distinct banks.
 __device__ __forceinline__ int swz_x(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// Chunk swizzle of k-major LDS rows (32 k = 4 chunks of 16 B per row).  A
+// fragment load reads the same chunk of consecutive rows; 8 consecutive
+// rows span 512 B and 16 span 1 KB, and in either group the rows sharing a
+// 128-byte (respectively 256-byte) bank window get 4 different chunks from
+// f(r) = 2 r2 + (r1 ^ r3) (r_i: bit i of the row), so a pass over 8 or 16
+// lanes hits each 16-byte bank group once.
+__device__ __forceinline__ int swz_k(int r) {
+  return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+}
+
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int x = b & 7, j = b >> 3, q = n >> 3, r = n & 7;
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
