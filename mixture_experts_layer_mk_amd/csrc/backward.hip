@@ -197,55 +197,77 @@ __global__ __launch_bounds__(256) void gate_grad_sum_kernel(BwdAuxArgs a) {
 }
 
 // dx = RNE(dy + dx_shared + sum_k dx_rows[slot_row[t][k]] + dl Wg): thread =
-// column j, DX_T tokens per workgroup.  The router term first (each Wg
-// element read once per workgroup, the tokens' dl rows staged in LDS), then
-// the row sums, four tokens' loads at a time.
+// columns 4 j .. 4 j + 3, DX_T tokens per workgroup.  The router term first
+// (each 4-column group of Wg read once per workgroup, the tokens' dl rows
+// staged in LDS), then the row sums, in a fixed order.
 constexpr int DX_T = 16;
+__device__ __forceinline__ void add_bf16x4(float* v, uint2 p) {
+  v[0] += __uint_as_float(p.x << 16);
+  v[1] += __uint_as_float(p.x & 0xffff0000u);
+  v[2] += __uint_as_float(p.y << 16);
+  v[3] += __uint_as_float(p.y & 0xffff0000u);
+}
 __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
   __shared__ float sdl[DX_T][MAX_EXPERTS];
   const int t0 = blockIdx.x * DX_T;
-  const int j = blockIdx.y * 256 + threadIdx.x;
+  const int j = (blockIdx.y * 256 + threadIdx.x) * 4;
   const int nt = min(DX_T, a.T - t0);
   for (int i = threadIdx.x; i < DX_T * a.E; i += 256) {
     const int tt = i / a.E, e = i % a.E;
     sdl[tt][e] = (tt < nt) ? a.dl[(size_t)(t0 + tt) * a.E + e] : 0.f;
   }
   __syncthreads();
-  if (j >= a.d) return;
-  float r[DX_T];
+  if (j >= a.d) return;   // d is a multiple of 4
+  float r[DX_T][4];
 #pragma unroll
-  for (int tt = 0; tt < DX_T; ++tt) r[tt] = 0.f;
+  for (int tt = 0; tt < DX_T; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[tt][q] = 0.f;
   for (int e = 0; e < a.E; ++e) {
-    const float w = a.w_gate[(size_t)e * a.d + j];
+    const float4 w = *reinterpret_cast<const float4*>(a.w_gate + (size_t)e * a.d + j);
 #pragma unroll
-    for (int tt = 0; tt < DX_T; ++tt) r[tt] = fmaf(sdl[tt][e], w, r[tt]);
+    for (int tt = 0; tt < DX_T; ++tt) {
+      const float l = sdl[tt][e];
+      r[tt][0] = fmaf(l, w.x, r[tt][0]);
+      r[tt][1] = fmaf(l, w.y, r[tt][1]);
+      r[tt][2] = fmaf(l, w.z, r[tt][2]);
+      r[tt][3] = fmaf(l, w.w, r[tt][3]);
+    }
   }
+  // four tokens at a time, their rows' loads issued together
 #pragma unroll
   for (int t4 = 0; t4 < DX_T; t4 += 4) {
-    float v[4];
+    float v[4][4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int t = t0 + t4 + q;
-      v[q] = 0.f;
-      if (t4 + q >= nt) continue;
-      v[q] = bf16_to_f32(a.dy[(size_t)t * a.d + j]);
-      if (a.dx_shared) v[q] += a.dx_shared[(size_t)t * a.d + j];
+      const int tt = t4 + q;
+      const size_t t = (size_t)(t0 + min(tt, nt - 1));
+      v[q][0] = v[q][1] = v[q][2] = v[q][3] = 0.f;
+      add_bf16x4(v[q], *reinterpret_cast<const uint2*>(a.dy + t * a.d + j));
+      if (a.dx_shared)
+        add_bf16x4(v[q], *reinterpret_cast<const uint2*>(a.dx_shared + t * a.d + j));
     }
     for (int k = 0; k < a.K; ++k) {
-      float w[4];
+      uint2 p[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int t = t0 + t4 + q;
-        w[q] = (t4 + q < nt)
-                   ? a.dx_rows[(size_t)a.slot_row[(size_t)t * a.K + k] * a.d + j] : 0.f;
+        const size_t t = (size_t)(t0 + min(t4 + q, nt - 1));
+        const size_t row = (size_t)a.slot_row[t * a.K + k];
+        p[q] = *reinterpret_cast<const uint2*>(a.dx_rows + row * a.d + j);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] += w[q];
+      for (int q = 0; q < 4; ++q) add_bf16x4(v[q], p[q]);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int t = t0 + t4 + q;
-      if (t4 + q < nt) a.dx[(size_t)t * a.d + j] = f32_to_bf16(v[q] + r[t4 + q]);
+      const int tt = t4 + q;
+      if (tt >= nt) continue;
+      uint2 o;
+      o.x = (uint32_t)f32_to_bf16(v[q][0] + r[tt][0]) |
+            ((uint32_t)f32_to_bf16(v[q][1] + r[tt][1]) << 16);
+      o.y = (uint32_t)f32_to_bf16(v[q][2] + r[tt][2]) |
+            ((uint32_t)f32_to_bf16(v[q][3] + r[tt][3]) << 16);
+      *reinterpret_cast<uint2*>(a.dx + (size_t)(t0 + tt) * a.d + j) = o;
     }
   }
 }
@@ -292,7 +314,7 @@ hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s) {
 
 hipError_t launch_dx_combine(const BwdAuxArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid((a.T + DX_T - 1) / DX_T, (a.d + 255) / 256);
+  const dim3 grid((a.T + DX_T - 1) / DX_T, (a.d + 1023) / 1024);
   hipLaunchKernelGGL(dx_combine_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -176,7 +176,7 @@ struct BwdGemmArgs {
   const bf16_t* da; int ldda;       // [rows][2 inner] (shared: per expert blocks)
   const bf16_t* hg; int ldhg;       // [rows][inner] g h (shared: per expert blocks)
   const bf16_t* zero;               // >= 512 zero bytes (k rows past the end)
-  float* c; int ldc;                // KIND 0: G [rows][ldc]; KIND 1: dX [rows][d]
+  float* c; bf16_t* cx; int ldc;    // KIND 0: G [rows][ldc] (fp32); KIND 1: dX [rows][d] (bf16)
   float* dw1; float* dw3; float* dw2;   // KIND 2/3 outputs [experts][..][..]
   int splits;                       // KIND 2/3: k split into this many ranges (>= 1)
   float* part;                      // splits > 1: [splits][experts][M][N] partial sums
@@ -199,8 +199,8 @@ struct BwdAuxArgs {
   const bf16_t* x; const bf16_t* dy;
   float* dwg_part; int n_chunk;     // [n_chunk][E][d] partial gate gradients
   float* dw_gate;                   // [E][d]
-  const float* dx_rows;             // [T K][d]
-  const float* dx_shared;           // [T][d] or NULL
+  const bf16_t* dx_rows;            // [T K][d]
+  const bf16_t* dx_shared;          // [T][d] or NULL
   bf16_t* dx;                       // [T][d]
   bf16_t* zero; int n_zero;         // zero-filled at the start
 };

@@ -32,6 +32,7 @@ constexpr int TK = 32;      // k per stage
 constexpr int NS = 4;       // stages in the LDS ring: NS - 1 in flight while one is computed
 
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float fv4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 // Chunk swizzle of mn-major LDS rows (32 chunks of 16 B per k-row).  Half a
@@ -362,14 +363,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
   // holds one row, so direct stores would write 32 bytes into each of 32
   // rows per instruction.  Each 32 x 64 half block (one mb, two nb) goes
   // through the wave's own LDS buffer instead (rows padded to 68 floats) and
-  // leaves as four whole 256-byte row segments per store instruction.  The
-  // buffers are free once every wave has passed the barrier (each wave's
-  // direct loads have completed above); a wave's LDS operations run in
-  // order, so the buffers need no further barrier. ----
+  // leaves in whole row segments: the rows' input gradients (KIND 1) rounded
+  // to bf16, 8 columns per lane; G and the weight gradients in fp32, 4
+  // columns per lane.  The buffers are free once every wave has passed the
+  // barrier (each wave's direct loads have completed above); a wave's LDS
+  // operations run in order, so the buffers need no further barrier. ----
   __syncthreads();
   constexpr int SP = 68;
   float* stg = reinterpret_cast<float*>(wave == 0 ? A0 : wave == 1 ? A1 : wave == 2 ? A2 : A3);
-  const int rq = lane >> 4, cq = (lane & 15) * 4;   // read-back: row rq + 4 i, columns cq..+3
+  // read-back position: KIND 1 row rq + 8 i, columns cq..cq+7 of the half;
+  // the others row rq + 4 i, columns cq..cq+3
+  constexpr int CPL = (KIND == 1) ? 8 : 4, LPR = 64 / CPL, RPI = 64 / LPR;
+  const int rq = lane / LPR, cq = (lane % LPR) * CPL;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -388,26 +393,33 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
         }
       const int n = t.n0 + wn * 128 + h * 64 + cq;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int rr = rq + 4 * i;
-        const float4 v = *reinterpret_cast<const float4*>(stg + rr * SP + cq);
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int rr = rq + RPI * i;
         const int m = t.m0 + wm * 128 + mb * 32 + rr;
-        if (m >= t.mval || n >= t.nval) continue;
-        float* crow;
-        if (KIND == 0) {
-          const size_t col = SH ? (size_t)t.grp * a.inner : 0;
-          crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
-        } else if (KIND == 1) {
-          crow = a.c + (size_t)(t.row0 + m) * a.ldc;
-        } else if (a.splits > 1) {   // partial sums [split][group][M][N], reduced later
-          crow = a.part + (((size_t)t.split * a.n_experts + t.grp) * t.mval + m) * t.nval;
-        } else if (KIND == 2) {
-          crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
+        const float4 v = *reinterpret_cast<const float4*>(stg + rr * SP + cq);
+        if constexpr (KIND == 1) {
+          const float4 w = *reinterpret_cast<const float4*>(stg + rr * SP + cq + 4);
+          if (m >= t.mval || n >= t.nval) continue;
+          bf16_t* crow = a.cx + (size_t)(t.row0 + m) * a.ldc;
+          const u32x4 p = {pack2(v.x, v.y), pack2(v.z, v.w), pack2(w.x, w.y), pack2(w.z, w.w)};
+          *reinterpret_cast<u32x4*>(crow + n) = p;
         } else {
-          crow = (m < a.inner) ? a.dw1 + ((size_t)t.grp * a.inner + m) * a.d
-                               : a.dw3 + ((size_t)t.grp * a.inner + (m - a.inner)) * a.d;
+          if (m >= t.mval || n >= t.nval) continue;
+          float* crow;
+          if (KIND == 0) {
+            const size_t col = SH ? (size_t)t.grp * a.inner : 0;
+            crow = a.c + (size_t)(t.row0 + m) * a.ldc + col;
+          } else if (a.splits > 1) {   // partial sums [split][group][M][N], reduced later
+            crow = a.part + (((size_t)t.split * a.n_experts + t.grp) * t.mval + m) * t.nval;
+          } else if (KIND == 2) {
+            crow = a.dw2 + ((size_t)t.grp * a.d + m) * a.inner;
+          } else {
+            crow = (m < a.inner) ? a.dw1 + ((size_t)t.grp * a.inner + m) * a.d
+                                 : a.dw3 + ((size_t)t.grp * a.inner + (m - a.inner)) * a.d;
+          }
+          // non-temporal: not read again by this kernel
+          __builtin_nontemporal_store(fv4{v.x, v.y, v.z, v.w}, reinterpret_cast<fv4*>(crow + n));
         }
-        *reinterpret_cast<float4*>(crow + n) = v;
       }
     }
   }

@@ -448,8 +448,8 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   B.g_s = d.n_shared > 0 ? take((int64_t)d.T * ksi * 4) : -1;
   B.da_r = take(TK * 2 * d.inner * 2);
   B.da_s = d.n_shared > 0 ? take((int64_t)d.T * 2 * ksi * 2) : -1;
-  B.dx_rows = take(TK * d.d * 4);
-  B.dx_s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
+  B.dx_rows = take(TK * d.d * 2);
+  B.dx_s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 2) : -1;
   B.row_g = take(TK * 4);
   B.dg_part = take(TK * B.n_part * 4);
   B.dg = take(TK * 4);
@@ -550,8 +550,8 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   aux.x = xb; aux.dy = dyb;
   aux.dwg_part = static_cast<float*>(at(B.dwg_part)); aux.n_chunk = B.n_chunk;
   aux.dw_gate = dw_gate;
-  aux.dx_rows = static_cast<const float*>(at(B.dx_rows));
-  aux.dx_shared = static_cast<const float*>(at(B.dx_s));
+  aux.dx_rows = static_cast<const bf16_t*>(at(B.dx_rows));
+  aux.dx_shared = static_cast<const bf16_t*>(at(B.dx_s));
   aux.dx = static_cast<bf16_t*>(dx);
   aux.zero = static_cast<bf16_t*>(at(B.zero)); aux.n_zero = 512;
   MOE_CHECK(launch_bwd_prep(aux, s));
@@ -609,7 +609,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   };
   auto shared_dx = [&](hipStream_t st_) {
     BwdGemmArgs g = sb;
-    g.kind = 1; g.c = static_cast<float*>(at(B.dx_s)); g.ldc = d.d;
+    g.kind = 1; g.cx = static_cast<bf16_t*>(at(B.dx_s)); g.ldc = d.d;
     return launch_gemm_bwd(g, st_);
   };
   auto shared_dw = [&](int kind, hipStream_t st_) {
@@ -674,7 +674,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   {
     if (!mark(6)) return MOE_ERR_HIP;
     BwdGemmArgs g = rb;
-    g.kind = 1; g.c = static_cast<float*>(at(B.dx_rows)); g.ldc = d.d;
+    g.kind = 1; g.cx = static_cast<bf16_t*>(at(B.dx_rows)); g.ldc = d.d;
     MOE_CHECK(launch_gemm_bwd(g, s));
     if (!mark(7)) return MOE_ERR_HIP;
     if (in_order) MOE_CHECK(shared_dx(s));

@@ -7,9 +7,12 @@ layer's bound, which covers dx's own rounding at the output) plus, for the
 results of products that take an operand rounded to bf16 -- the SwiGLU input
 gradients dA (dW1, dW3 and dx's expert part) and g h (dW2) -- 2^-7 times the
 sum of the absolute values of that product's terms (the oracle reports these
-sums): bf16 keeps 8 significant bits, so rounding one factor of every term
-moves the result by at most 2^-8 of that sum, and 2^-7 leaves room for the
-fp32 accumulation and the recomputed pre-activations.  The expert choice must
+sums).  bf16 keeps 8 significant bits (relative rounding error <= 2^-9): dA
+is rounded once, and each routed row's share of dx (and the shared experts'
+share) once more before the shares are summed, so every term of dx moves by at
+most about 2^-8 of its size and every term of a weight gradient by 2^-9;
+2^-7 leaves room for the fp32 accumulation and the recomputed
+pre-activations.  The expert choice must
 equal the oracle's on every token whose selection margin exceeds 1e-5 and
 equal the forward's on every token.
 
