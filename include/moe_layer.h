@@ -39,7 +39,10 @@
  *    and the shared experts', one grouped down-projection launch (routed
  *    rows and the shared experts' sum), and the combine.
  *  - Validation errors are returned before anything is enqueued.  A failed
- *    kernel launch returns MOE_ERR_HIP.
+ *    kernel launch returns MOE_ERR_HIP.  An error left pending in the calling
+ *    thread's HIP error state by an earlier, unrelated HIP call is cleared at
+ *    entry (it is not this call's failure); a device fault stays sticky and
+ *    fails the call.
  *  - Results are bitwise reproducible for identical inputs and shapes (no
  *    floating-point atomics; the expert-contiguous order is stable).
  */

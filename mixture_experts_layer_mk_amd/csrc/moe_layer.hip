@@ -34,6 +34,13 @@ const char* const kBwdStageNames[kBwdStages] = {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Every launch is checked with hipGetLastError, which also returns an error
+// left pending on the calling thread by any earlier HIP call (another
+// library's failed probe, a query that returned not-ready).  Entry points that
+// launch work clear that state first, so that a status reports this call's
+// own work only.  A device fault is sticky and still fails the next call.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 // Bytes per element of x / out (bf16 for bf16 and FP8 layers) and of the
 // SwiGLU activations H (one E4M3 byte for FP8 layers).
 int elem_size(const moe_layer_desc_t& d) { return d.dtype == MOE_F32 ? 4 : 2; }
@@ -90,7 +97,7 @@ struct SideStreamCache {
 // The side stream of the caller's stream's device (the null stream: the
 // current device); created with that device current.  nullptr on any
 // failure, and the call then runs every stage in order on `s`.
-SideStream* side_stream(hipStream_t s) {
+SideStream* side_stream_or_null(hipStream_t s) {
   thread_local SideStreamCache cache;
   int dev = 0;
   if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
@@ -111,6 +118,14 @@ SideStream* side_stream(hipStream_t s) {
   if (cur != dev) (void)hipSetDevice(cur);
   if (!ok) return nullptr;
   return &cache.by_device.emplace(dev, ss).first->second;
+}
+
+// The same; a failure also clears the error it left pending, since the call
+// then goes on in order and checks its launches.
+SideStream* side_stream(hipStream_t s) {
+  SideStream* r = side_stream_or_null(s);
+  if (!r) clear_pending_error();
+  return r;
 }
 
 moe_status_t validate(const moe_layer_desc_t* d) {
@@ -286,6 +301,7 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
                           int32_t* expert_counts, void* workspace,
                           size_t workspace_bytes, void* stream_ptr,
                           void* const* events) {
+  clear_pending_error();
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_layer_desc_t& d = *desc;
@@ -479,6 +495,7 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
                            moe_ffn_grads_t d_routed, moe_ffn_grads_t d_shared,
                            int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                            void* stream_ptr, void* const* events) {
+  clear_pending_error();
   moe_status_t st = validate(desc);
   if (st != MOE_OK) return st;
   const moe_layer_desc_t& d = *desc;
@@ -878,6 +895,7 @@ moe_status_t moe_quantize_fp8_blocks(const void* src, int32_t src_dtype, int64_t
   if (batch == 0 || rows == 0 || cols == 0) return MOE_OK;
   if (!src || !codes || !scales) return MOE_ERR_INVALID_ARG;
   if ((int64_t)rows * cols >= (int64_t(1) << 40) / batch) return MOE_ERR_UNSUPPORTED;
+  clear_pending_error();
   QuantArgs q{};
   q.src = src; q.src_f32 = src_dtype == MOE_F32; q.batch = batch; q.rows = rows; q.cols = cols;
   q.codes = codes; q.scales = scales;
@@ -889,6 +907,7 @@ moe_status_t moe_bias_update(const int32_t* counts, int32_t n_routed, float gamm
                              float* select_bias, float* rel_load, void* stream) {
   if (!counts || n_routed < 1 || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
   if (n_routed > MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  clear_pending_error();
   BiasUpdateArgs a{};
   a.counts = counts; a.n = n_routed; a.gamma = gamma;
   a.bias = select_bias; a.rel_load = rel_load;

@@ -256,3 +256,29 @@ def test_routed_scale():
     cfg = C["deepseekmoe-16b"].replace(T=400, d=256, inner=128, shared_inner=128,
                                        routed_scale=2.5)
     check_case(Case(cfg))
+
+
+def test_pending_hip_error_is_not_this_calls_failure():
+    """An error left pending in the thread's HIP error state by an earlier,
+    unrelated runtime call (here hipSetDevice on a device that does not exist,
+    which fails without touching the GPU) must not make the next forward or
+    backward report a failed launch; the results equal a clean call's."""
+    import ctypes
+    import mixture_experts_layer_mk_amd as moe
+    hip = ctypes.CDLL("libamdhip64.so")
+    cfg = C["deepseekmoe-16b"].replace(T=300, d=256, inner=128, shared_inner=128, seed=7)
+    case = Case(cfg)
+    d = case.dev
+    ref = moe.moe_layer_forward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k)
+    dout = torch.ones_like(d["x"])
+    gref = moe.moe_layer_backward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k,
+                                  dout)
+    torch.cuda.synchronize()
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0      # leaves an error pending
+    out = moe.moe_layer_forward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k)
+    assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+    g = moe.moe_layer_backward(d["x"], d["w_gate"], d["routed"], d["shared"], cfg.top_k, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(g["dx"], gref["dx"])
+    assert torch.equal(g["routed"][0], gref["routed"][0])
