@@ -451,14 +451,19 @@ __device__ __forceinline__ void gemm_part(const GemmArgs& a, int blk, int nblk, 
                                           u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
                                           u32x4* Bs2, float* red) {
   const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
-  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int L = xcd_remap(blk, nblk);
+  // Routed launches are sized for the most M-tiles any routing can make; the
+  // tiles are numbered over the M-tiles the routing did make, so the blocks
+  // past them (which exit at once) are the last ones and every XCD gets an
+  // equal share of real tiles.
+  const int mdim = routed ? *a.n_tiles : (a.T + BM - 1) / BM;
   // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
   // one M-tile are adjacent, then the next M-tile (same expert, same weight
   // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
   // both its token-row tiles and its weight tiles in L2.
   const int ndim = n_tiles_of<MODE, BM>(a);
-  if (L >= mdim * ndim) return;              // padding of a launch's first part
+  const int ntl = mdim * ndim;
+  const int L = !routed ? xcd_remap(blk, nblk) : (blk < ntl ? xcd_remap(blk, ntl) : ntl);
+  if (L >= ntl) return;                      // padding
   int mt, nt;
   constexpr int NGRP = ngrp_for<BM>();
   {
@@ -470,7 +475,6 @@ __device__ __forceinline__ void gemm_part(const GemmArgs& a, int blk, int nblk, 
     nt = ntg * NGRP + rem % g;
   }
   if (routed) {
-    if (mt >= *a.n_tiles) return;
     const MTile t = a.tiles[mt];
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {

@@ -79,13 +79,17 @@ struct TileDesc {
 
 template <int KIND, bool SH>
 __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
   if (KIND == 0 || KIND == 1) {
     const int per = (KIND == 0) ? (a.inner + BN - 1) / BN : (a.d + BN - 1) / BN;
     const int ndim = (KIND == 0 && SH) ? per * a.n_experts : per;
+    // Routed launches are sized for the most M-tiles any routing can make;
+    // tiles are numbered over the ones it did make (the blocks past them
+    // exit), so every XCD gets an equal share of real tiles.
+    const int nreal = SH ? (int)gridDim.x : *a.n_tiles * ndim;
+    if ((int)blockIdx.x >= nreal) return false;
+    const int L = xcd_remap(blockIdx.x, nreal);
     const int mt = L / ndim, nt = L % ndim;
     if (!SH) {
-      if (mt >= *a.n_tiles) return false;
       const MTile m = a.tiles[mt];
       t.row0 = m.row0; t.mval = m.rows; t.grp = m.expert;
     } else {
@@ -97,6 +101,7 @@ __device__ __forceinline__ bool decode(const BwdGemmArgs& a, TileDesc& t) {
     t.K = (KIND == 0) ? a.d : (SH ? 2 * a.inner * a.n_experts : 2 * a.inner);
     t.koff = 0; t.kbeg = 0; t.split = 0;
   } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
     const int M = (KIND == 2) ? a.d : 2 * a.inner;
     const int N = (KIND == 2) ? a.inner : a.d;
     const int mdim = (M + TM - 1) / TM, ndim = (N + BN - 1) / BN;

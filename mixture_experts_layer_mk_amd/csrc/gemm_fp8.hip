@@ -424,10 +424,13 @@ __device__ __forceinline__ void gemm8_part(const GemmArgs& a, int blk, int nblk,
                                            u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
                                            u32x4* Bs2, uint8_t* sA, uint8_t* sB, float* gmax) {
   const bool routed = !(MODE == 2 || (MODE == 0 && a.shared));
-  const int mdim = routed ? a.max_mtiles : (a.T + BM - 1) / BM;
-  const int L = xcd_remap(blk, nblk);
+  // Tiles numbered over the M-tiles the routing made (blocks past them exit),
+  // so every XCD gets an equal share of real tiles.
+  const int mdim = routed ? *a.n_tiles : (a.T + BM - 1) / BM;
   const int ndim = n_tiles_of<MODE, BM>(a);
-  if (L >= mdim * ndim) return;              // padding of a launch's first part
+  const int ntl = mdim * ndim;
+  const int L = !routed ? xcd_remap(blk, nblk) : (blk < ntl ? xcd_remap(blk, ntl) : ntl);
+  if (L >= ntl) return;                      // padding
   int mt, nt;
   constexpr int NGRP = ngrp_for<BM>();
   {
@@ -439,7 +442,6 @@ __device__ __forceinline__ void gemm8_part(const GemmArgs& a, int blk, int nblk,
     nt = ntg * NGRP + rem % g;
   }
   if (routed) {
-    if (mt >= *a.n_tiles) return;
     const MTile t = a.tiles[mt];
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
