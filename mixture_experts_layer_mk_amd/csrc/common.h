@@ -90,7 +90,8 @@ struct SelectArgs {
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 // Partial logits only (bf16 x: the gate planes must already be split).
 hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
-int router_tokens_per_block(int T);   // tokens per histogram block
+// Tokens per histogram block (dtype: 0 = f32, 1 = bf16 x).
+int router_tokens_per_block(int T, int E, int d, int dtype);
 int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 // True when logits and selection run fused (no partial-logit buffer).
 bool router_fused(int T, int E, int K, int n_groups, int dtype);

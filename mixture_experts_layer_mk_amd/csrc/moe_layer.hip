@@ -168,7 +168,7 @@ Layout layout_of(const moe_layer_desc_t& d) {
   };
   const int64_t esz = elem_size(d);
   const int64_t TK = (int64_t)d.T * d.top_k;
-  const int rt = router_tokens_per_block(d.T);
+  const int rt = router_tokens_per_block(d.T, d.n_routed, d.d, d.dtype != MOE_F32 ? 1 : 0);
   L.nblk = (d.T + rt - 1) / rt;
   L.bm = choose_bm(d);
   L.max_mtiles = (int32_t)((TK + (int64_t)d.n_routed * (L.bm - 1)) / L.bm);
@@ -280,7 +280,8 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
   if (!mark(2)) return MOE_ERR_HIP;
   {
     PermuteArgs p{};
-    p.T = d.T; p.K = d.top_k; p.E = d.n_routed; p.rt = router_tokens_per_block(d.T);
+    p.T = d.T; p.K = d.top_k; p.E = d.n_routed;
+    p.rt = router_tokens_per_block(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
     p.nblk = L.nblk;
     p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
     p.block_base = static_cast<const int32_t*>(at(L.block_base));

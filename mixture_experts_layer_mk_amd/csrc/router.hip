@@ -199,6 +199,174 @@ __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
 //  e. block histogram and in-block ranks: every kept (token, expert) ORs the
 //     token's bit into the expert's 64-bit LDS mask (order-free, so
 //     deterministic); counts and ranks are popcounts.
+// Selection of one histogram block from its logits in LDS (lg, row stride
+// ld): steps a-e above.  The first 8 TBK threads take the block's (at most
+// TBK) tokens, eight lanes each, over at most EMAX experts; every thread of
+// the workgroup reaches the barrier.  masks (per expert) start at zero;
+// sbias holds the selection bias (or zeros); gsc has TBK rows.
+template <int KMAX, int EMAX, int TBK>
+__device__ __forceinline__ void select_block(const SelectArgs& a, const float* lg, int ld,
+                                             int t0, int ntok,
+                                             unsigned long long* masks,
+                                             float (*gsc)[MAX_GROUPS + 1],
+                                             const float* sbias) {
+  const int tid = threadIdx.x;
+  const int E = a.E, K = a.K;
+  const bool act = tid < TBK * 8;             // whole waves: TBK * 8 is a multiple of 64
+  const int j = tid & 7;                      // lane of the token's eight
+  const int tl = tid >> 3;                    // token in the block
+  const int t = t0 + tl;
+  const bool live = tl < ntok;
+  float ts[KMAX];                             // kept scores and experts, in order
+  int ti[KMAX];
+  if (act) {
+    const float* my = lg + (live ? tl : 0) * ld;   // dead tokens shadow row 0
+    constexpr int CM = EMAX / 8;                // experts per lane, at most
+    const int C = (E + 7) / 8;
+    const int e0 = min(E, j * C), e1 = min(E, e0 + C);
+    auto xor8 = [](float v, int m) { return __shfl_xor(v, m, 8); };
+
+    // a. scores and keys of the lane's experts, in registers
+    float sv[CM], kv[CM];
+#pragma unroll
+    for (int i = 0; i < CM; ++i) sv[i] = (e0 + i < e1) ? my[e0 + i] : 0.f;
+    if (a.score == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < CM; ++i)
+        if (e0 + i < e1) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, xor8(mx, 1));
+      mx = fmaxf(mx, xor8(mx, 2));
+      mx = fmaxf(mx, xor8(mx, 4));
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < CM; ++i)
+        if (e0 + i < e1) {
+          sv[i] = expf(sv[i] - mx);
+          z += sv[i];
+        }
+      z += xor8(z, 1);
+      z += xor8(z, 2);
+      z += xor8(z, 4);
+#pragma unroll
+      for (int i = 0; i < CM; ++i) sv[i] = sv[i] / z;
+    } else {
+#pragma unroll
+      for (int i = 0; i < CM; ++i) sv[i] = 1.f / (1.f + expf(-sv[i]));
+    }
+#pragma unroll
+    for (int i = 0; i < CM; ++i) {
+      const float k = sv[i] + ((e0 + i < e1) ? sbias[e0 + i] : 0.f);
+      kv[i] = (k != k) ? -INFINITY : k;     // NaN never outranks a score
+    }
+
+    // b. group limit: bitmask of the kept groups, then the lane's kept experts
+    uint64_t keep = ~0ull;
+    int gsz = E;
+    uint32_t avail = 0;                         // bit i: expert e0 + i may be kept
+    if (a.n_groups > 1) {
+      gsz = E / a.n_groups;
+      const int g_lo = e0 / gsz, g_hi = (e1 > e0) ? (e1 - 1) / gsz : g_lo - 1;
+      for (int g = 0; g < a.n_groups; ++g) {
+        float b1 = -INFINITY, b2 = -INFINITY;
+        if (g >= g_lo && g <= g_hi) {
+          const int lo = g * gsz - e0, hi_i = (g + 1) * gsz - e0;
+#pragma unroll
+          for (int i = 0; i < CM; ++i) {
+            if (i < lo || i >= hi_i || e0 + i >= e1) continue;
+            const float k = kv[i];
+            if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {   // top two of both lanes' top two
+          const float c1 = xor8(b1, m), c2 = xor8(b2, m);
+          const float n2 = fmaxf(fminf(b1, c1), fmaxf(b2, c2));
+          b1 = fmaxf(b1, c1);
+          b2 = n2;
+        }
+        if (j == 0) gsc[tl][g] = (gsz > 1) ? b1 + b2 : b1;
+      }
+      __builtin_amdgcn_wave_barrier();
+      keep = 0;
+      for (int r = 0; r < a.topk_groups; ++r) {
+        float bk = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int g = 0; g < a.n_groups; ++g) {
+          if ((keep >> g) & 1) continue;
+          const float v = gsc[tl][g];
+          if (better(v, g, bk, bi)) { bk = v; bi = g; }
+        }
+        keep |= 1ull << bi;
+      }
+      for (int g = g_lo; g <= g_hi; ++g) {
+        if (!((keep >> g) & 1)) continue;
+        const int lo = max(0, g * gsz - e0), hi_i = min(e1 - e0, (g + 1) * gsz - e0);
+        avail |= (uint32_t)((hi_i >= 32 ? ~0ull : ((1ull << hi_i) - 1)) & ~((1ull << lo) - 1));
+      }
+    } else {
+      const int n = e1 - e0;
+      avail = (n >= 32) ? ~0u : ((1u << n) - 1);
+    }
+
+    // c. top-K: K rounds of the best available expert over the eight lanes
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      ts[r] = 0.f;
+      ti[r] = 0x7fffffff;
+      if (r >= K) continue;
+      // the lane's best: increasing index, so a tie keeps the lower index
+      float bk = -INFINITY, bs = 0.f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < CM; ++i) {
+        if (!((avail >> i) & 1)) continue;
+        if (bi == 0x7fffffff || kv[i] > bk) { bk = kv[i]; bs = sv[i]; bi = e0 + i; }
+      }
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        const float ok = xor8(bk, m), os = xor8(bs, m);
+        const int oi = __shfl_xor(bi, m, 8);
+        if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bs = os; }
+      }
+      ts[r] = bs;
+      ti[r] = bi;
+      if (bi >= e0 && bi < e1) avail &= ~(1u << (bi - e0));
+    }
+
+    // d. gate weights; lane j writes the slots r = j mod 8
+    float gsum = 0.f;
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r)
+      if (r < K) gsum += ts[r];
+    if (live) {
+#pragma unroll
+      for (int r = 0; r < KMAX; ++r) {
+        if (r >= K || (r & 7) != j) continue;
+        float g = ts[r];
+        if (a.norm_topk) g = g / gsum;
+        g *= a.routed_scale;
+        a.topk_idx[(size_t)t * K + r] = ti[r];
+        a.topk_w[(size_t)t * K + r] = g;
+        atomicOr(&masks[ti[r]], 1ull << tl);
+      }
+    }
+  }
+  __syncthreads();
+
+  // e. block histogram and in-block ranks (token order)
+  for (int e = tid; e < E; e += (int)blockDim.x)   // layout [blocks][E]
+    a.block_counts[(size_t)blockIdx.x * E + e] = __popcll(masks[e]);
+  if (act && live) {
+    const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
+#pragma unroll
+    for (int r = 0; r < KMAX; ++r) {
+      if (r >= K || (r & 7) != j) continue;
+      a.rank[(size_t)t * K + r] = __popcll(masks[ti[r]] & below);
+    }
+  }
+}
+
 template <int KMAX>
 __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
   extern __shared__ float lg[];               // [64][E + 1]: logits, then scores
@@ -237,159 +405,8 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-
-  const int j = tid & 7;                      // lane of the token's eight
-  const int tl = tid >> 3;                    // token in the block
-  const int t = t0 + tl;
-  const bool live = tl < ntok;
-  const float* my = lg + (live ? tl : 0) * ld;   // dead tokens shadow row 0
-  constexpr int CM = MAX_EXPERTS / 8;         // experts per lane, at most
-  const int C = (E + 7) / 8;
-  const int e0 = min(E, j * C), e1 = min(E, e0 + C);
-  auto xor8 = [](float v, int m) { return __shfl_xor(v, m, 8); };
-
-  // a. scores and keys of the lane's experts, in registers
-  float sv[CM], kv[CM];
-#pragma unroll
-  for (int i = 0; i < CM; ++i) sv[i] = (e0 + i < e1) ? my[e0 + i] : 0.f;
-  if (a.score == 0) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < CM; ++i)
-      if (e0 + i < e1) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, xor8(mx, 1));
-    mx = fmaxf(mx, xor8(mx, 2));
-    mx = fmaxf(mx, xor8(mx, 4));
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < CM; ++i)
-      if (e0 + i < e1) {
-        sv[i] = expf(sv[i] - mx);
-        z += sv[i];
-      }
-    z += xor8(z, 1);
-    z += xor8(z, 2);
-    z += xor8(z, 4);
-#pragma unroll
-    for (int i = 0; i < CM; ++i) sv[i] = sv[i] / z;
-  } else {
-#pragma unroll
-    for (int i = 0; i < CM; ++i) sv[i] = 1.f / (1.f + expf(-sv[i]));
-  }
-#pragma unroll
-  for (int i = 0; i < CM; ++i) {
-    const float k = sv[i] + ((e0 + i < e1) ? sbias[e0 + i] : 0.f);
-    kv[i] = (k != k) ? -INFINITY : k;     // NaN never outranks a score
-  }
-
-  // b. group limit: bitmask of the kept groups, then the lane's kept experts
-  uint64_t keep = ~0ull;
-  int gsz = E;
-  uint32_t avail = 0;                         // bit i: expert e0 + i may be kept
-  if (a.n_groups > 1) {
-    gsz = E / a.n_groups;
-    const int g_lo = e0 / gsz, g_hi = (e1 > e0) ? (e1 - 1) / gsz : g_lo - 1;
-    for (int g = 0; g < a.n_groups; ++g) {
-      float b1 = -INFINITY, b2 = -INFINITY;
-      if (g >= g_lo && g <= g_hi) {
-        const int lo = g * gsz - e0, hi_i = (g + 1) * gsz - e0;
-#pragma unroll
-        for (int i = 0; i < CM; ++i) {
-          if (i < lo || i >= hi_i || e0 + i >= e1) continue;
-          const float k = kv[i];
-          if (k > b1) { b2 = b1; b1 = k; } else if (k > b2) { b2 = k; }
-        }
-      }
-#pragma unroll
-      for (int m = 1; m < 8; m <<= 1) {   // top two of both lanes' top two
-        const float c1 = xor8(b1, m), c2 = xor8(b2, m);
-        const float n2 = fmaxf(fminf(b1, c1), fmaxf(b2, c2));
-        b1 = fmaxf(b1, c1);
-        b2 = n2;
-      }
-      if (j == 0) gsc[tl][g] = (gsz > 1) ? b1 + b2 : b1;
-    }
-    __builtin_amdgcn_wave_barrier();
-    keep = 0;
-    for (int r = 0; r < a.topk_groups; ++r) {
-      float bk = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int g = 0; g < a.n_groups; ++g) {
-        if ((keep >> g) & 1) continue;
-        const float v = gsc[tl][g];
-        if (better(v, g, bk, bi)) { bk = v; bi = g; }
-      }
-      keep |= 1ull << bi;
-    }
-    for (int g = g_lo; g <= g_hi; ++g) {
-      if (!((keep >> g) & 1)) continue;
-      const int lo = max(0, g * gsz - e0), hi_i = min(e1 - e0, (g + 1) * gsz - e0);
-      avail |= (uint32_t)((hi_i >= 32 ? ~0ull : ((1ull << hi_i) - 1)) & ~((1ull << lo) - 1));
-    }
-  } else {
-    const int n = e1 - e0;
-    avail = (n >= 32) ? ~0u : ((1u << n) - 1);
-  }
-
-  // c. top-K: K rounds of the best available expert over the eight lanes
-  float ts[KMAX];
-  int ti[KMAX];
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    ts[r] = 0.f;
-    ti[r] = 0x7fffffff;
-    if (r >= K) continue;
-    // the lane's best: increasing index, so a tie keeps the lower index
-    float bk = -INFINITY, bs = 0.f;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < CM; ++i) {
-      if (!((avail >> i) & 1)) continue;
-      if (bi == 0x7fffffff || kv[i] > bk) { bk = kv[i]; bs = sv[i]; bi = e0 + i; }
-    }
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) {
-      const float ok = xor8(bk, m), os = xor8(bs, m);
-      const int oi = __shfl_xor(bi, m, 8);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; bs = os; }
-    }
-    ts[r] = bs;
-    ti[r] = bi;
-    if (bi >= e0 && bi < e1) avail &= ~(1u << (bi - e0));
-  }
-
-  // d. gate weights; lane j writes the slots r = j mod 8
-  float gsum = 0.f;
-#pragma unroll
-  for (int r = 0; r < KMAX; ++r)
-    if (r < K) gsum += ts[r];
-  if (live) {
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      if (r >= K || (r & 7) != j) continue;
-      float g = ts[r];
-      if (a.norm_topk) g = g / gsum;
-      g *= a.routed_scale;
-      a.topk_idx[(size_t)t * K + r] = ti[r];
-      a.topk_w[(size_t)t * K + r] = g;
-      atomicOr(&masks[ti[r]], 1ull << tl);
-    }
-  }
-  __syncthreads();
-
-  // e. block histogram and in-block ranks (token order)
-  for (int e = tid; e < E; e += 512)   // layout [blocks][E]
-    a.block_counts[(size_t)blockIdx.x * E + e] = __popcll(masks[e]);
-  if (live) {
-    const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
-#pragma unroll
-    for (int r = 0; r < KMAX; ++r) {
-      if (r >= K || (r & 7) != j) continue;
-      a.rank[(size_t)t * K + r] = __popcll(masks[ti[r]] & below);
-    }
-  }
+  select_block<KMAX, MAX_EXPERTS, 64>(a, lg, ld, t0, ntok, masks, gsc, sbias);
 }
-
 
 // ---------------------------------------------------------------------------
 // 4. fused logits + selection (bf16 x, at most 64 experts, K <= 8, no
@@ -516,9 +533,12 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
       issue_w(wf, kc + FR_NSW - 1);
       mult(xb, wb);
     };
-    issue_x(xs0, 0); issue_x(xs1, 1); issue_x(xs2, 2);
-    issue_w(ws0, 0); issue_w(ws1, 1); issue_w(ws2, 2);
-    // chunk 0: everything but chunks 1 and 2 (16 ops) has landed
+    // Chunk by chunk (rows, then planes), the order of every later refill:
+    // the wait counts below count loads in issue order.
+    issue_x(xs0, 0); issue_w(ws0, 0);
+    issue_x(xs1, 1); issue_w(ws1, 1);
+    issue_x(xs2, 2); issue_w(ws2, 2);
+    // chunk 0: everything but chunks 1 and 2 (the last 16 ops) has landed
     gemm::stage_sync<16>();
     // The slots of chunk k0 + j are xs[j], ws[j].  The loop body is straight
     // line (a conditional chunk inside it made the compiler wait for every
@@ -677,9 +697,165 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
 
 }
 
+// ---------------------------------------------------------------------------
+// 5. small batches: logits and selection fused, 16 tokens per workgroup
+//    (bf16 x, at most 64 experts)
+// ---------------------------------------------------------------------------
+// Below a thousand tokens the router is latency-bound: few workgroups, each
+// waiting on long chains of dependent loads.  Here one workgroup of 16 waves
+// takes a histogram block of 16 tokens.  Wave w computes the logits of the
+// block's tokens and all experts over the w-th sixteenth of the hidden
+// dimension, l = x.hi + x.mid + x.lo as in 2a, splitting the fp32 gate
+// weights into their three bf16 parts in registers (as in 1).  The sixteen
+// partial sums are added in wave order through LDS, the logit bias follows,
+// then the selection of 3 runs on the block.  Every workgroup reads the
+// whole gate; workgroup b also stores the split parts of the k-steps whose
+// index is b modulo the number of workgroups (the backward's logits read
+// them), so each part is written once.
+constexpr int SR_TOK = 16;     // tokens per workgroup (one histogram block)
+constexpr int SR_WAVES = 16;   // waves per workgroup = slices of the hidden dimension
+
+template <int KMAX>
+__global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs r) {
+  using gemm::u32x4;
+  __shared__ float part[SR_WAVES][SR_TOK][65];
+  __shared__ float lg[SR_TOK][65];
+  __shared__ unsigned long long masks[64];
+  __shared__ float gsc[SR_TOK][MAX_GROUPS + 1];
+  __shared__ float sbias[64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int t0 = blockIdx.x * SR_TOK;
+  const int E = r.E, d = r.d;
+  const int ntok = min(SR_TOK, r.T - t0);
+  if (tid < E) {
+    sbias[tid] = r.select_bias ? r.select_bias[tid] : 0.f;
+    masks[tid] = 0ull;
+  }
+
+  // a. partial logits, 32 experts x 32 token columns per matrix op (columns
+  // past the block's tokens repeat its last token and are dropped)
+  const int kspan = d / SR_WAVES;            // a multiple of 16
+  const int k0 = wave * kspan;
+  const bf16_t* xp =
+      static_cast<const bf16_t*>(r.x) + (size_t)(t0 + min(l32, ntok - 1)) * d + k0 + 8 * hi;
+  const int n_eb = (E + 31) / 32;            // expert blocks: 1 or 2
+  const float* wp[2];
+  size_t prow[2];
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb) {
+    const int er = min(eb * 32 + l32, E - 1);
+    wp[eb] = r.w_gate + (size_t)er * d + k0 + 8 * hi;
+    prow[eb] = (size_t)er * d + k0 + 8 * hi;
+  }
+  const size_t pn = (size_t)E * d;
+  f32x16 acc[2];
+#pragma unroll
+  for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[eb][q] = 0.f;
+  // split 8 fp32 gate weights into hi, mid, lo bf16 parts
+  auto split8 = [](float4 a, float4 b, bf16x8& ph, bf16x8& pm, bf16x8& pl) {
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hh[2], mm[2], ll[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float f = v[2 * i + q];
+        const bf16_t bh = f32_to_bf16(f);
+        const float r1 = f - bf16_to_f32(bh);
+        const bf16_t bm = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(bm);
+        hh[q] = bh; mm[q] = bm; ll[q] = f32_to_bf16(r2);
+      }
+      h[i] = hh[0] | (hh[1] << 16); m[i] = mm[0] | (mm[1] << 16); l[i] = ll[0] | (ll[1] << 16);
+    }
+    ph = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+    pm = __builtin_bit_cast(bf16x8, (u32x4){m[0], m[1], m[2], m[3]});
+    pl = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+  };
+  constexpr int U = 2;   // k-steps of 16 whose loads are in flight together
+  for (int k = 0; k < kspan; k += 16 * U) {
+    bf16x8 xf[U];
+    float4 wv[U][2][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = min(k + 16 * u, kspan - 16);   // past the end: re-read, unused
+      xf[u] = *reinterpret_cast<const bf16x8*>(xp + kk);
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) {
+        if (eb >= n_eb) continue;
+        wv[u][eb][0] = *reinterpret_cast<const float4*>(wp[eb] + kk);
+        wv[u][eb][1] = *reinterpret_cast<const float4*>(wp[eb] + kk + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + 16 * u >= kspan) continue;
+      const int kk = k + 16 * u;
+      const bool mine = ((k0 + kk) / 16) % (int)gridDim.x == (int)blockIdx.x;
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) {
+        if (eb >= n_eb) continue;
+        bf16x8 ph, pm, pl;
+        split8(wv[u][eb][0], wv[u][eb][1], ph, pm, pl);
+        acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, xf[u], acc[eb], 0, 0, 0);
+        acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, xf[u], acc[eb], 0, 0, 0);
+        acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, xf[u], acc[eb], 0, 0, 0);
+        if (mine && eb * 32 + l32 < E) {
+          bf16_t* dst = r.planes + prow[eb] + kk;
+          *reinterpret_cast<bf16x8*>(dst) = ph;
+          *reinterpret_cast<bf16x8*>(dst + pn) = pm;
+          *reinterpret_cast<bf16x8*>(dst + 2 * pn) = pl;
+        }
+      }
+    }
+  }
+  // acc[eb][q] = D[e][t]: e = 32 eb + 8 (q / 4) + 4 hi + q % 4, t = l32
+  if (l32 < SR_TOK) {
+#pragma unroll
+    for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = eb * 32 + 8 * (q / 4) + 4 * hi + (q % 4);
+        if (eb < n_eb && e < E) part[wave][l32][e] = acc[eb][q];
+      }
+  }
+  __syncthreads();
+  // the slices' sum in wave order, then the logit bias
+  for (int i = tid; i < SR_TOK * E; i += SR_WAVES * 64) {
+    const int t = i / E, e = i % E;
+    float v = part[0][t][e];
+#pragma unroll
+    for (int w = 1; w < SR_WAVES; ++w) v += part[w][t][e];
+    lg[t][e] = v + (r.logit_bias ? r.logit_bias[e] : 0.f);
+  }
+  __syncthreads();
+
+  SelectArgs sa{};
+  sa.logit_bias = r.logit_bias; sa.select_bias = r.select_bias;
+  sa.T = r.T; sa.E = E; sa.K = r.K; sa.score = r.score;
+  sa.n_groups = r.n_groups; sa.topk_groups = r.topk_groups; sa.norm_topk = r.norm_topk;
+  sa.routed_scale = r.routed_scale;
+  sa.topk_idx = r.topk_idx; sa.topk_w = r.topk_w; sa.rank = r.rank;
+  sa.block_counts = r.block_counts;
+  select_block<KMAX, 64, SR_TOK>(sa, &lg[0][0], 65, t0, ntok, masks, gsc, sbias);
+}
+
 }  // namespace
 
-int router_tokens_per_block(int) { return 64; }
+// Small batches (bf16 x, at most 64 experts, hidden dimension a multiple
+// of 256): the fused 16-token kernel of 5.
+static bool router_small(int T, int E, int d, int dtype) {
+  return dtype == 1 && T > 0 && T < 1024 && E <= 64 && d % (16 * SR_WAVES) == 0;
+}
+
+int router_tokens_per_block(int T, int E, int d, int dtype) {
+  return router_small(T, E, d, dtype) ? SR_TOK : 64;
+}
 
 // Waves of the logits kernel for one d-slice.
 static int logits_tiles(int T, int E) {
@@ -711,6 +887,12 @@ hipError_t launch_logits(const LogitsArgs& la, hipStream_t s) {
 }
 
 hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
+  if (router_small(r.T, r.E, r.d, r.dtype)) {
+    const dim3 grid((r.T + SR_TOK - 1) / SR_TOK), block(SR_WAVES * 64);
+    if (r.K <= 8) hipLaunchKernelGGL(router_small_kernel<8>, grid, block, 0, s, r);
+    else hipLaunchKernelGGL(router_small_kernel<MAX_TOPK>, grid, block, 0, s, r);
+    return hipGetLastError();
+  }
   if (router_fused(r.T, r.E, r.K, r.n_groups, r.dtype)) {
     const int64_t n = (int64_t)r.E * r.d;
     hipLaunchKernelGGL(split_gate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
