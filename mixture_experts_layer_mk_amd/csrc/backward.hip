@@ -116,13 +116,24 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(BwdAuxArgs a) {
     }
     u += se * dsk;
   }
+  // dl in fp32, and as its bf16 hi and lo parts for the gate gradient's
+  // matrix ops (dl - hi - lo is below 2^-16 |dl|); pad columns zero
+  bf16_t* ph = a.dlp + (size_t)t * a.ldp;
+  bf16_t* pl = ph + a.ldp / 2;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     const int e = lane + 64 * c;
-    if (e >= a.E) continue;
+    if (e >= a.ldp / 2) continue;
+    if (e >= a.E) {
+      ph[e] = pl[e] = (bf16_t)0;
+      continue;
+    }
     const float s = sv[c];
     const float dl = (a.score == 0) ? s * (ds[c] - u) : ds[c] * s * (1.f - s);
     a.dl[(size_t)t * a.E + e] = dl;
+    const bf16_t h = f32_to_bf16(dl);
+    ph[e] = h;
+    pl[e] = f32_to_bf16(dl - bf16_to_f32(h));
   }
 }
 
@@ -145,55 +156,17 @@ __global__ __launch_bounds__(256) void dl_colsum_kernel(BwdAuxArgs a, const floa
   a.dlogit_bias[e] = s;
 }
 
-// dWg partials: thread = column j, 32 experts per workgroup, one chunk of
-// tokens; dl of 64 tokens at a time staged in LDS.
-constexpr int GG_E = 32, GG_T = 64;
-__global__ __launch_bounds__(256) void gate_grad_part_kernel(BwdAuxArgs a) {
-  __shared__ float sdl[GG_T][GG_E];
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  const int e0 = blockIdx.y * GG_E;
-  const int chunk = blockIdx.z;
-  const int per = (a.T + a.n_chunk - 1) / a.n_chunk;
-  const int t0 = chunk * per, t1 = min(t0 + per, a.T);
-  float acc[GG_E];
-#pragma unroll
-  for (int i = 0; i < GG_E; ++i) acc[i] = 0.f;
-  for (int tb = t0; tb < t1; tb += GG_T) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < GG_T * GG_E; i += 256) {
-      const int tt = i / GG_E, ee = i % GG_E;
-      const int t = tb + tt, e = e0 + ee;
-      sdl[tt][ee] = (t < t1 && e < a.E) ? a.dl[(size_t)t * a.E + e] : 0.f;
-    }
-    __syncthreads();
-    if (j < a.d) {
-      const int n = min(GG_T, t1 - tb);
-      for (int t8 = 0; t8 < n; t8 += 8) {
-        float xv[8];      // eight token loads in flight (zeros past the chunk)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          xv[q] = (t8 + q < n) ? bf16_to_f32(a.x[(size_t)(tb + t8 + q) * a.d + j]) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-          for (int i = 0; i < GG_E; ++i) acc[i] = fmaf(sdl[t8 + q][i], xv[q], acc[i]);
-      }
-    }
-  }
-  if (j >= a.d) return;
-#pragma unroll
-  for (int i = 0; i < GG_E; ++i) {
-    const int e = e0 + i;
-    if (e < a.E) a.dwg_part[((size_t)chunk * a.E + e) * a.d + j] = acc[i];
-  }
-}
+// dWg = dl^T x on the matrix cores: the grouped backward GEMM's shared
+// dW1/dW3 product (k = tokens, both operands mn-major) with dl's bf16 hi
+// and lo parts as the "dA" operand, so the hi rows of the result are hi^T x
+// and the lo rows lo^T x.  k is split into gg_splits ranges; the GEMM's own
+// split reduction adds them in order into split 0's place (its dW1 / dW3
+// outputs are pointed there), and the gate gradient is hi rows + lo rows.
 __global__ __launch_bounds__(256) void gate_grad_sum_kernel(BwdAuxArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = (int64_t)a.E * a.d;
   if (i >= n) return;
-  float s = 0.f;
-  for (int c = 0; c < a.n_chunk; ++c) s += a.dwg_part[(size_t)c * n + i];
-  a.dw_gate[i] = s;
+  a.dw_gate[i] = a.dwg_part[i] + a.dwg_part[(size_t)(a.ldp / 2) * a.d + i];
 }
 
 // dx = RNE(dy + dx_shared + sum_k dx_rows[slot_row[t][k]] + dl Wg): thread =
@@ -305,10 +278,22 @@ hipError_t launch_router_bwd(const BwdAuxArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s) {
-  const dim3 grid((a.d + 255) / 256, (a.E + GG_E - 1) / GG_E, a.n_chunk);
-  hipLaunchKernelGGL(gate_grad_part_kernel, grid, dim3(256), 0, s, a);
   const int64_t n = (int64_t)a.E * a.d;
-  hipLaunchKernelGGL(gate_grad_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  if (a.T > 0) {
+    BwdGemmArgs g{};
+    g.kind = 3; g.shared = true;
+    g.T = a.T; g.d = a.d; g.inner = a.ldp / 2; g.n_experts = 1;
+    g.x = a.x; g.da = a.dlp; g.ldda = a.ldp; g.zero = a.zero;
+    // the product's hi rows, then its lo rows, in split 0's place
+    g.dw1 = a.dwg_part; g.dw3 = a.dwg_part + (size_t)(a.ldp / 2) * a.d;
+    g.splits = a.gg_splits; g.part = a.dwg_part;
+    const hipError_t e = launch_gemm_bwd(g, s);
+    if (e != hipSuccess) return e;
+  } else {
+    return launch_fill_zero(a.dw_gate, n, s);
+  }
+  hipLaunchKernelGGL(gate_grad_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -198,7 +198,8 @@ struct BwdAuxArgs {
   float* dl;                        // [T][E] logit gradient
   float* dlogit_bias;               // [E] or NULL
   const bf16_t* x; const bf16_t* dy;
-  float* dwg_part; int n_chunk;     // [n_chunk][E][d] partial gate gradients
+  bf16_t* dlp; int ldp;             // dl as bf16 hi and lo parts: [T][ldp], lo at ldp / 2
+  float* dwg_part; int gg_splits;   // [gg_splits][ldp][d] partial gate gradients (hi rows, lo rows)
   float* dw_gate;                   // [E][d]
   const bf16_t* dx_rows;            // [T K][d]
   const bf16_t* dx_shared;          // [T][d] or NULL

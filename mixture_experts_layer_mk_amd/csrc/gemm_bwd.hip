@@ -431,7 +431,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bwd_kernel(BwdGemmArgs a) {
 }
 
 // Sum of the split-k partials of a weight gradient, splits in order, into
-// the gradient's own layout (4 consecutive elements per thread).
+// the gradient's own layout (4 consecutive elements per thread).  The
+// outputs may alias split 0's partials (the gate gradient points them
+// there): a thread reads its elements of every split before it writes them.
 template <int KIND>
 __global__ __launch_bounds__(256) void split_reduce_kernel(BwdGemmArgs a) {
   const int M = (KIND == 2) ? a.d : 2 * a.inner;

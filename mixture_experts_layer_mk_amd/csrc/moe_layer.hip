@@ -430,9 +430,9 @@ moe_status_t forward_impl(const moe_layer_desc_t* desc, const void* x,
 // regions hold g h for the weight gradients), then the backward's own.
 struct BwdLayout {
   Layout f;
-  int64_t plog, g_r, g_s, da_r, da_s, dx_rows, dx_s, row_g, dg_part, dg, dl, dwg_part, zero,
+  int64_t plog, g_r, g_s, da_r, da_s, dx_rows, dx_s, row_g, dg_part, dg, dl, dlp, dwg_part, zero,
       part, total;
-  int32_t n_part, n_chunk;
+  int32_t n_part, gg_splits, ldp;
   int32_t splits2, splits3;   // k splits of the shared dW2 and dW1/dW3 GEMMs
 };
 
@@ -445,7 +445,14 @@ int32_t shared_wgrad_splits(int64_t tiles, int64_t T) {
   return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, 16));
 }
 
-constexpr int kGateGradChunks = 128;
+// k splits of the gate gradient's GEMM (dl^T x, 2 inner_p x d per split):
+// about one tile per CU, keeping >= 512 tokens per split.
+int32_t gate_grad_splits(int64_t d, int64_t T) {
+  const int64_t tiles = (d + 255) / 256;
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(T / 512, 1));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
 
 BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   BwdLayout B;
@@ -459,7 +466,8 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   const int64_t TK = (int64_t)d.T * d.top_k;
   const int64_t ksi = (int64_t)d.n_shared * d.shared_inner;
   B.n_part = (d.inner + 127) / 128;
-  B.n_chunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(kGateGradChunks, d.T / 64));
+  B.gg_splits = gate_grad_splits(d.d, d.T);
+  B.ldp = 2 * ((d.n_routed + 3) & ~3);
   B.plog = take((int64_t)B.f.ds * d.T * B.f.ep * 4);
   B.g_r = take(TK * d.inner * 4);
   B.g_s = d.n_shared > 0 ? take((int64_t)d.T * ksi * 4) : -1;
@@ -472,7 +480,8 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   B.dg = take(TK * 4);
   B.dl = take((int64_t)d.T * d.n_routed * 4);
   const int64_t colsum = (int64_t)((d.T + 255) / 256) * d.n_routed;
-  B.dwg_part = take(std::max<int64_t>((int64_t)B.n_chunk * d.n_routed * d.d, colsum) * 4);
+  B.dlp = take((int64_t)d.T * B.ldp * 2);
+  B.dwg_part = take(std::max<int64_t>((int64_t)B.gg_splits * B.ldp * d.d, colsum) * 4);
   B.zero = take(1024);
   B.splits2 = B.splits3 = 1;
   if (d.n_shared > 0) {
@@ -566,7 +575,8 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   aux.dl = static_cast<float*>(at(B.dl));
   aux.dlogit_bias = dlogit_bias;
   aux.x = xb; aux.dy = dyb;
-  aux.dwg_part = static_cast<float*>(at(B.dwg_part)); aux.n_chunk = B.n_chunk;
+  aux.dlp = static_cast<bf16_t*>(at(B.dlp)); aux.ldp = B.ldp;
+  aux.dwg_part = static_cast<float*>(at(B.dwg_part)); aux.gg_splits = B.gg_splits;
   aux.dw_gate = dw_gate;
   aux.dx_rows = static_cast<const bf16_t*>(at(B.dx_rows));
   aux.dx_shared = static_cast<const bf16_t*>(at(B.dx_s));
