@@ -73,6 +73,8 @@ struct RouterArgs {
   int ds, ep;                 // d-slices of the logits GEMM; logit row stride
   bf16_t* planes;             // [3][E][d] gate split into bf16 parts (bf16 x)
   float* plog;                // [ds][T][ep] partial logits
+  float* logits;              // or NULL: [T][ep] logits before the logit bias (fused and
+                              // small-batch paths; the split path leaves them in plog)
   int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
 };
 struct LogitsArgs {
@@ -88,13 +90,13 @@ struct SelectArgs {
   int32_t* topk_idx; float* topk_w; int32_t* rank; int32_t* block_counts;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
-// Partial logits only (bf16 x: the gate planes must already be split).
-hipError_t launch_logits(const LogitsArgs& a, hipStream_t s);
 // Tokens per histogram block (dtype: 0 = f32, 1 = bf16 x).
 int router_tokens_per_block(int T, int E, int d, int dtype);
 int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 // True when logits and selection run fused (no partial-logit buffer).
 bool router_fused(int T, int E, int K, int n_groups, int dtype);
+// True when small batches route with the fused 16-token kernel.
+bool router_small(int T, int E, int d, int dtype);
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s);

@@ -231,10 +231,13 @@ hipError_t quant_x_rows(const moe_layer_desc_t& d, const Layout& L, char* ws, co
 // choice).  mark(i) records trace event i before step i.
 // (FP8 layers: also the token rows in E4M3.)
 template <class Mark>
+// logits (or NULL): where the fused and small-batch routers store the logits
+// before the logit bias, [T][ep] (the split router leaves them in L.plog).
 moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws,
                             const void* x, const float* w_gate, const float* logit_bias,
                             const float* select_bias, int32_t* idx, float* gw,
-                            int32_t* expert_counts, hipStream_t s, Mark mark) {
+                            int32_t* expert_counts, hipStream_t s, Mark mark,
+                            float* logits = nullptr) {
   auto at = [&](int64_t off) -> void* { return off < 0 ? nullptr : ws + off; };
   const bool bf16 = d.dtype != MOE_F32;
   const bool fp8 = d.dtype == MOE_FP8;
@@ -256,6 +259,7 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
     r.ds = L.ds; r.ep = L.ep;
     r.planes = static_cast<bf16_t*>(at(L.planes));
     r.plog = static_cast<float*>(at(L.plog));
+    r.logits = logits;
     r.topk_idx = idx; r.topk_w = gw;
     r.rank = static_cast<int32_t*>(at(L.rank));
     r.block_counts = static_cast<int32_t*>(at(L.block_counts));
@@ -468,7 +472,12 @@ BwdLayout bwd_layout_of(const moe_layer_desc_t& d) {
   B.n_part = (d.inner + 127) / 128;
   B.gg_splits = gate_grad_splits(d.d, d.T);
   B.ldp = 2 * ((d.n_routed + 3) & ~3);
-  B.plog = take((int64_t)B.f.ds * d.T * B.f.ep * 4);
+  // logits left by the fused and small-batch routers (the split router's
+  // partial slices stay in the forward layout's plog)
+  const int rdt = d.dtype != MOE_F32 ? 1 : 0;
+  const bool one_slice = router_fused(d.T, d.n_routed, d.top_k, d.n_groups, rdt) ||
+                         router_small(d.T, d.n_routed, d.d, rdt);
+  B.plog = one_slice ? take((int64_t)d.T * B.f.ep * 4) : -1;
   B.g_r = take(TK * d.inner * 4);
   B.g_s = d.n_shared > 0 ? take((int64_t)d.T * ksi * 4) : -1;
   B.da_r = take(TK * 2 * d.inner * 2);
@@ -549,8 +558,14 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   float* gw = static_cast<float*>(at(L.topk_w));
   if (!mark(0)) return MOE_ERR_HIP;
   auto no_mark = [](int) { return true; };
+  // The routing pass leaves the logits for the router backward: the fused
+  // and small-batch routers store them (one slice) in B.plog, the split
+  // router's partial slices are in L.plog.
+  const int rdt = d.dtype != MOE_F32 ? 1 : 0;
+  const bool one_slice = router_fused(d.T, d.n_routed, d.top_k, d.n_groups, rdt) ||
+                         router_small(d.T, d.n_routed, d.d, rdt);
   st = route_dispatch(d, L, ws, x, w_gate, logit_bias, select_bias, idx, gw, nullptr, s,
-                      no_mark);
+                      no_mark, one_slice ? static_cast<float*>(at(B.plog)) : nullptr);
   if (st != MOE_OK) return st;
   hipError_t err;
 #define MOE_CHECK(call)                      \
@@ -566,7 +581,8 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
   BwdAuxArgs aux{};
   aux.T = d.T; aux.d = d.d; aux.E = d.n_routed; aux.K = d.top_k; aux.score = d.score;
   aux.norm_topk = d.norm_topk; aux.routed_scale = d.routed_scale;
-  aux.plog = static_cast<const float*>(at(B.plog)); aux.ds = L.ds; aux.ep = L.ep;
+  aux.plog = static_cast<const float*>(at(one_slice ? B.plog : L.plog));
+  aux.ds = one_slice ? 1 : L.ds; aux.ep = L.ep;
   aux.logit_bias = logit_bias; aux.w_gate = w_gate;
   aux.topk_idx = idx; aux.topk_w = gw; aux.slot_row = slot_row;
   aux.dg_part = static_cast<const float*>(at(B.dg_part)); aux.n_part = B.n_part;
@@ -686,15 +702,10 @@ moe_status_t backward_impl(const moe_layer_desc_t* desc, const void* x, const fl
     if (!mark(4)) return MOE_ERR_HIP;
     if (in_order) MOE_CHECK(shared_gateup(s));
   }
-  // 3. router: logits again (partial sums), scores, dg, dl, logit-bias and
+  // 3. router: scores from the routing pass's logits, dg, dl, logit-bias and
   // gate gradients
   {
     if (!mark(5)) return MOE_ERR_HIP;
-    LogitsArgs la{};
-    la.x = xb; la.planes = static_cast<const bf16_t*>(at(L.planes));
-    la.T = d.T; la.d = d.d; la.E = d.n_routed; la.ep = L.ep; la.ds = L.ds;
-    la.plog = static_cast<float*>(at(B.plog));
-    MOE_CHECK(launch_logits(la, s));
     MOE_CHECK(launch_router_bwd(aux, s));
     MOE_CHECK(launch_gate_grad(aux, s));
   }

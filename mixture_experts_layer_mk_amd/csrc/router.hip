@@ -555,6 +555,16 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
     if (k0 + 2 < nch) chunk(k0 + 2, xs2, ws2, xs1, ws1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the redundant tail loads
     // acc[r] = D[e][t]: e = 32 (w & 1) + 8 (r / 4) + 4 hi + r % 4, t = tr
+    if (a.logits && t0 + tr < T) {   // before the bias; 4 consecutive experts per store
+      float* row = a.logits + (size_t)(t0 + tr) * a.ep;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = (wave & 1) * 32 + 8 * g + 4 * hi;
+        if (e < a.ep)
+          *reinterpret_cast<float4*>(row + e) =
+              make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int e = (wave & 1) * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
@@ -831,6 +841,7 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
     float v = part[0][t][e];
 #pragma unroll
     for (int w = 1; w < SR_WAVES; ++w) v += part[w][t][e];
+    if (r.logits && t < ntok) r.logits[(size_t)(t0 + t) * r.ep + e] = v;   // before the bias
     lg[t][e] = v + (r.logit_bias ? r.logit_bias[e] : 0.f);
   }
   __syncthreads();
@@ -849,7 +860,7 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
 
 // Small batches (bf16 x, at most 64 experts, hidden dimension a multiple
 // of 256): the fused 16-token kernel of 5.
-static bool router_small(int T, int E, int d, int dtype) {
+bool router_small(int T, int E, int d, int dtype) {
   return dtype == 1 && T > 0 && T < 1024 && E <= 64 && d % (16 * SR_WAVES) == 0;
 }
 
@@ -877,13 +888,6 @@ int router_dsplit(int T, int E, int d, int dtype) {
 // 75 us).
 bool router_fused(int T, int E, int K, int n_groups, int dtype) {
   return dtype == 1 && T >= 1024 && E <= 64 && K <= FR_KMAX && n_groups == 1;
-}
-
-hipError_t launch_logits(const LogitsArgs& la, hipStream_t s) {
-  if (la.T == 0) return hipSuccess;
-  const int tiles = logits_tiles(la.T, la.E) * la.ds;
-  hipLaunchKernelGGL(logits_mfma_kernel, dim3((tiles + 3) / 4), dim3(256), 0, s, la);
-  return hipGetLastError();
 }
 
 hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
