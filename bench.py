@@ -41,10 +41,15 @@ GATEUP = {
              os.path.join(ROOT, "profiles", "traffic_gemm_gateup_16b.json")),
     "fp8": ("gemm_fp8_kernel<0", ("common.h", "gemm_common.h", "gemm_fp8.hip"),
             os.path.join(ROOT, "profiles", "traffic_gemm_fp8_gateup_16b.json")),
-    # the backward's slowest GEMM stage: routed dW1/dW3
-    "bwd": ("gemm_bwd_kernel<3, false>", ("common.h", "gemm_common.h", "gemm_bwd.hip"),
-            os.path.join(ROOT, "profiles", "traffic_gemm_bwd_dw13_routed_16b.json")),
+    # the backward's two slowest GEMM stages (either can be the longer one):
+    # the recomputed routed gate/up with the SwiGLU backward, routed dW1/dW3
+    "bwd_gateup": ("gemm_bf16_kernel<3", ("common.h", "gemm_common.h", "gemm_bf16.hip"),
+                   os.path.join(ROOT, "profiles", "traffic_gemm_gateup_bwd_16b.json")),
+    "bwd_dw13": ("gemm_bwd_kernel<3, false>", ("common.h", "gemm_common.h", "gemm_bwd.hip"),
+                 os.path.join(ROOT, "profiles", "traffic_gemm_bwd_dw13_routed_16b.json")),
 }
+# The backward stages whose launch a committed traffic summary covers.
+BWD_TRAFFIC = {"gateup_bwd_routed": "bwd_gateup", "dw13_routed": "bwd_dw13"}
 
 
 def gateup_flops(cfg) -> float:
@@ -81,12 +86,15 @@ def measured_traffic(kind: str = "bf16"):
 
 
 def summarize_traffic(fetch_csv, write_csv, copy_mb):
-    """Write the traffic summaries of the dominant kernels (routed gate/up
-    launch of the bf16 and of the FP8 variant) from two rocprofv3 --pmc
-    counter files (FETCH_SIZE run, WRITE_SIZE run, both of a bench run with
+    """Write the traffic summaries of the dominant kernels (the gate/up launch
+    of the bf16 and of the FP8 forward; the backward's routed gate/up and
+    routed dW1/dW3 launches) from two rocprofv3 --pmc counter files
+    (FETCH_SIZE run, WRITE_SIZE run, both of a bench run with
     --copy-calibration-mb copy_mb).  Each counter is scaled by what it reads
     for the plain device copy of copy_mb MiB; of the launches of a kernel the
-    one with the largest grid is the gate/up launch (routed and shared tiles)."""
+    one with the largest grid is the one summarised (the forward gate/up
+    launch holds the routed and shared tiles; the backward's routed launches
+    are larger than its shared ones)."""
     import csv
     import collections
 
@@ -99,8 +107,10 @@ def summarize_traffic(fetch_csv, write_csv, copy_mb):
 
     vals = {"fetch": per_kernel(fetch_csv, "FETCH_SIZE"),
             "write": per_kernel(write_csv, "WRITE_SIZE")}
+    whats = {"bwd_gateup": "routed gate/up + SwiGLU backward launch",
+             "bwd_dw13": "routed dW1/dW3 launch"}
     for kind, (prefix, _, path) in GATEUP.items():
-        what = "routed dW1/dW3 launch" if kind == "bwd" else "gate/up launch (routed + shared)"
+        what = whats.get(kind, "gate/up launch (routed + shared)")
         out = {"source_hash": source_hash(kind), "kernel": prefix.rstrip(">") + ">, " + what,
                "copy_calibration_mib": copy_mb}
         for name in ("fetch", "write"):
@@ -402,7 +412,8 @@ def time_backward(moe, cfg, d, steps, warmup):
         "roofline": {"kernel": BWD_KERNEL[dom], "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("bwd") if dom == "dw13_routed" else None,
+                     "traffic": (measured_traffic(BWD_TRAFFIC[dom]) if dom in BWD_TRAFFIC
+                                 else None),
                      "flops_per_launch": flops[dom], "avg_launch_ms": round(stage_ms[dom], 4)},
     }
 
