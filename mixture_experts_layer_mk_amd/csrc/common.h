@@ -84,6 +84,7 @@ struct LogitsArgs {
 };
 struct SelectArgs {
   const float* plog; int ep, ds;
+  float* logits;              // or NULL: the summed logits before the bias, [T][ep]
   const float* logit_bias; const float* select_bias;
   int T, E, K, score, n_groups, topk_groups, norm_topk;
   float routed_scale;
@@ -95,8 +96,10 @@ int router_tokens_per_block(int T, int E, int d, int dtype);
 int router_dsplit(int T, int E, int d, int dtype);   // d-slices of the logits GEMM
 // True when logits and selection run fused (no partial-logit buffer).
 bool router_fused(int T, int E, int K, int n_groups, int dtype);
-// True when small batches route with the fused 16-token kernel.
+// True when small batches route with the fused 16-token kernel, and its
+// hidden-dimension slices (partial logits [slices][T][ep] in plog).
 bool router_small(int T, int E, int d, int dtype);
+int router_small_slices(int d);
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s);

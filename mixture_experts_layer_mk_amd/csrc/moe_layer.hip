@@ -203,9 +203,14 @@ Layout layout_of(const moe_layer_desc_t& d) {
   L.s = d.n_shared > 0 ? take((int64_t)d.T * d.d * 4) : -1;
   L.ds = router_dsplit(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
   L.ep = (d.n_routed + 3) & ~3;
-  L.planes = bf16 ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
-  L.plog = router_fused(d.T, d.n_routed, d.top_k, d.n_groups, bf16 ? 1 : 0)
-               ? -1 : take((int64_t)L.ds * d.T * L.ep * 4);
+  // router: the gate's bf16 parts (fused and split paths), partial logits
+  // (split and small-batch paths)
+  const bool small = router_small(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
+  const bool fused = router_fused(d.T, d.n_routed, d.top_k, d.n_groups, bf16 ? 1 : 0);
+  L.planes = (bf16 && !small) ? take((int64_t)3 * d.n_routed * d.d * 2) : -1;
+  const int64_t slices = small ? router_small_slices(d.d) : L.ds;
+  L.plog = fused ? -1 : take(slices * d.T * L.ep * 4);
+
   L.total = off;
   return L;
 }

@@ -367,25 +367,26 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const float* l
   }
 }
 
-template <int KMAX>
-__global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
-  extern __shared__ float lg[];               // [64][E + 1]: logits, then scores
+// TB tokens per block (64, or 16 for the small-batch path), 8 TB threads.
+template <int KMAX, int TB>
+__global__ __launch_bounds__(TB * 8) void select_kernel(SelectArgs a) {
+  extern __shared__ float lg[];               // [TB][E + 1]: logits, then scores
   __shared__ unsigned long long masks[MAX_EXPERTS];
-  __shared__ float gsc[64][MAX_GROUPS + 1];
+  __shared__ float gsc[TB][MAX_GROUPS + 1];
   __shared__ float sbias[MAX_EXPERTS];        // selection bias (0 without one)
   const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * 64;
+  const int t0 = blockIdx.x * TB;
   const int E = a.E, K = a.K, ld = E + 1;
-  const int ntok = min(64, a.T - t0);
+  const int ntok = min(TB, a.T - t0);
 
   const int q4 = a.ep / 4;
   const float4* p4 = reinterpret_cast<const float4*>(a.plog);
   const size_t slice4 = (size_t)a.T * q4;
-  for (int e = tid; e < E; e += 512) {
+  for (int e = tid; e < E; e += TB * 8) {
     sbias[e] = a.select_bias ? a.select_bias[e] : 0.f;
     masks[e] = 0ull;
   }
-  for (int i = tid; i < ntok * q4; i += 512) {
+  for (int i = tid; i < ntok * q4; i += TB * 8) {
     const int r = i / q4, c = i % q4;
     const size_t o = (size_t)(t0 + r) * q4 + c;
     // all slices' loads in flight first, then the sum in slice order
@@ -397,6 +398,8 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int sl = 1; sl < 16; ++sl)
       if (sl < a.ds) { v.x += w[sl].x; v.y += w[sl].y; v.z += w[sl].z; v.w += w[sl].w; }
+    if (a.logits)   // the logits before the bias, [T][ep]
+      reinterpret_cast<float4*>(a.logits)[(size_t)(t0 + r) * q4 + c] = v;
     const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(512) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  select_block<KMAX, MAX_EXPERTS, 64>(a, lg, ld, t0, ntok, masks, gsc, sbias);
+  select_block<KMAX, MAX_EXPERTS, TB>(a, lg, ld, t0, ntok, masks, gsc, sbias);
 }
 
 // ---------------------------------------------------------------------------
@@ -708,64 +711,53 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 5. small batches: logits and selection fused, 16 tokens per workgroup
-//    (bf16 x, at most 64 experts)
+// 5. small batches: logits over many workgroups, then the selection of 3
+//    on 16-token blocks (bf16 x, at most 64 experts)
 // ---------------------------------------------------------------------------
-// Below a thousand tokens the router is latency-bound: few workgroups, each
-// waiting on long chains of dependent loads.  Here one workgroup of 16 waves
-// takes a histogram block of 16 tokens.  Wave w computes the logits of the
-// block's tokens and all experts over the w-th sixteenth of the hidden
-// dimension, l = x.hi + x.mid + x.lo as in 2a, splitting the fp32 gate
-// weights into their three bf16 parts in registers (as in 1).  The sixteen
-// partial sums are added in wave order through LDS, the logit bias follows,
-// then the selection of 3 runs on the block.  Every workgroup reads the
-// whole gate; workgroup b also stores the split parts of the k-steps whose
-// index is b modulo the number of workgroups (the backward's logits read
-// them), so each part is written once.
-constexpr int SR_TOK = 16;     // tokens per workgroup (one histogram block)
-constexpr int SR_WAVES = 16;   // waves per workgroup = slices of the hidden dimension
+// Below a thousand tokens the router is latency-bound, and a workgroup that
+// reads the whole gate for its tokens is bound by its CU's load path.  Here
+// the hidden dimension is split over DS workgroups per 16-token histogram
+// block (grid = blocks x DS): workgroup (b, s) computes the block's logits
+// over the s-th slice, l = x.hi + x.mid + x.lo as in 2a with the fp32 gate
+// split into its bf16 parts in registers, one quarter of the slice per wave,
+// with every load of a wave in flight at once, and stores the slice's
+// partial logits (its four waves added in order) as the split path's plog.
+// select_kernel<K, 16> then adds the slices in order and selects.  (A single
+// kernel in which the last workgroup of a block went on to select, after a
+// ticket between release and acquire fences, spent 15 us of 28 in the
+// fences and the hand-off.)
+constexpr int SR_TOK = 16;     // tokens per histogram block
+constexpr int SR_WAVES = 4;    // waves per workgroup
 
-template <int KMAX>
-__global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs r) {
+__global__ __launch_bounds__(SR_WAVES * 64) void logits_small_kernel(RouterArgs r) {
   using gemm::u32x4;
   __shared__ float part[SR_WAVES][SR_TOK][65];
-  __shared__ float lg[SR_TOK][65];
-  __shared__ unsigned long long masks[64];
-  __shared__ float gsc[SR_TOK][MAX_GROUPS + 1];
-  __shared__ float sbias[64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  const int slice = blockIdx.y, DS = gridDim.y;
   const int t0 = blockIdx.x * SR_TOK;
-  const int E = r.E, d = r.d;
-  const int ntok = min(SR_TOK, r.T - t0);
-  if (tid < E) {
-    sbias[tid] = r.select_bias ? r.select_bias[tid] : 0.f;
-    masks[tid] = 0ull;
-  }
+  const int E = r.E, d = r.d, T = r.T;
+  const int ntok = min(SR_TOK, T - t0);
 
-  // a. partial logits, 32 experts x 32 token columns per matrix op (columns
-  // past the block's tokens repeat its last token and are dropped)
-  const int kspan = d / SR_WAVES;            // a multiple of 16
-  const int k0 = wave * kspan;
+  // partial logits of the wave's quarter of the slice, 32 experts x 32
+  // token columns per matrix op (columns past the block's tokens repeat its
+  // last token and are dropped)
+  const int kspan = d / (DS * SR_WAVES);     // a multiple of 16
+  const int k0 = (slice * SR_WAVES + wave) * kspan;
   const bf16_t* xp =
       static_cast<const bf16_t*>(r.x) + (size_t)(t0 + min(l32, ntok - 1)) * d + k0 + 8 * hi;
   const int n_eb = (E + 31) / 32;            // expert blocks: 1 or 2
   const float* wp[2];
-  size_t prow[2];
 #pragma unroll
-  for (int eb = 0; eb < 2; ++eb) {
-    const int er = min(eb * 32 + l32, E - 1);
-    wp[eb] = r.w_gate + (size_t)er * d + k0 + 8 * hi;
-    prow[eb] = (size_t)er * d + k0 + 8 * hi;
-  }
-  const size_t pn = (size_t)E * d;
+  for (int eb = 0; eb < 2; ++eb)
+    wp[eb] = r.w_gate + (size_t)min(eb * 32 + l32, E - 1) * d + k0 + 8 * hi;
   f32x16 acc[2];
 #pragma unroll
   for (int eb = 0; eb < 2; ++eb)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[eb][q] = 0.f;
-  // split 8 fp32 gate weights into hi, mid, lo bf16 parts
+  // split 8 fp32 gate weights into hi, mid, lo bf16 parts (as in 1)
   auto split8 = [](float4 a, float4 b, bf16x8& ph, bf16x8& pm, bf16x8& pl) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t h[4], m[4], l[4];
@@ -787,7 +779,7 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
     pm = __builtin_bit_cast(bf16x8, (u32x4){m[0], m[1], m[2], m[3]});
     pl = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
   };
-  constexpr int U = 2;   // k-steps of 16 whose loads are in flight together
+  constexpr int U = 4;   // k-steps of 16 whose loads are in flight together
   for (int k = 0; k < kspan; k += 16 * U) {
     bf16x8 xf[U];
     float4 wv[U][2][2];
@@ -805,8 +797,6 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (k + 16 * u >= kspan) continue;
-      const int kk = k + 16 * u;
-      const bool mine = ((k0 + kk) / 16) % (int)gridDim.x == (int)blockIdx.x;
 #pragma unroll
       for (int eb = 0; eb < 2; ++eb) {
         if (eb >= n_eb) continue;
@@ -815,12 +805,6 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
         acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, xf[u], acc[eb], 0, 0, 0);
         acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, xf[u], acc[eb], 0, 0, 0);
         acc[eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, xf[u], acc[eb], 0, 0, 0);
-        if (mine && eb * 32 + l32 < E) {
-          bf16_t* dst = r.planes + prow[eb] + kk;
-          *reinterpret_cast<bf16x8*>(dst) = ph;
-          *reinterpret_cast<bf16x8*>(dst + pn) = pm;
-          *reinterpret_cast<bf16x8*>(dst + 2 * pn) = pl;
-        }
       }
     }
   }
@@ -835,25 +819,14 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
       }
   }
   __syncthreads();
-  // the slices' sum in wave order, then the logit bias
-  for (int i = tid; i < SR_TOK * E; i += SR_WAVES * 64) {
+  // the slice's partial logits (its waves in order), [slice][T][ep]
+  for (int i = tid; i < ntok * E; i += SR_WAVES * 64) {
     const int t = i / E, e = i % E;
     float v = part[0][t][e];
 #pragma unroll
     for (int w = 1; w < SR_WAVES; ++w) v += part[w][t][e];
-    if (r.logits && t < ntok) r.logits[(size_t)(t0 + t) * r.ep + e] = v;   // before the bias
-    lg[t][e] = v + (r.logit_bias ? r.logit_bias[e] : 0.f);
+    r.plog[((size_t)slice * T + t0 + t) * r.ep + e] = v;
   }
-  __syncthreads();
-
-  SelectArgs sa{};
-  sa.logit_bias = r.logit_bias; sa.select_bias = r.select_bias;
-  sa.T = r.T; sa.E = E; sa.K = r.K; sa.score = r.score;
-  sa.n_groups = r.n_groups; sa.topk_groups = r.topk_groups; sa.norm_topk = r.norm_topk;
-  sa.routed_scale = r.routed_scale;
-  sa.topk_idx = r.topk_idx; sa.topk_w = r.topk_w; sa.rank = r.rank;
-  sa.block_counts = r.block_counts;
-  select_block<KMAX, 64, SR_TOK>(sa, &lg[0][0], 65, t0, ntok, masks, gsc, sbias);
 }
 
 }  // namespace
@@ -861,8 +834,12 @@ __global__ __launch_bounds__(SR_WAVES * 64) void router_small_kernel(RouterArgs 
 // Small batches (bf16 x, at most 64 experts, hidden dimension a multiple
 // of 256): the fused 16-token kernel of 5.
 bool router_small(int T, int E, int d, int dtype) {
-  return dtype == 1 && T > 0 && T < 1024 && E <= 64 && d % (16 * SR_WAVES) == 0;
+  return dtype == 1 && T > 0 && T < 1024 && E <= 64 && d % 256 == 0;
 }
+
+// Hidden-dimension slices of the small-batch router (each wave's quarter of
+// a slice a multiple of 16 columns).
+int router_small_slices(int d) { return d % 512 == 0 ? 8 : 4; }
 
 int router_tokens_per_block(int T, int E, int d, int dtype) {
   return router_small(T, E, d, dtype) ? SR_TOK : 64;
@@ -890,11 +867,32 @@ bool router_fused(int T, int E, int K, int n_groups, int dtype) {
   return dtype == 1 && T >= 1024 && E <= 64 && K <= FR_KMAX && n_groups == 1;
 }
 
+// The selection's arguments: partial logits in r.plog, ds slices.
+static SelectArgs select_args(const RouterArgs& r, int ds) {
+  SelectArgs sa{};
+  sa.plog = r.plog; sa.ep = r.ep; sa.ds = ds;
+  sa.logits = r.logits;
+  sa.logit_bias = r.logit_bias; sa.select_bias = r.select_bias;
+  sa.T = r.T; sa.E = r.E; sa.K = r.K; sa.score = r.score;
+  sa.n_groups = r.n_groups; sa.topk_groups = r.topk_groups; sa.norm_topk = r.norm_topk;
+  sa.routed_scale = r.routed_scale;
+  sa.topk_idx = r.topk_idx; sa.topk_w = r.topk_w; sa.rank = r.rank;
+  sa.block_counts = r.block_counts;
+  return sa;
+}
+
 hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
   if (router_small(r.T, r.E, r.d, r.dtype)) {
-    const dim3 grid((r.T + SR_TOK - 1) / SR_TOK), block(SR_WAVES * 64);
-    if (r.K <= 8) hipLaunchKernelGGL(router_small_kernel<8>, grid, block, 0, s, r);
-    else hipLaunchKernelGGL(router_small_kernel<MAX_TOPK>, grid, block, 0, s, r);
+    const int nblk = (r.T + SR_TOK - 1) / SR_TOK;
+    const int ds = router_small_slices(r.d);
+    hipLaunchKernelGGL(logits_small_kernel, dim3(nblk, ds), dim3(SR_WAVES * 64), 0, s, r);
+    SelectArgs sa = select_args(r, ds);
+    const size_t lds = (size_t)SR_TOK * (r.E + 1) * sizeof(float);
+    if (r.K <= 8)
+      hipLaunchKernelGGL((select_kernel<8, SR_TOK>), dim3(nblk), dim3(SR_TOK * 8), lds, s, sa);
+    else
+      hipLaunchKernelGGL((select_kernel<MAX_TOPK, SR_TOK>), dim3(nblk), dim3(SR_TOK * 8), lds, s,
+                         sa);
     return hipGetLastError();
   }
   if (router_fused(r.T, r.E, r.K, r.n_groups, r.dtype)) {
@@ -933,19 +931,13 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
     const int nb = ((r.T + 63) / 64) * ((r.E + 63) / 64);
     hipLaunchKernelGGL(logits_f32_kernel, dim3(nb), dim3(256), 0, s, la);
   }
-  // 3: selection
-  SelectArgs sa{};
-  sa.plog = r.plog; sa.ep = r.ep; sa.ds = r.dtype == 1 ? r.ds : 1;
-  sa.logit_bias = r.logit_bias; sa.select_bias = r.select_bias;
-  sa.T = r.T; sa.E = r.E; sa.K = r.K; sa.score = r.score;
-  sa.n_groups = r.n_groups; sa.topk_groups = r.topk_groups; sa.norm_topk = r.norm_topk;
-  sa.routed_scale = r.routed_scale;
-  sa.topk_idx = r.topk_idx; sa.topk_w = r.topk_w; sa.rank = r.rank;
-  sa.block_counts = r.block_counts;
+  // 3: selection (the split path's logits stay in plog: no logits output)
+  SelectArgs sa = select_args(r, r.dtype == 1 ? r.ds : 1);
+  sa.logits = nullptr;
   const dim3 grid((r.T + 63) / 64);
   const size_t lds = (size_t)64 * (r.E + 1) * sizeof(float);
-  if (r.K <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, dim3(512), lds, s, sa);
-  else hipLaunchKernelGGL(select_kernel<MAX_TOPK>, grid, dim3(512), lds, s, sa);
+  if (r.K <= 8) hipLaunchKernelGGL((select_kernel<8, 64>), grid, dim3(512), lds, s, sa);
+  else hipLaunchKernelGGL((select_kernel<MAX_TOPK, 64>), grid, dim3(512), lds, s, sa);
   return hipGetLastError();
 }
 
