@@ -42,6 +42,90 @@ using namespace gemm;
 
 constexpr int BK = 64;    // k per stage (8 chunks of 16 B)
 
+// Epilogue of the down-projection tiles (DOWN, DOWN_SHARED) from the
+// accumulators of a wave's WM x WN sub-tile: acc[nb][mb][r] = D[n][m] with
+// n = nb*32 + 8*(r/4) + 4*hi + (r%4) and m = mb*32 + l32 inside it.
+template <int MODE, int MB, int NB, int WM, int WN>
+__device__ __forceinline__ void down_epilogue(const GemmArgs& a, const f32x16 (&acc)[NB][MB],
+                                              int row0, int rows, int n0, int wm, int wn,
+                                              int l32, int hi) {
+  if constexpr (MODE == 1) {
+    // Y rows in fp16, each 64-column group of a row scaled so that its
+    // largest magnitude lands just below 2^15; the inverse scales go to
+    // yscale[row][col / 64].  The group's columns are column blocks
+    // nb = 2 gi, 2 gi + 1 of this lane and of lane ^ 32 (same row).
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    const int gpr = a.d / Y_GROUP;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = wm * WM + mb * 32 + l32;
+#pragma unroll
+      for (int gi = 0; gi < NB / 2; ++gi) {
+        float amax = 0.f;
+#pragma unroll
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[nb][mb][r]));
+        amax = max_halves(amax);
+        float sc, inv;
+        y_scale_of(amax, sc, inv);
+        if (m >= rows) continue;
+        uint16_t* orow = out + (size_t)(row0 + m) * a.ldo;
+#pragma unroll
+        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
+          // d is a multiple of 64: a 32-column block is all in or all out.
+          const int n = n0 + wn * WN + nb * 32;
+          if (n >= a.d) continue;
+          uint32_t p[4][2];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            p[g][0] = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
+            p[g][1] = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
+          }
+          swap_halves(p);
+          store_block(orow + n + 8 * hi, p);
+        }
+        const int ng = n0 + wn * WN + gi * Y_GROUP;
+        if (hi == 0 && ng < a.d) a.yscale[(size_t)(row0 + m) * gpr + ng / Y_GROUP] = inv;
+      }
+    }
+  } else {
+    // Shared experts' down-projection: S = x + sum_s H_s W2_s^T in fp32
+    // (the residual and the shared experts; the combine adds the kept
+    // experts).  The rows of x are read in 16-byte chunks, 8 consecutive
+    // columns per lane, then swapped into the accumulator layout (a block
+    // past d reads the row's last block; its values are never stored).
+    const bf16_t* x = static_cast<const bf16_t*>(a.x);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int m = wm * WM + mb * 32 + l32;
+      if (m >= rows) continue;
+      const int t = row0 + m;
+      const bf16_t* xrow = x + (size_t)t * a.d;
+      float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int cblk = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
+        uint32_t p[4][2];
+        load_block(xrow + cblk, p);
+        swap_halves(p);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
+          if (n >= a.d) continue;
+          *reinterpret_cast<float4*>(srow + n) = make_float4(
+              bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0],
+              bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1],
+              bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2],
+              bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3]);
+        }
+      }
+    }
+  }
+}
+
 // One tile: rows [row0, row0 + rows) (at most BM) of the M dimension (expert
 // e for routed tiles) times N-tile nt, through the LDS buffers As0/As1 (at
 // least BM x 128 B each) and Bs0/Bs1.  MODE 0 GATEUP, 1 DOWN, 2 DOWN_SHARED,
@@ -366,81 +450,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int row0, int rows,
         a.dg_part[(size_t)(row0 + m) * a.n_part + nt] = sum;
       }
     }
-  } else if (MODE == 1) {
-    // Y rows in fp16, each 64-column group of a row scaled so that its
-    // largest magnitude lands just below 2^15; the inverse scales go to
-    // yscale[row][col / 64].  The group's columns are column blocks
-    // nb = 2 gi, 2 gi + 1 of this lane and of lane ^ 32 (same row).
-    uint16_t* out = static_cast<uint16_t*>(a.out);
-    const int gpr = a.d / Y_GROUP;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int m = wm * WM + mb * 32 + l32;
-#pragma unroll
-      for (int gi = 0; gi < NB / 2; ++gi) {
-        float amax = 0.f;
-#pragma unroll
-        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[nb][mb][r]));
-        amax = max_halves(amax);
-        float sc, inv;
-        y_scale_of(amax, sc, inv);
-        if (m >= rows) continue;
-        uint16_t* orow = out + (size_t)(row0 + m) * a.ldo;
-#pragma unroll
-        for (int nb = 2 * gi; nb < 2 * gi + 2; ++nb) {
-          // d is a multiple of 64: a 32-column block is all in or all out.
-          const int n = n0 + wn * WN + nb * 32;
-          if (n >= a.d) continue;
-          uint32_t p[4][2];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            p[g][0] = pack_h2(acc[nb][mb][4 * g + 0] * sc, acc[nb][mb][4 * g + 1] * sc);
-            p[g][1] = pack_h2(acc[nb][mb][4 * g + 2] * sc, acc[nb][mb][4 * g + 3] * sc);
-          }
-          swap_halves(p);
-          store_block(orow + n + 8 * hi, p);
-        }
-        const int ng = n0 + wn * WN + gi * Y_GROUP;
-        if (hi == 0 && ng < a.d) a.yscale[(size_t)(row0 + m) * gpr + ng / Y_GROUP] = inv;
-      }
-    }
   } else {
-    // Shared experts' down-projection: S = x + sum_s H_s W2_s^T in fp32
-    // (the residual and the shared experts; the combine adds the kept
-    // experts).  The rows of x are read in 16-byte chunks, 8 consecutive
-    // columns per lane, then swapped into the accumulator layout (a block
-    // past d reads the row's last block; its values are never stored).
-    const bf16_t* x = static_cast<const bf16_t*>(a.x);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int m = wm * WM + mb * 32 + l32;
-      if (m >= rows) continue;
-      const int t = row0 + m;
-      const bf16_t* xrow = x + (size_t)t * a.d;
-      float* srow = static_cast<float*>(a.out) + (size_t)t * a.ldo;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int cblk = min(n0 + wn * WN + nb * 32, a.d - 32) + 8 * hi;
-        uint32_t p[4][2];
-        load_block(xrow + cblk, p);
-        swap_halves(p);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + nb * 32 + 8 * g + 4 * hi;
-          if (n >= a.d) continue;
-          *reinterpret_cast<float4*>(srow + n) = make_float4(
-              bf16_to_f32((bf16_t)(p[g][0] & 0xffff)) + acc[nb][mb][4 * g + 0],
-              bf16_to_f32((bf16_t)(p[g][0] >> 16)) + acc[nb][mb][4 * g + 1],
-              bf16_to_f32((bf16_t)(p[g][1] & 0xffff)) + acc[nb][mb][4 * g + 2],
-              bf16_to_f32((bf16_t)(p[g][1] >> 16)) + acc[nb][mb][4 * g + 3]);
-        }
-      }
-    }
+    down_epilogue<MODE, MB, NB, WM, WN>(a, acc, row0, rows, n0, wm, wn, l32, hi);
   }
+}
+
+// Tile `blk` of `nblk` of a stage-MODE part: M-tile mt, N-tile nt; false
+// for the padding blocks.  Routed launches are sized for the most M-tiles any
+// routing can make; the tiles are numbered over the M-tiles the routing did
+// make, so the blocks past them (which exit at once) are the last ones and
+// every XCD gets an equal share of real tiles.
+// Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
+// one M-tile are adjacent, then the next M-tile (same expert, same weight
+// tiles).  A run of adjacent tiles (one XCD's resident set) then shares both
+// its token-row tiles and its weight tiles in L2.
+template <int MODE, int BM>
+__device__ __forceinline__ bool tile_of(const GemmArgs& a, int blk, int nblk, int& mt,
+                                        int& nt) {
+  const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
+  const int mdim = routed ? *a.n_tiles : (a.T + BM - 1) / BM;
+  const int ndim = n_tiles_of<MODE, BM>(a);
+  const int ntl = mdim * ndim;
+  const int L = !routed ? xcd_remap(blk, nblk) : (blk < ntl ? xcd_remap(blk, ntl) : ntl);
+  if (L >= ntl) return false;                // padding
+  constexpr int NGRP = ngrp_for<BM>();
+  const int full = ndim / NGRP;
+  const int ntg = L / (mdim * NGRP);
+  const int g = (ntg < full) ? NGRP : ndim - full * NGRP;
+  const int rem = L - ntg * mdim * NGRP;
+  mt = rem / g;
+  nt = ntg * NGRP + rem % g;
+  return true;
 }
 
 // One part of a grouped GEMM launch: block `blk` of `nblk` runs one tile of
@@ -451,32 +491,28 @@ __device__ __forceinline__ void gemm_part(const GemmArgs& a, int blk, int nblk, 
                                           u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
                                           u32x4* Bs2, float* red) {
   const bool routed = !(MODE == 2 || (is_gateup<MODE>() && a.shared));
-  // Routed launches are sized for the most M-tiles any routing can make; the
-  // tiles are numbered over the M-tiles the routing did make, so the blocks
-  // past them (which exit at once) are the last ones and every XCD gets an
-  // equal share of real tiles.
-  const int mdim = routed ? *a.n_tiles : (a.T + BM - 1) / BM;
-  // Tile order: N-tiles in groups of NGRP; inside a group the NGRP N-tiles of
-  // one M-tile are adjacent, then the next M-tile (same expert, same weight
-  // tiles).  A run of adjacent tiles (one XCD's resident set) then shares
-  // both its token-row tiles and its weight tiles in L2.
-  const int ndim = n_tiles_of<MODE, BM>(a);
-  const int ntl = mdim * ndim;
-  const int L = !routed ? xcd_remap(blk, nblk) : (blk < ntl ? xcd_remap(blk, ntl) : ntl);
-  if (L >= ntl) return;                      // padding
   int mt, nt;
-  constexpr int NGRP = ngrp_for<BM>();
-  {
-    const int full = ndim / NGRP;
-    const int ntg = L / (mdim * NGRP);
-    const int g = (ntg < full) ? NGRP : ndim - full * NGRP;
-    const int rem = L - ntg * mdim * NGRP;
-    mt = rem / g;
-    nt = ntg * NGRP + rem % g;
-  }
+  if (!tile_of<MODE, BM>(a, blk, nblk, mt, nt)) return;
   if (routed) {
     const MTile t = a.tiles[mt];
-    if constexpr (BM >= 128) {
+    if constexpr (BM == 256) {
+      // An expert's last tile at 64-row granularity: 64, 128 or 192 rows.
+      if (t.rows <= 64) {
+        gemm_tile<MODE, 64, NW / 4, NS, NW>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2,
+                                            Bs0, Bs1, Bs2, red);
+        return;
+      }
+      if (t.rows <= 128) {
+        gemm_tile<MODE, 128, NW / 4, NS, NW>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2,
+                                             Bs0, Bs1, Bs2, red);
+        return;
+      }
+      if (t.rows <= 192) {
+        gemm_tile<MODE, 192, 2, NS, NW>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0,
+                                        Bs1, Bs2, red);
+        return;
+      }
+    } else if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
         gemm_tile<MODE, BM / 2, NW / 4, NS, NW>(a, t.row0, t.rows, t.expert, nt, As0, As1,
                                                 As2, Bs0, Bs1, Bs2, red);
@@ -506,6 +542,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a, GemmA
   // Tiles of at most 128 rows stream their weights and keep three stages
   // in flight-or-compute (3 x (BM + 256) x 128 B <= 144 KB of LDS).
   constexpr int NS = (BM <= 128) ? 3 : 2;
+  const int blk = blockIdx.x;
   __shared__ u32x4 As0[BM * 8], As1[BM * 8], As2[NS == 3 ? BM * 8 : 1];
   __shared__ u32x4 Bs0[BN * 8], Bs1[BN * 8], Bs2[NS == 3 ? BN * 8 : 1];
   // Row sums of GATEUP_BWD (the A buffers are free by the epilogue, but a
@@ -513,7 +550,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(GemmArgs a, GemmA
   __shared__ float red[MODE == 3 ? 4 * BM : 1];
   // Each part reads its own argument struct (a run-time choice of struct
   // made the compiler copy both to scratch memory).
-  const int blk = blockIdx.x;
   if (blk >= a_blocks)
     gemm_part<MODE_B, BM, WAVES_M, NW, NS>(b, blk - a_blocks, (int)gridDim.x - a_blocks, As0,
                                            As1, As2, Bs0, Bs1, Bs2, red);
@@ -554,14 +590,14 @@ void launch_bm(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
   constexpr int NWG = (BM == 256) ? 8 : 4;
   if (a.mode == 0) launch_pair<0, 0, BM, WAVES_M, NWG>(a, b, s);
   else if (a.mode == 1) launch_pair<1, 2, BM, WAVES_M, 4>(a, b, s);
-  else if (a.mode == 2) launch_pair<2, 2, BM, WAVES_M, 4>(a, nullptr, s);
   else launch_pair<3, 3, BM, WAVES_M, NWG>(a, b, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, const GemmArgs* b) {
-  if (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode) || a.mode == 2))
+  // DOWN_SHARED runs only as the second part of a DOWN launch.
+  if (a.mode == 2 || (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode))))
     return hipErrorInvalidValue;
   switch (a.bm) {
     case 256: launch_bm<256, 2>(a, b, s); break;
