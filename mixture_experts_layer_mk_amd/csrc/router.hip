@@ -367,13 +367,14 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, const float* l
   }
 }
 
-// TB tokens per block (64, or 16 for the small-batch path), 8 TB threads.
-template <int KMAX, int TB>
+// TB tokens per block (64, or 16 for the small-batch path), 8 TB threads,
+// at most EMAX experts (a lane holds EMAX / 8 of them in registers).
+template <int KMAX, int TB, int EMAX>
 __global__ __launch_bounds__(TB * 8) void select_kernel(SelectArgs a) {
   extern __shared__ float lg[];               // [TB][E + 1]: logits, then scores
-  __shared__ unsigned long long masks[MAX_EXPERTS];
+  __shared__ unsigned long long masks[EMAX];
   __shared__ float gsc[TB][MAX_GROUPS + 1];
-  __shared__ float sbias[MAX_EXPERTS];        // selection bias (0 without one)
+  __shared__ float sbias[EMAX];               // selection bias (0 without one)
   const int tid = threadIdx.x;
   const int t0 = blockIdx.x * TB;
   const int E = a.E, K = a.K, ld = E + 1;
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(TB * 8) void select_kernel(SelectArgs a) {
     }
   }
   __syncthreads();
-  select_block<KMAX, MAX_EXPERTS, TB>(a, lg, ld, t0, ntok, masks, gsc, sbias);
+  select_block<KMAX, EMAX, TB>(a, lg, ld, t0, ntok, masks, gsc, sbias);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,7 +723,7 @@ __global__ __launch_bounds__(256) void router_fused_kernel(RouterArgs a) {
 // split into its bf16 parts in registers, one quarter of the slice per wave,
 // with every load of a wave in flight at once, and stores the slice's
 // partial logits (its four waves added in order) as the split path's plog.
-// select_kernel<K, 16> then adds the slices in order and selects.  (A single
+// select_kernel<K, 16, 64> then adds the slices in order and selects.  (A single
 // kernel in which the last workgroup of a block went on to select, after a
 // ticket between release and acquire fences, spent 15 us of 28 in the
 // fences and the hand-off.)
@@ -888,11 +889,12 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
     hipLaunchKernelGGL(logits_small_kernel, dim3(nblk, ds), dim3(SR_WAVES * 64), 0, s, r);
     SelectArgs sa = select_args(r, ds);
     const size_t lds = (size_t)SR_TOK * (r.E + 1) * sizeof(float);
-    if (r.K <= 8)
-      hipLaunchKernelGGL((select_kernel<8, SR_TOK>), dim3(nblk), dim3(SR_TOK * 8), lds, s, sa);
-    else
-      hipLaunchKernelGGL((select_kernel<MAX_TOPK, SR_TOK>), dim3(nblk), dim3(SR_TOK * 8), lds, s,
+    if (r.K <= 8)   // at most 64 experts on this path
+      hipLaunchKernelGGL((select_kernel<8, SR_TOK, 64>), dim3(nblk), dim3(SR_TOK * 8), lds, s,
                          sa);
+    else
+      hipLaunchKernelGGL((select_kernel<MAX_TOPK, SR_TOK, 64>), dim3(nblk), dim3(SR_TOK * 8), lds,
+                         s, sa);
     return hipGetLastError();
   }
   if (router_fused(r.T, r.E, r.K, r.n_groups, r.dtype)) {
@@ -936,8 +938,14 @@ hipError_t launch_router(const RouterArgs& r, hipStream_t s) {
   sa.logits = nullptr;
   const dim3 grid((r.T + 63) / 64);
   const size_t lds = (size_t)64 * (r.E + 1) * sizeof(float);
-  if (r.K <= 8) hipLaunchKernelGGL((select_kernel<8, 64>), grid, dim3(512), lds, s, sa);
-  else hipLaunchKernelGGL((select_kernel<MAX_TOPK, 64>), grid, dim3(512), lds, s, sa);
+  if (r.E <= 64) {
+    if (r.K <= 8) hipLaunchKernelGGL((select_kernel<8, 64, 64>), grid, dim3(512), lds, s, sa);
+    else hipLaunchKernelGGL((select_kernel<MAX_TOPK, 64, 64>), grid, dim3(512), lds, s, sa);
+  } else if (r.K <= 8) {
+    hipLaunchKernelGGL((select_kernel<8, 64, MAX_EXPERTS>), grid, dim3(512), lds, s, sa);
+  } else {
+    hipLaunchKernelGGL((select_kernel<MAX_TOPK, 64, MAX_EXPERTS>), grid, dim3(512), lds, s, sa);
+  }
   return hipGetLastError();
 }
 
