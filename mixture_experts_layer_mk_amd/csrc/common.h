@@ -101,7 +101,6 @@ bool router_fused(int T, int E, int K, int n_groups, int dtype);
 bool router_small(int T, int E, int d, int dtype);
 int router_small_slices(int d);
 
-hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s);
 
 struct PermuteArgs {
@@ -110,6 +109,10 @@ struct PermuteArgs {
   const int32_t* offsets; int32_t* slot_row; int32_t* row_src;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// The dispatch scan; with `p`, also the permute in the same launch (at most
+// SCAN_PERMUTE_MAX_SLOTS slots T K).
+constexpr int64_t SCAN_PERMUTE_MAX_SLOTS = 8192;
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s, const PermuteArgs* p = nullptr);
 
 // Grouped GEMM stages.
 //  GATEUP : H[r][c] = silu(A W1^T) * (A W3^T)   A = xp rows (routed) or x (shared)

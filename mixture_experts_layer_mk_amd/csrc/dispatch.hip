@@ -137,19 +137,32 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanArgs a) {
   dispatch_scan<SCAN_THREADS>(a);
 }
 
-// One thread per (token, slot): the slot's row is the expert's first row,
-// plus the rows of the expert in earlier router blocks, plus the slot's rank
-// among the expert's slots in its own block (token order).  Writes the two
-// row maps.
-__global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  if (q >= a.T * a.K) return;
+// Slot q = (token, slot): its row is the expert's first row, plus the rows
+// of the expert in earlier router blocks, plus the slot's rank among the
+// expert's slots in its own block (token order).  Writes the two row maps.
+__device__ __forceinline__ void permute_slot(const PermuteArgs& a, int q) {
   const int t = q / a.K;
   const int b = t / a.rt;
   const int e = a.topk_idx[q];
   const int row = a.offsets[e] + a.block_base[(size_t)b * a.E + e] + a.rank[q];
   a.slot_row[q] = row;
   a.row_src[row] = t;
+}
+
+// One thread per slot.
+__global__ __launch_bounds__(256) void permute_kernel(PermuteArgs a) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q < a.T * a.K) permute_slot(a, q);
+}
+
+// Small batches: the scan, then the permute by the same workgroup (one
+// launch fewer on a latency-bound path).  The barrier makes the scan's
+// offsets and block bases, written to global memory, visible to the
+// workgroup's threads.
+__global__ __launch_bounds__(SCAN_THREADS) void scan_permute_kernel(ScanArgs a, PermuteArgs p) {
+  dispatch_scan<SCAN_THREADS>(a);
+  __syncthreads();
+  for (int q = threadIdx.x; q < p.T * p.K; q += SCAN_THREADS) permute_slot(p, q);
 }
 
 // counts[0 .. n) = 0 (a forward with no tokens still reports its counts).
@@ -166,8 +179,10 @@ hipError_t launch_zero_counts(int32_t* counts, int n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s, const PermuteArgs* p) {
+  if (p && (int64_t)p->T * p->K > SCAN_PERMUTE_MAX_SLOTS) return hipErrorInvalidValue;
+  if (p) hipLaunchKernelGGL(scan_permute_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a, *p);
+  else hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -271,8 +271,18 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
     MOE_CHECK(launch_router(r, s));
     if (fp8) MOE_CHECK(quant_x_rows(d, L, ws, x, s));
   }
-  // 2. scan + tile schedule
+  // 2. scan + tile schedule; 3. permute (small batches: in the scan's launch)
   if (!mark(1)) return MOE_ERR_HIP;
+  PermuteArgs p{};
+  p.T = d.T; p.K = d.top_k; p.E = d.n_routed;
+  p.rt = router_tokens_per_block(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
+  p.nblk = L.nblk;
+  p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
+  p.block_base = static_cast<const int32_t*>(at(L.block_base));
+  p.offsets = static_cast<const int32_t*>(at(L.offsets));
+  p.slot_row = static_cast<int32_t*>(at(L.slot_row));
+  p.row_src = static_cast<int32_t*>(at(L.row_src));
+  const bool fuse = (int64_t)d.T * d.top_k <= SCAN_PERMUTE_MAX_SLOTS;
   {
     ScanArgs c{};
     c.block_counts = static_cast<const int32_t*>(at(L.block_counts));
@@ -283,22 +293,10 @@ moe_status_t route_dispatch(const moe_layer_desc_t& d, const Layout& L, char* ws
     c.tiles = static_cast<MTile*>(at(L.tiles));
     c.n_tiles = static_cast<int32_t*>(at(L.n_tiles));
     c.nblk = L.nblk; c.E = d.n_routed; c.bm = L.bm;
-    MOE_CHECK(launch_scan(c, s));
+    MOE_CHECK(launch_scan(c, s, fuse ? &p : nullptr));
   }
-  // 3. permute
   if (!mark(2)) return MOE_ERR_HIP;
-  {
-    PermuteArgs p{};
-    p.T = d.T; p.K = d.top_k; p.E = d.n_routed;
-    p.rt = router_tokens_per_block(d.T, d.n_routed, d.d, bf16 ? 1 : 0);
-    p.nblk = L.nblk;
-    p.topk_idx = idx; p.rank = static_cast<const int32_t*>(at(L.rank));
-    p.block_base = static_cast<const int32_t*>(at(L.block_base));
-    p.offsets = static_cast<const int32_t*>(at(L.offsets));
-    p.slot_row = static_cast<int32_t*>(at(L.slot_row));
-    p.row_src = static_cast<int32_t*>(at(L.row_src));
-    MOE_CHECK(launch_permute(p, s));
-  }
+  if (!fuse) MOE_CHECK(launch_permute(p, s));
 #undef MOE_CHECK
   return MOE_OK;
 }
