@@ -35,7 +35,8 @@
  *  - moe_layer_forward* are asynchronous: they enqueue kernels on `stream`
  *    (a hipStream_t, NULL = the null stream) and return without waiting.
  *    The forward enqueues, in order: the router, the dispatch scan, the row
- *    maps, one grouped gate/up GEMM launch over the routed experts' tiles
+ *    maps (in the scan's launch when T * top_k <= 8192), one grouped gate/up
+ *    GEMM launch over the routed experts' tiles
  *    and the shared experts', one grouped down-projection launch (routed
  *    rows and the shared experts' sum), and the combine.
  *  - Validation errors are returned before anything is enqueued.  A failed
@@ -233,7 +234,8 @@ const char* moe_layer_trace_stage_name(int32_t i);
 /* moe_layer_forward, with hipEvent_t events[i] recorded on `stream` before
  * stage i and events[n] after the last stage (n = stage count: router, scan,
  * permute, gemm_gateup, gemm_down, combine), so the caller can time every
- * stage.  `events` holds n + 1 created events (MOE_ERR_INVALID_ARG if
+ * stage (the permute stage is empty when the scan's launch writes the row
+ * maps).  `events` holds n + 1 created events (MOE_ERR_INVALID_ARG if
  * n_events is smaller).  The same launches as the untraced call; the
  * results are bitwise equal.  Otherwise identical. */
 moe_status_t moe_layer_forward_traced(
