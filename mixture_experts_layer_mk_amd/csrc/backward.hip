@@ -169,81 +169,146 @@ __global__ __launch_bounds__(256) void gate_grad_sum_kernel(BwdAuxArgs a) {
   a.dw_gate[i] = a.dwg_part[i] + a.dwg_part[(size_t)(a.ldp / 2) * a.d + i];
 }
 
-// dx = RNE(dy + dx_shared + sum_k dx_rows[slot_row[t][k]] + dl Wg): thread =
-// columns 4 j .. 4 j + 3, DX_T tokens per workgroup.  The router term first
-// (each 4-column group of Wg read once per workgroup, the tokens' dl rows
-// staged in LDS), then the row sums, in a fixed order.  Eight tokens per
-// workgroup (measured on the 16B-shaped backward: 0.185 ms against 0.202
-// with four, 0.224 with sixteen, 0.295 with 32: the router term's registers
-// limit the waves in flight).
-constexpr int DX_T = 8;
-__device__ __forceinline__ void add_bf16x4(float* v, uint2 p) {
-  v[0] += __uint_as_float(p.x << 16);
-  v[1] += __uint_as_float(p.x & 0xffff0000u);
-  v[2] += __uint_as_float(p.y << 16);
-  v[3] += __uint_as_float(p.y & 0xffff0000u);
+// dx = RNE(dy + dx_shared + sum_k dx_rows[slot_row[t][k]] + dl Wg), one
+// workgroup (4 waves) per 32 tokens x 256 columns:
+//  a. the router term r = dl Wg on the matrix cores (32 x 32 x 16 bf16): wave
+//     w takes the tile's columns 64 w .. 64 w + 63 for its 32 tokens, over the
+//     experts in steps of 16.  dl enters as its bf16 hi and lo parts (written
+//     by the router backward, |dl - hi - lo| < 2^-16 |dl|), Wg as its hi and
+//     mid parts split here (|w - hi - mid| < 2^-16 |w|); the three products
+//     hi hi, mid hi and hi lo carry r to about 2^-15 of its terms' size,
+//     far below the bf16 rounding of dx.  r goes to LDS.
+//  b. the row sums: dy, dx_shared, then the kept experts' rows in slot
+//     order, 8 columns (16 bytes) per lane and four tokens per lane (their
+//     loads of a slot in flight together), and one rounding of sum + r.
+// The router term's Wg reads (64 KB per workgroup) are shared by 32 tokens.
+// Measured on the 16B-shaped backward: 0.183 ms for the stage with the
+// router term as fp32 FMAs (each workgroup reading all of Wg's columns for 8
+// tokens), 0.164 with this layout at two tokens per lane, 0.156 at four;
+// loading four slots' row indices and rows together was slower (0.182).
+constexpr int DX_T = 32, DX_C = 256;
+
+// Two floats to packed bf16, round to nearest even.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+__device__ __forceinline__ void add_bf16x8(float* v, uint4 p) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] += __uint_as_float(w[i] << 16);
+    v[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
 __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
-  __shared__ float sdl[DX_T][MAX_EXPERTS];
-  const int t0 = blockIdx.x * DX_T;
-  const int j = (blockIdx.y * 256 + threadIdx.x) * 4;
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  constexpr int RP = DX_C + 4;                  // LDS row pitch (floats)
+  __shared__ float rt[DX_T * RP];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int t0 = blockIdx.x * DX_T, c0 = blockIdx.y * DX_C;
   const int nt = min(DX_T, a.T - t0);
-  for (int i = threadIdx.x; i < DX_T * a.E; i += 256) {
-    const int tt = i / a.E, e = i % a.E;
-    sdl[tt][e] = (tt < nt) ? a.dl[(size_t)(t0 + tt) * a.E + e] : 0.f;
+  const int half = a.ldp / 2;                   // dl parts' columns (E rounded up to 4, zero pad)
+
+  // a. router term
+  {
+    f32x16_t acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+    const bf16_t* dh = a.dlp + (size_t)(t0 + min(l32, nt - 1)) * a.ldp;
+    const int cw = c0 + wave * 64;
+    for (int e0 = 0; e0 < a.E; e0 += 16) {
+      const int ek = e0 + 8 * hi;               // this lane's 8 experts
+      uint4 ph = make_uint4(0, 0, 0, 0), pl = ph;
+      if (ek + 8 <= half) {
+        ph = *reinterpret_cast<const uint4*>(dh + ek);
+        pl = *reinterpret_cast<const uint4*>(dh + half + ek);
+      } else if (ek + 4 <= half) {
+        const uint2 h2 = *reinterpret_cast<const uint2*>(dh + ek);
+        const uint2 l2 = *reinterpret_cast<const uint2*>(dh + half + ek);
+        ph.x = h2.x; ph.y = h2.y; pl.x = l2.x; pl.y = l2.y;
+      }
+      const bf16x8_t fh = __builtin_bit_cast(bf16x8_t, ph);
+      const bf16x8_t fl = __builtin_bit_cast(bf16x8_t, pl);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int c = min(cw + nb * 32 + l32, a.d - 1);
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          w[i] = (ek + i < a.E) ? a.w_gate[(size_t)(ek + i) * a.d + c] : 0.f;
+        uint32_t wh[4], wm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wh[i] = bf16x2_rne(w[2 * i], w[2 * i + 1]);
+          const float r0 = w[2 * i] - __uint_as_float(wh[i] << 16);
+          const float r1 = w[2 * i + 1] - __uint_as_float(wh[i] & 0xffff0000u);
+          wm[i] = bf16x2_rne(r0, r1);
+        }
+        const bf16x8_t gh = __builtin_bit_cast(bf16x8_t, make_uint4(wh[0], wh[1], wh[2], wh[3]));
+        const bf16x8_t gm = __builtin_bit_cast(bf16x8_t, make_uint4(wm[0], wm[1], wm[2], wm[3]));
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, fh, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gm, fh, acc[nb], 0, 0, 0);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, fl, acc[nb], 0, 0, 0);
+      }
+    }
+    // acc[nb][r] = r[token l32][column 64 wave + 32 nb + 8 (r / 4) + 4 hi + r % 4]
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(&rt[l32 * RP + wave * 64 + nb * 32 + 8 * g + 4 * hi]) =
+            make_float4(acc[nb][4 * g], acc[nb][4 * g + 1], acc[nb][4 * g + 2],
+                        acc[nb][4 * g + 3]);
   }
   __syncthreads();
-  if (j >= a.d) return;   // d is a multiple of 4
-  float r[DX_T][4];
+
+  // b. row sums: lane group (tid & 31) takes columns 8 (tid & 31) .., row
+  // group tid >> 5 the tokens tid / 32 + 8 i
+  const int cl = (tid & 31) * 8, j = c0 + cl;
+  if (j >= a.d) return;   // d is a multiple of 64
+  const int tr = tid >> 5;
+  constexpr int NQ = DX_T / 8;   // tokens per lane
 #pragma unroll
-  for (int tt = 0; tt < DX_T; ++tt)
+  for (int i0 = 0; i0 < DX_T / 8; i0 += NQ) {
+    float v[NQ][8];
+    int tt[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[tt][q] = 0.f;
-  for (int e = 0; e < a.E; ++e) {
-    const float4 w = *reinterpret_cast<const float4*>(a.w_gate + (size_t)e * a.d + j);
+    for (int q = 0; q < NQ; ++q) {
+      tt[q] = tr + 8 * (i0 + q);
+      const size_t t = (size_t)(t0 + min(tt[q], nt - 1));
 #pragma unroll
-    for (int tt = 0; tt < DX_T; ++tt) {
-      const float l = sdl[tt][e];
-      r[tt][0] = fmaf(l, w.x, r[tt][0]);
-      r[tt][1] = fmaf(l, w.y, r[tt][1]);
-      r[tt][2] = fmaf(l, w.z, r[tt][2]);
-      r[tt][3] = fmaf(l, w.w, r[tt][3]);
-    }
-  }
-  // four tokens at a time, their rows' loads issued together
-#pragma unroll
-  for (int t4 = 0; t4 < DX_T; t4 += 4) {
-    float v[4][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tt = t4 + q;
-      const size_t t = (size_t)(t0 + min(tt, nt - 1));
-      v[q][0] = v[q][1] = v[q][2] = v[q][3] = 0.f;
-      add_bf16x4(v[q], *reinterpret_cast<const uint2*>(a.dy + t * a.d + j));
+      for (int c = 0; c < 8; ++c) v[q][c] = 0.f;
+      add_bf16x8(v[q], *reinterpret_cast<const uint4*>(a.dy + t * a.d + j));
       if (a.dx_shared)
-        add_bf16x4(v[q], *reinterpret_cast<const uint2*>(a.dx_shared + t * a.d + j));
+        add_bf16x8(v[q], *reinterpret_cast<const uint4*>(a.dx_shared + t * a.d + j));
     }
     for (int k = 0; k < a.K; ++k) {
-      uint2 p[4];
+      uint4 p[NQ];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const size_t t = (size_t)(t0 + min(t4 + q, nt - 1));
+      for (int q = 0; q < NQ; ++q) {
+        const size_t t = (size_t)(t0 + min(tt[q], nt - 1));
         const size_t row = (size_t)a.slot_row[t * a.K + k];
-        p[q] = *reinterpret_cast<const uint2*>(a.dx_rows + row * a.d + j);
+        p[q] = *reinterpret_cast<const uint4*>(a.dx_rows + row * a.d + j);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) add_bf16x4(v[q], p[q]);
+      for (int q = 0; q < NQ; ++q) add_bf16x8(v[q], p[q]);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tt = t4 + q;
-      if (tt >= nt) continue;
-      uint2 o;
-      o.x = (uint32_t)f32_to_bf16(v[q][0] + r[tt][0]) |
-            ((uint32_t)f32_to_bf16(v[q][1] + r[tt][1]) << 16);
-      o.y = (uint32_t)f32_to_bf16(v[q][2] + r[tt][2]) |
-            ((uint32_t)f32_to_bf16(v[q][3] + r[tt][3]) << 16);
-      *reinterpret_cast<uint2*>(a.dx + (size_t)(t0 + tt) * a.d + j) = o;
+    for (int q = 0; q < NQ; ++q) {
+      if (tt[q] >= nt) continue;
+      const float* r = &rt[tt[q] * RP + cl];
+      uint4 o;
+      o.x = bf16x2_rne(v[q][0] + r[0], v[q][1] + r[1]);
+      o.y = bf16x2_rne(v[q][2] + r[2], v[q][3] + r[3]);
+      o.z = bf16x2_rne(v[q][4] + r[4], v[q][5] + r[5]);
+      o.w = bf16x2_rne(v[q][6] + r[6], v[q][7] + r[7]);
+      *reinterpret_cast<uint4*>(a.dx + (size_t)(t0 + tt[q]) * a.d + j) = o;
     }
   }
 }
@@ -302,7 +367,7 @@ hipError_t launch_gate_grad(const BwdAuxArgs& a, hipStream_t s) {
 
 hipError_t launch_dx_combine(const BwdAuxArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid((a.T + DX_T - 1) / DX_T, (a.d + 1023) / 1024);
+  const dim3 grid((a.T + DX_T - 1) / DX_T, (a.d + DX_C - 1) / DX_C);
   hipLaunchKernelGGL(dx_combine_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
