@@ -192,6 +192,12 @@ constexpr int DX_T = 32, DX_C = 256;
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
+// Non-temporal 16-byte load and store (the dx combine streams its rows once).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+  const u32x4_nt q = __builtin_nontemporal_load(static_cast<const u32x4_nt*>(p));
+  return make_uint4(q.x, q.y, q.z, q.w);
+}
 __device__ __forceinline__ void add_bf16x8(float* v, uint4 p) {
   const uint32_t w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
@@ -284,9 +290,8 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
       const size_t t = (size_t)(t0 + min(tt[q], nt - 1));
 #pragma unroll
       for (int c = 0; c < 8; ++c) v[q][c] = 0.f;
-      add_bf16x8(v[q], *reinterpret_cast<const uint4*>(a.dy + t * a.d + j));
-      if (a.dx_shared)
-        add_bf16x8(v[q], *reinterpret_cast<const uint4*>(a.dx_shared + t * a.d + j));
+      add_bf16x8(v[q], ld_nt(a.dy + t * a.d + j));
+      if (a.dx_shared) add_bf16x8(v[q], ld_nt(a.dx_shared + t * a.d + j));
     }
     for (int k = 0; k < a.K; ++k) {
       uint4 p[NQ];
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
       for (int q = 0; q < NQ; ++q) {
         const size_t t = (size_t)(t0 + min(tt[q], nt - 1));
         const size_t row = (size_t)a.slot_row[t * a.K + k];
-        p[q] = *reinterpret_cast<const uint4*>(a.dx_rows + row * a.d + j);
+        p[q] = ld_nt(a.dx_rows + row * a.d + j);
       }
 #pragma unroll
       for (int q = 0; q < NQ; ++q) add_bf16x8(v[q], p[q]);
@@ -308,7 +313,8 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(BwdAuxArgs a) {
       o.y = bf16x2_rne(v[q][2] + r[2], v[q][3] + r[3]);
       o.z = bf16x2_rne(v[q][4] + r[4], v[q][5] + r[5]);
       o.w = bf16x2_rne(v[q][6] + r[6], v[q][7] + r[7]);
-      *reinterpret_cast<uint4*>(a.dx + (size_t)(t0 + tt[q]) * a.d + j) = o;
+      __builtin_nontemporal_store(u32x4_nt{o.x, o.y, o.z, o.w},
+                                  reinterpret_cast<u32x4_nt*>(a.dx + (size_t)(t0 + tt[q]) * a.d + j));
     }
   }
 }
