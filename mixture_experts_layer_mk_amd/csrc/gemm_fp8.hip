@@ -443,6 +443,14 @@ __device__ __forceinline__ void gemm8_part(const GemmArgs& a, int blk, int nblk,
   }
   if (routed) {
     const MTile t = a.tiles[mt];
+    if constexpr (BM == 256) {
+      // an expert's last rows: 64-row layout for at most 64 of them
+      if (t.rows <= 64) {
+        gemm8_tile<MODE, 64, 1, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0, Bs1,
+                                    Bs2, sA, sB, gmax);
+        return;
+      }
+    }
     if constexpr (BM >= 128) {
       if (t.rows <= BM / 2) {
         gemm8_tile<MODE, BM / 2, 1, NS>(a, t.row0, t.rows, t.expert, nt, As0, As1, As2, Bs0,
@@ -508,14 +516,14 @@ void launch_pair8(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
 template <int BM, int WAVES_M>
 void launch_bm8(const GemmArgs& a, const GemmArgs* b, hipStream_t s) {
   if (a.mode == 0) launch_pair8<0, 0, BM, WAVES_M>(a, b, s);
-  else if (a.mode == 1) launch_pair8<1, 2, BM, WAVES_M>(a, b, s);
-  else launch_pair8<2, 2, BM, WAVES_M>(a, nullptr, s);
+  else launch_pair8<1, 2, BM, WAVES_M>(a, b, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp8(const GemmArgs& a, hipStream_t s, const GemmArgs* b) {
-  if (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode) || a.mode == 2))
+  // DOWN_SHARED runs only as the second part of a DOWN launch.
+  if (a.mode == 2 || (b && (b->bm != a.bm || (a.mode == 1 ? b->mode != 2 : b->mode != a.mode))))
     return hipErrorInvalidValue;
   switch (a.bm) {
     case 256: launch_bm8<256, 2>(a, b, s); break;
