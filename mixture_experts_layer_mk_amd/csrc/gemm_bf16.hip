@@ -484,8 +484,9 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& a, int blk, int nblk, in
 }
 
 // One part of a grouped GEMM launch: block `blk` of `nblk` runs one tile of
-// stage MODE.  Routed tail tiles of at most BM / 2 rows (an expert's last
-// rows) run the half-height tile layout, which does half the matrix work.
+// stage MODE.  An expert's last routed tile (its remaining rows) runs the
+// smallest layout that holds them: 64, 128 or 192 rows in the 256-row
+// launches, half height in the others, with matrix work in proportion.
 template <int MODE, int BM, int WAVES_M, int NW, int NS>
 __device__ __forceinline__ void gemm_part(const GemmArgs& a, int blk, int nblk, u32x4* As0,
                                           u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,

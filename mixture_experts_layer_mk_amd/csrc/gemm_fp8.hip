@@ -417,8 +417,9 @@ __device__ __forceinline__ void gemm8_tile(const GemmArgs& a, int row0, int rows
   }
 }
 
-// One part of a grouped FP8 GEMM launch (block `blk` of `nblk`): routed tail
-// tiles of at most BM / 2 rows run the half-height layout.
+// One part of a grouped FP8 GEMM launch (block `blk` of `nblk`): an expert's
+// last routed tile runs the 64-row layout for at most 64 rows in the 256-row
+// launches, and the half-height layout for at most BM / 2 rows.
 template <int MODE, int BM, int WAVES_M, int NS>
 __device__ __forceinline__ void gemm8_part(const GemmArgs& a, int blk, int nblk, u32x4* As0,
                                            u32x4* As1, u32x4* As2, u32x4* Bs0, u32x4* Bs1,
